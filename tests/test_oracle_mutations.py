@@ -1,0 +1,84 @@
+"""Plant plausible mistakes in the oracle (on the CPU, in a private copy of
+its source) and check that the pins catch every one of them: a dropped term,
+a wrong index or sign, a transposed or reversed operand, an off-by-one mask."""
+import importlib.util
+import os
+import types
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+import test_oracle_quant_append_counts as qpins
+
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+
+ATTENTION_MUTANTS = [
+    ("g = h // group", "g = h % hkv"),                                   # wrong GQA head map
+    ("p = ctx - q_len + i", "p = i"),                                    # top-left causal alignment
+    ("vis &= j <= p", "vis &= j < p"),                                   # diagonal masked
+    ("vis &= (p - j) <= window_left", "vis &= (p - j) < window_left"),   # window one short
+    ("s = scale * (q_rows @ keys.T)", "s = q_rows @ keys.T"),            # dropped scale
+    ("num = e @ values", "num = e @ values[::-1]"),                      # wrong value index
+    ("slot = t % page_size", "slot = (t + 1) % page_size"),              # wrong slot
+    ("phys = block_row[t // page_size]", "phys = block_row[(t // page_size) // 2]"),  # wrong page
+    ("lse[ok] = m_safe[ok] + np.log(denom[ok])", "lse[ok] = m_safe[ok] - np.log(denom[ok])"),  # sign
+    ("e = np.exp(s - m_safe[:, None])", "e = np.exp(s - m_safe[:, None] / 2)"),  # max not subtracted fully
+    ("(1.0 / np.sqrt(d))", "(1.0 / d)"),                                 # wrong default scale
+    ("q_rows @ keys.T", "q_rows @ keys[::-1].T"),                        # reversed keys
+]
+
+QUANT_MUTANTS = [
+    ("np.float32(127.0)", "np.float32(128.0)"),
+    ("np.rint(y)", "np.floor(y)"),
+    ("np.abs(x).max(axis=(1, 3))", "x.max(axis=(1, 3))"),
+    ("axis=(1, 3)", "axis=(1, 2)"),
+]
+
+
+def _load_mutant(filename, old, new):
+    src = open(os.path.join(ORACLE_DIR, filename)).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old}"
+    src = src.replace(old, new)
+    mod = types.ModuleType("oracle_mutant_" + filename[:-3])
+    exec(compile(src, filename + " (mutant)", "exec"), mod.__dict__)
+    return mod
+
+
+def _attention_battery():
+    for kw in pins.CASES:
+        pins.test_oracle_matches_brute_force(kw)
+    for args in [(4, 4, True, -1), (8, 2, True, -1), (6, 3, False, -1), (4, 2, True, 4)]:
+        pins.test_oracle_matches_torch_sdpa(*args)
+    pins.test_closed_form_example()
+    pins.test_causal_row0_and_zero_query()
+    pins.test_window_special_cases()
+    pins.test_decode_equals_prefill_row()
+
+
+def _quant_battery():
+    qpins.test_int8_quantiser_bounds_and_roundtrip()
+    qpins.test_int8_quantiser_matches_per_element_fp32_loop()
+    qpins.test_int8_half_way_rounds_to_even()
+
+
+def test_battery_passes_on_the_real_oracle():
+    _attention_battery()
+    _quant_battery()
+
+
+@pytest.mark.parametrize("old,new", ATTENTION_MUTANTS)
+def test_attention_mutant_is_caught(monkeypatch, old, new):
+    mut = _load_mutant("attention.py", old, new)
+    for name in ("attention_paged", "decode_paged", "visible_mask", "gather_sequence"):
+        monkeypatch.setattr(oracle, name, getattr(mut, name))
+    with pytest.raises(AssertionError):
+        _attention_battery()
+
+
+@pytest.mark.parametrize("old,new", QUANT_MUTANTS)
+def test_quant_mutant_is_caught(monkeypatch, old, new):
+    mut = _load_mutant("quant.py", old, new)
+    monkeypatch.setattr(oracle, "quantize_int8_pages", mut.quantize_int8_pages)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        _quant_battery()

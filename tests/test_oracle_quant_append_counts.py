@@ -1,0 +1,124 @@
+"""Pins of the oracle's int8 group quantiser, cache append and work counters."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bf16_values(shape, seed):
+    """float32 values that are exactly bf16 (low 16 bits cleared, rounded)."""
+    x = np.random.default_rng(seed).standard_normal(shape).astype(np.float32)
+    u = x.view(np.uint32)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+    return u.view(np.float32)
+
+
+def test_int8_quantiser_bounds_and_roundtrip():
+    x = _bf16_values((5, 16, 3, 8), 1)
+    codes, scales = oracle.quantize_int8_pages(x)
+    assert codes.dtype == np.int8 and scales.dtype == np.float32 and scales.shape == (5, 3)
+    assert codes.min() >= -127 and codes.max() <= 127          # -128 never produced
+    xh = oracle.dequantize_int8_pages(codes, scales)
+    err = np.abs(xh - x.astype(np.float64))
+    assert (err <= scales.astype(np.float64)[:, None, :, None] / 2 * (1 + 1e-6)).all()
+    # the largest magnitude of each group lands on +-127
+    for n in range(5):
+        for h in range(3):
+            g = x[n, :, h, :]
+            idx = np.unravel_index(np.abs(g).argmax(), g.shape)
+            assert abs(int(codes[n, idx[0], h, idx[1]])) == 127
+    # requantising the dequantised values with the same scales returns the codes
+    y = (xh.astype(np.float32) / scales[:, None, :, None]).astype(np.float32)
+    assert np.array_equal(np.rint(np.clip(y, -128, 127)).astype(np.int8), codes)
+
+
+def test_int8_quantiser_matches_per_element_fp32_loop():
+    """Element by element, in float32 scalar arithmetic: scale = absmax / 127,
+    code = round-half-even(clamp(x / scale))."""
+    x = _bf16_values((2, 4, 2, 4), 2)
+    x[1, :, 1, :] = 0.0                     # an all-zero group: scale 1, codes 0
+    codes, scales = oracle.quantize_int8_pages(x)
+    for n in range(2):
+        for h in range(2):
+            am = np.float32(0.0)
+            for s in range(4):
+                for d in range(4):
+                    am = max(am, np.float32(abs(x[n, s, h, d])))
+            sc = np.float32(am / np.float32(127.0)) if am != 0 else np.float32(1.0)
+            assert scales[n, h] == sc
+            for s in range(4):
+                for d in range(4):
+                    y = np.float32(x[n, s, h, d] / sc)
+                    y = min(max(y, np.float32(-128)), np.float32(127))
+                    c = int(round(float(y)))        # Python round = half-to-even
+                    assert codes[n, s, h, d] == c
+
+
+def test_int8_half_way_rounds_to_even():
+    # absmax 127 -> scale 1 exactly; 2.5 -> 2, 3.5 -> 4, -2.5 -> -2
+    x = np.zeros((1, 1, 1, 4), dtype=np.float32)
+    x[0, 0, 0, :] = [127.0, 2.5, 3.5, -2.5]
+    codes, scales = oracle.quantize_int8_pages(x)
+    assert scales[0, 0] == 1.0
+    assert codes[0, 0, 0].tolist() == [127, 2, 4, -2]
+
+
+def test_append_scatter_matches_loop_and_leaves_other_slots():
+    r = np.random.default_rng(3)
+    P, hkv, d = 4, 2, 3
+    k_pool = r.integers(-1000, 1000, (6, P, hkv, d)).astype(np.int16)   # raw 16-bit words
+    v_pool = r.integers(-1000, 1000, (6, P, hkv, d)).astype(np.int16)
+    table = np.array([[4, 1, 3], [0, 5, -1]])
+    start = [2, 3]
+    n_new = [7, 2]
+    cu = [0, 7, 9]
+    k_new = r.integers(-1000, 1000, (9, hkv, d)).astype(np.int16)
+    v_new = r.integers(-1000, 1000, (9, hkv, d)).astype(np.int16)
+    k2, v2 = oracle.append_pages(k_pool, v_pool, k_new, v_new, table, start, cu, P)
+    expect_k = k_pool.copy()
+    expect_v = v_pool.copy()
+    written = set()
+    for b in range(2):
+        for rr in range(n_new[b]):
+            pos = start[b] + rr
+            page, slot = table[b][pos // P], pos % P
+            expect_k[page, slot] = k_new[cu[b] + rr]
+            expect_v[page, slot] = v_new[cu[b] + rr]
+            written.add((page, slot))
+    assert np.array_equal(k2, expect_k) and np.array_equal(v2, expect_v)
+    assert k2.dtype == np.int16
+    for page in range(6):
+        for slot in range(P):
+            if (page, slot) not in written:
+                assert np.array_equal(k2[page, slot], k_pool[page, slot])
+    # sequence 0 positions 2..8: pages 4 (slots 2,3), 1 (0..3), 3 (slot 0)
+    assert (4, 2) in written and (3, 0) in written and (3, 1) not in written
+
+
+def test_counts_match_the_pages_examples():
+    g = json.load(open(os.path.join(GOLDEN, "page_counts.json")))
+    n = g["pair_count"]["tokens"]
+    with_self = oracle.visible_pairs(n, n, causal=True)
+    assert with_self - n == g["pair_count"]["pairs_excluding_self"]
+    assert with_self == n * (n + 1) // 2
+    kb = g["kv_bytes_per_token"]
+    assert oracle.kv_bytes_per_token(kb["num_layers"], kb["d_k"], kb["d_v"],
+                                     kb["bytes_per_value"]) == kb["bytes_per_token"]
+    gq = g["gqa_kv_saving"]
+    assert 1 - gq["num_groups"] / gq["num_q_heads"] == gq["kv_fraction_saved"]
+
+
+def test_counts_match_mask_and_workload_figures():
+    for q_len, ctx, causal, w in [(7, 7, True, -1), (3, 10, True, 2), (5, 5, False, -1), (9, 9, True, 0)]:
+        assert oracle.visible_pairs(q_len, ctx, causal, w) == int(oracle.visible_mask(q_len, ctx, causal, w).sum())
+    # Llama-2-7B-shaped causal prefill, L = 2048, 32 heads, D = 128
+    assert oracle.attention_flops(oracle.visible_pairs(2048, 2048), 128, 32) == 34_376_515_584
+    # 32k prefill with a 128-token left window: sum_i min(i + 1, 129)
+    assert oracle.visible_pairs(32768, 32768, True, 128) == 4_218_816
+    assert oracle.kv_read_bytes([10, 300], 8, 128, 2) == 2 * 310 * 8 * 128 * 2
+    assert oracle.kv_read_bytes([10, 300], 8, 128, 1, 4, 256) == 2 * 310 * 8 * 128 + 2 * 3 * 8 * 4
