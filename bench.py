@@ -1,0 +1,256 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one pass of the hot path over one batch of synthetic input:
+  * prefill step (the headline workload): kv_cache_append of a 2048-token
+    Llama-2-7B-shaped prompt (32 heads, D=128, bf16) into 256-token pages with
+    a permuted block table, then causal attn_prefill_paged over it;
+  * decode step (reported beside it): kv_cache_append of one new token for
+    each of 64 Llama-2-70B-shaped GQA sequences (64 q heads, 8 KV heads,
+    contexts uniform in [512, 8192]) and attn_decode_paged over their pages.
+
+``value`` is prefill TFLOP/s over the whole prefill step (algorithmic FLOPs:
+4 * D * Hq per visible (query, key) pair); the decode object gives KV-read
+GB/s (each valid K/V element once per KV head).  Inputs are resident in HBM
+before timing.  Kernel durations for the roofline objects come from HIP
+events around back-to-back launches on the stream the library launches on
+(torch's current stream).  One JSON line is printed.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from flashattention_paged_kv_amd import ops  # noqa: E402
+from flashattention_paged_kv_amd import workloads as wl  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def causal_pairs(n: int, window_left: int = -1) -> int:
+    if window_left < 0:
+        return n * (n + 1) // 2
+    w1 = window_left + 1
+    full = min(n, w1)
+    return full * (full + 1) // 2 + (n - full) * w1
+
+
+def _kernel_source_sha(name: str) -> str:
+    p = os.path.join(ROOT, "flashattention_paged_kv_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(kernel: str, source: str, per_launch_units: float):
+    """HBM bytes per launch from committed rocprofv3 counter runs, only if the
+    kernel source is unchanged since they were taken."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_sha") != _kernel_source_sha(source):
+        return None
+    return t["hbm_bytes_per_launch"]
+
+
+def _time_loop(fn, steps: int, warmup: int) -> float:
+    """Average ms per call of fn() over `steps` back-to-back calls."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def bench_prefill(w: wl.PrefillWorkload, steps: int, warmup: int) -> dict:
+    dev = torch.device("cuda")
+    inp = wl.prefill_inputs(w)
+    tdt = torch.bfloat16
+    shape = (inp["num_pages"], w.page_size, w.num_kv_heads, w.head_dim)
+    cache = ops.KVCache(torch.zeros(shape, dtype=tdt, device=dev), torch.zeros(shape, dtype=tdt, device=dev))
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    bt, cu, ctx, start = (inp[n].to(dev) for n in ("block_table", "cu_q", "ctx_lens", "start_pos"))
+    out = torch.empty_like(q)
+    max_len = max(w.seq_lens)
+
+    def append():
+        ops.kv_cache_append(cache, k, v, bt, start, cu, max_new=max_len)
+
+    def prefill():
+        ops.attn_prefill_paged(q, cu, cache, bt, ctx, max_q_len=max_len, softmax_scale=w.softmax_scale,
+                               causal=w.causal, window_left=w.window_left, out=out)
+
+    def step():
+        append()
+        prefill()
+
+    ms_step = _time_loop(step, steps, warmup)
+    ms_kernel = _time_loop(prefill, steps, warmup)
+    pairs = sum(causal_pairs(n, w.window_left) for n in w.seq_lens)
+    flops = 4 * w.head_dim * w.num_q_heads * pairs
+    kv_bytes = 2 * sum(w.seq_lens) * w.num_kv_heads * w.head_dim * 2
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+    return dict(workload=w.name, ms_per_step=ms_step, ms_prefill_kernel=ms_kernel, flops=flops,
+                tflops_step=flops / (ms_step * 1e-3) / 1e12, tflops_kernel=achieved, kv_bytes=kv_bytes,
+                roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                              frac=round(achieved / PEAK_BF16_TFLOPS, 4),
+                              traffic=_traffic("prefill_bf16_kernel", "prefill.hip", 1)))
+
+
+def bench_decode(w: wl.DecodeWorkload, steps: int, warmup: int) -> dict:
+    dev = torch.device("cuda")
+    inp = wl.decode_inputs(w)
+    bt, ctx, start, cun = (inp[n].to(dev) for n in ("block_table", "ctx_lens", "start_pos", "cu_new"))
+    q, k_new, v_new = (inp[n].to(dev) for n in ("q", "k_new", "v_new"))
+    kd, vd = inp["k_pool"].to(dev), inp["v_pool"].to(dev)
+    if w.kv_dtype == "i8":
+        ops.kv_cache_append(ops.KVCache(kd, vd), k_new, v_new, bt, start, cun, max_new=1)
+        kc, ks = ops.kv_pages_quantize_int8(kd)
+        vc, vs = ops.kv_pages_quantize_int8(vd)
+        del kd, vd
+        cache = ops.KVCache(kc, vc, ks, vs)
+        append = None
+    else:
+        cache = ops.KVCache(kd, vd)
+
+        def append():
+            ops.kv_cache_append(cache, k_new, v_new, bt, start, cun, max_new=1)
+    nbytes = ops.decode_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, bt.shape[1],
+                                        w.page_size)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+
+    def decode():
+        ops.attn_decode_paged(q, cache, bt, ctx, softmax_scale=w.softmax_scale, window_left=w.window_left,
+                              out=out, workspace=ws)
+
+    def step():
+        if append is not None:
+            append()
+        decode()
+
+    ms_step = _time_loop(step, steps, warmup)
+    ms_kernel = _time_loop(decode, steps, warmup)
+    ctx_np = inp["ctx_lens"].numpy().astype(np.int64)
+    esz = 1 if w.kv_dtype == "i8" else 2
+    kv_bytes = int(2 * ctx_np.sum() * w.num_kv_heads * w.head_dim * esz)
+    if w.kv_dtype == "i8":
+        kv_bytes += int(2 * sum(-(-int(c) // w.page_size) for c in ctx_np) * w.num_kv_heads * 4)
+    gbs = kv_bytes / (ms_kernel * 1e-3) / 1e9
+    return dict(workload=w.name, ms_per_step=ms_step, ms_decode_kernels=ms_kernel, kv_bytes=kv_bytes,
+                gbs_step=kv_bytes / (ms_step * 1e-3) / 1e9, gbs_kernel=gbs, sum_ctx=int(ctx_np.sum()),
+                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                              frac=round(gbs / PEAK_HBM_GBS, 4),
+                              traffic=_traffic("decode_split_kernel", "decode.hip", 1)))
+
+
+def cpu_baseline(w: wl.PrefillWorkload, budget_s: float = 15.0) -> dict:
+    """The CPU oracle (float64 numpy) on a bounded sample of the prefill
+    workload: the whole prompt's append, then as many heads of the causal
+    attention as fit in about `budget_s` seconds (heads are independent)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    inp = wl.prefill_inputs(w)
+    f64 = lambda t: t.float().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    shape = (inp["num_pages"], w.page_size, w.num_kv_heads, w.head_dim)
+    kp, vp = oracle.append_pages(np.zeros(shape), np.zeros(shape), f64(inp["k"]), f64(inp["v"]),
+                                 inp["block_table"].numpy(), inp["start_pos"].numpy(), inp["cu_q"].numpy(),
+                                 w.page_size)
+    q = f64(inp["q"])
+    heads = 0
+    while heads < w.num_q_heads and time.perf_counter() - t0 < budget_s:
+        h = heads
+        oracle.attention_paged(q[:, h:h + 1], inp["cu_q"].numpy(), kp[:, :, h:h + 1], vp[:, :, h:h + 1],
+                               inp["block_table"].numpy(), inp["ctx_lens"].numpy(), w.page_size,
+                               w.softmax_scale, w.causal, w.window_left)
+        heads += 1
+    dt = time.perf_counter() - t0
+    pairs = sum(causal_pairs(n, w.window_left) for n in w.seq_lens)
+    flops = 4 * w.head_dim * heads * pairs
+    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=int(threads), kind="oracle",
+                sample=f"{w.name}: append of all {sum(w.seq_lens)} tokens + causal attention of {heads} of "
+                       f"{w.num_q_heads} heads ({dt:.1f} s, float64 numpy)")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default=None, help="bench a single named workload instead")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this library runs on a single device (no collectives); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    ops.load_library()
+
+    if args.workload:
+        w = wl.WORKLOADS[args.workload]
+        r = bench_prefill(w, args.steps, args.warmup) if isinstance(w, wl.PrefillWorkload) \
+            else bench_decode(w, args.steps, args.warmup)
+        print(json.dumps(r), flush=True)
+        return 0
+
+    pre = bench_prefill(wl.LLAMA7B_PREFILL, args.steps, args.warmup)
+    dec = bench_decode(wl.LLAMA70B_DECODE, args.steps, args.warmup)
+    line = {
+        "metric": "prefill TFLOP/s & decode KV-read GB/s, as % of MI355X MFMA/HBM peak",
+        "value": round(pre["tflops_step"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, permuted page tables)",
+        "config": {"workload": pre["workload"], "batch": 1, "seq_len": 2048, "num_q_heads": 32,
+                   "num_kv_heads": 32, "head_dim": 128, "page_size": 256, "causal": True,
+                   "step": "kv_cache_append + attn_prefill_paged"},
+        "roofline": pre["roofline"],
+        "prefill_kernel_ms": round(pre["ms_prefill_kernel"], 5),
+        "decode": {"metric": "decode KV-read GB/s", "value": round(dec["gbs_step"], 1), "unit": "GB/s",
+                   "ms_per_step": round(dec["ms_per_step"], 5), "kernel_ms": round(dec["ms_decode_kernels"], 5),
+                   "kv_bytes": dec["kv_bytes"], "sum_ctx": dec["sum_ctx"],
+                   "config": {"workload": dec["workload"], "step": "kv_cache_append + attn_decode_paged"},
+                   "roofline": dec["roofline"]},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl.LLAMA7B_PREFILL)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,260 @@
+// C ABI of libpagedattn.so: argument checks, dispatch and launch.  Every
+// check that the host can make is made before anything is enqueued.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/pagedattn.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+
+pa_status fail(pa_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+pa_status fail(pa_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pa_status ok() {
+  g_detail[0] = '\0';
+  return PA_OK;
+}
+
+pa_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int log2_exact(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return (1 << l) == v ? l : -1;
+}
+
+// Checks shared by every call that reads a cache.
+pa_status check_cache(const pa_kv_cache *c, bool need_scales_if_i8) {
+  if (c == nullptr) return fail(PA_ERR_INVALID_ARG, "cache is NULL");
+  if (c->k_pages == nullptr || c->v_pages == nullptr) return fail(PA_ERR_INVALID_ARG, "cache pages are NULL");
+  if (c->num_pages <= 0) return fail(PA_ERR_INVALID_ARG, "num_pages must be > 0 (got %d)", c->num_pages);
+  if (c->num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be > 0 (got %d)", c->num_kv_heads);
+  if (c->dtype != PA_F32 && c->dtype != PA_BF16 && c->dtype != PA_I8)
+    return fail(PA_ERR_UNSUPPORTED, "unknown cache dtype %d", c->dtype);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", c->head_dim);
+  const int lp = log2_exact(c->page_size);
+  if (lp < 4 || lp > 8) return fail(PA_ERR_UNSUPPORTED, "page_size must be a power of two in [16, 256] (got %d)", c->page_size);
+  if (c->dtype == PA_I8 && need_scales_if_i8 && (c->k_scales == nullptr || c->v_scales == nullptr))
+    return fail(PA_ERR_INVALID_ARG, "int8 cache needs k_scales and v_scales");
+  return PA_OK;
+}
+
+pa::CacheView view_of(const pa_kv_cache *c) {
+  pa::CacheView v;
+  v.k = c->k_pages;
+  v.v = c->v_pages;
+  v.k_scales = c->k_scales;
+  v.v_scales = c->v_scales;
+  v.num_pages = c->num_pages;
+  v.page_size = c->page_size;
+  v.log2_page = log2_exact(c->page_size);
+  v.num_kv_heads = c->num_kv_heads;
+  v.head_dim = c->head_dim;
+  v.dtype = c->dtype;
+  return v;
+}
+
+pa_status check_scale(float s) {
+  if (!(s > 0.f) || !isfinite(s)) return fail(PA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  return PA_OK;
+}
+
+size_t decode_ws_bytes(int batch, int hq, int d, int max_splits) {
+  return (size_t)batch * hq * max_splits * ((size_t)d + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char *pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+  }
+  return "unknown status";
+}
+
+const char *pa_last_error_detail(void) { return g_detail; }
+
+pa_status kv_cache_append(const pa_kv_cache *cache, const void *k_new, const void *v_new,
+                          const int32_t *block_table, int32_t max_pages_per_seq, const int32_t *start_pos,
+                          const int32_t *cu_new, int32_t batch, int32_t max_new, void *stream) {
+  pa_status st = check_cache(cache, false);
+  if (st != PA_OK) return st;
+  if (cache->dtype == PA_I8)
+    return fail(PA_ERR_UNSUPPORTED, "append into an int8 cache is not supported; quantise whole pages instead");
+  if (batch < 0 || max_new < 0) return fail(PA_ERR_INVALID_ARG, "batch and max_new must be >= 0");
+  if (batch == 0 || max_new == 0) return ok();
+  if (k_new == nullptr || v_new == nullptr || block_table == nullptr || start_pos == nullptr || cu_new == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (max_pages_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq must be > 0");
+  pa::AppendArgs a;
+  a.k_pages = cache->k_pages;
+  a.v_pages = cache->v_pages;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.block_table = block_table;
+  a.max_pages = max_pages_per_seq;
+  a.start_pos = start_pos;
+  a.cu_new = cu_new;
+  a.batch = batch;
+  a.max_new = max_new;
+  a.page_size = cache->page_size;
+  a.log2_page = log2_exact(cache->page_size);
+  a.row_bytes = cache->num_kv_heads * cache->head_dim * (cache->dtype == PA_F32 ? 4 : 2);
+  return hip_status(pa::launch_append(a, (hipStream_t)stream), "kv_cache_append launch");
+}
+
+pa_status kv_pages_quantize_int8(const void *src, int8_t *codes, float *scales, int32_t num_pages,
+                                 int32_t page_size, int32_t num_kv_heads, int32_t head_dim, void *stream) {
+  if (src == nullptr || codes == nullptr || scales == nullptr) return fail(PA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (num_pages < 0 || num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARG, "bad num_pages / num_kv_heads");
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  const int lp = log2_exact(page_size);
+  if (lp < 4 || lp > 8) return fail(PA_ERR_UNSUPPORTED, "page_size must be a power of two in [16, 256]");
+  if (num_pages == 0) return ok();
+  pa::QuantArgs a;
+  a.src = (const uint16_t *)src;
+  a.codes = codes;
+  a.scales = scales;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  return hip_status(pa::launch_quantize(a, (hipStream_t)stream), "kv_pages_quantize_int8 launch");
+}
+
+pa_status attn_prefill_paged(const void *q, const int32_t *cu_q, const pa_kv_cache *cache,
+                             const int32_t *block_table, int32_t max_pages_per_seq, const int32_t *ctx_lens,
+                             int32_t batch, int32_t max_q_len, int32_t num_q_heads, float softmax_scale,
+                             int32_t causal, int32_t window_left, void *out, float *lse, void *stream) {
+  pa_status st = check_cache(cache, false);
+  if (st != PA_OK) return st;
+  if (cache->dtype == PA_I8) return fail(PA_ERR_UNSUPPORTED, "prefill over an int8 cache is not supported");
+  if (batch < 0 || max_q_len < 0) return fail(PA_ERR_INVALID_ARG, "batch and max_q_len must be >= 0");
+  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, cache->num_kv_heads);
+  if ((st = check_scale(softmax_scale)) != PA_OK) return st;
+  if (causal != 0 && causal != 1) return fail(PA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (batch == 0 || max_q_len == 0) return ok();
+  if (q == nullptr || cu_q == nullptr || block_table == nullptr || ctx_lens == nullptr || out == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (max_pages_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq must be > 0");
+  pa::PrefillArgs a;
+  a.q = q;
+  a.cu_q = cu_q;
+  a.c = view_of(cache);
+  a.block_table = block_table;
+  a.max_pages = max_pages_per_seq;
+  a.ctx_lens = ctx_lens;
+  a.batch = batch;
+  a.max_q_len = max_q_len;
+  a.num_q_heads = num_q_heads;
+  a.group = num_q_heads / cache->num_kv_heads;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.causal = causal;
+  a.window_left = window_left < 0 ? -1 : window_left;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(pa::launch_prefill(a, (hipStream_t)stream), "attn_prefill_paged launch");
+}
+
+size_t attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_pages_per_seq, int32_t page_size) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_pages_per_seq <= 0 ||
+      log2_exact(page_size) < 0)
+    return 0;
+  const int split = pa::decode_split_tokens(batch, num_kv_heads, max_pages_per_seq, page_size);
+  const long long max_tokens = (long long)max_pages_per_seq * page_size;
+  const int max_splits = (int)((max_tokens + split - 1) / split);
+  return decode_ws_bytes(batch, num_q_heads, head_dim, max_splits);
+}
+
+pa_status attn_decode_paged(const void *q, const pa_kv_cache *cache, const int32_t *block_table,
+                            int32_t max_pages_per_seq, const int32_t *ctx_lens, int32_t batch, int32_t num_q_heads,
+                            float softmax_scale, int32_t window_left, void *out, float *lse, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  pa_status st = check_cache(cache, true);
+  if (st != PA_OK) return st;
+  if (batch < 0) return fail(PA_ERR_INVALID_ARG, "batch must be >= 0");
+  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, cache->num_kv_heads);
+  const int group = num_q_heads / cache->num_kv_heads;
+  if (cache->dtype != PA_F32 && group > 16)
+    return fail(PA_ERR_UNSUPPORTED, "decode supports at most 16 query heads per KV head (got %d)", group);
+  if ((st = check_scale(softmax_scale)) != PA_OK) return st;
+  if (batch == 0) return ok();
+  if (q == nullptr || block_table == nullptr || ctx_lens == nullptr || out == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (max_pages_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq must be > 0");
+
+  if (cache->dtype == PA_F32) {
+    pa::PrefillArgs a;
+    a.q = q;
+    a.cu_q = nullptr;  // one query per sequence
+    a.c = view_of(cache);
+    a.block_table = block_table;
+    a.max_pages = max_pages_per_seq;
+    a.ctx_lens = ctx_lens;
+    a.batch = batch;
+    a.max_q_len = 1;
+    a.num_q_heads = num_q_heads;
+    a.group = group;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.causal = 1;
+    a.window_left = window_left < 0 ? -1 : window_left;
+    a.out = out;
+    a.lse = lse;
+    return hip_status(pa::launch_prefill(a, (hipStream_t)stream), "attn_decode_paged launch");
+  }
+
+  const int split = pa::decode_split_tokens(batch, cache->num_kv_heads, max_pages_per_seq, cache->page_size);
+  const long long max_tokens = (long long)max_pages_per_seq * cache->page_size;
+  const int max_splits = (int)((max_tokens + split - 1) / split);
+  const size_t need = decode_ws_bytes(batch, num_q_heads, cache->head_dim, max_splits);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "decode needs %zu workspace bytes (got %zu)", need, workspace_bytes);
+  pa::DecodeArgs a;
+  a.q = q;
+  a.c = view_of(cache);
+  a.block_table = block_table;
+  a.max_pages = max_pages_per_seq;
+  a.ctx_lens = ctx_lens;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.group = group;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.window_left = window_left < 0 ? -1 : window_left;
+  a.out = out;
+  a.lse = lse;
+  a.ws_o = (float *)workspace;
+  a.ws_ml = a.ws_o + (size_t)batch * num_q_heads * max_splits * cache->head_dim;
+  a.split_tokens = split;
+  a.max_splits = max_splits;
+  return hip_status(pa::launch_decode(a, (hipStream_t)stream), "attn_decode_paged launch");
+}
+
+}  // extern "C"

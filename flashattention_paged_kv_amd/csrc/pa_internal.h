@@ -1,0 +1,96 @@
+// Host-side argument bundles and kernel launchers shared by the library's
+// translation units (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// A paged cache as the kernels see it.
+struct CacheView {
+  const void *k;
+  const void *v;
+  const float *k_scales;
+  const float *v_scales;
+  int num_pages;
+  int page_size;
+  int log2_page;
+  int num_kv_heads;
+  int head_dim;
+  int dtype;  // pa_dtype
+};
+
+struct AppendArgs {
+  void *k_pages;
+  void *v_pages;
+  const void *k_new;
+  const void *v_new;
+  const int32_t *block_table;
+  int max_pages;
+  const int32_t *start_pos;
+  const int32_t *cu_new;
+  int batch;
+  int max_new;
+  int page_size;
+  int log2_page;
+  int row_bytes;  // num_kv_heads * head_dim * element size
+};
+
+struct QuantArgs {
+  const uint16_t *src;
+  int8_t *codes;
+  float *scales;
+  int num_pages;
+  int page_size;
+  int num_kv_heads;
+  int head_dim;
+};
+
+struct PrefillArgs {
+  const void *q;
+  const int32_t *cu_q;
+  CacheView c;
+  const int32_t *block_table;
+  int max_pages;
+  const int32_t *ctx_lens;
+  int batch;
+  int max_q_len;
+  int num_q_heads;
+  int group;           // num_q_heads / num_kv_heads
+  float scale_log2;    // softmax_scale * log2(e)
+  int causal;
+  int window_left;
+  void *out;
+  float *lse;
+};
+
+struct DecodeArgs {
+  const void *q;
+  CacheView c;
+  const int32_t *block_table;
+  int max_pages;
+  const int32_t *ctx_lens;
+  int batch;
+  int num_q_heads;
+  int group;
+  float scale_log2;
+  int window_left;
+  void *out;
+  float *lse;
+  float *ws_o;         // [batch, Hq, max_splits, head_dim]
+  float *ws_ml;        // [batch, Hq, max_splits, 2]  (max in log2 units, sum)
+  int split_tokens;    // keys per split: a multiple of 128 and of page_size
+  int max_splits;
+};
+
+// Decode split geometry used by both the workspace query and the call.
+int decode_split_tokens(int batch, int num_kv_heads, int max_pages_per_seq, int page_size);
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+
+}  // namespace pa

@@ -1,0 +1,234 @@
+"""Python binding of libpagedattn.so (ctypes).  Argument marshalling only:
+tensors are checked for device, dtype and contiguity, outputs are allocated
+with torch, and every computation runs in the library's HIP kernels on the
+current torch stream.  There is no fallback: if the library is missing or a
+call fails, an exception is raised.
+
+The entry points keep the library's names: ``kv_cache_append``,
+``kv_pages_quantize_int8``, ``attn_prefill_paged``, ``attn_decode_paged``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+
+PA_F32, PA_BF16, PA_I8 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8}
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"pagedattn status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [
+        ("k_pages", ctypes.c_void_p),
+        ("v_pages", ctypes.c_void_p),
+        ("k_scales", ctypes.c_void_p),
+        ("v_scales", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+EXPORTED = ("kv_cache_append", "kv_pages_quantize_int8", "attn_prefill_paged", "attn_decode_workspace_bytes",
+            "attn_decode_paged", "pa_status_string", "pa_last_error_detail", "pa_abi_version")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m flashattention_paged_kv_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    CP = ctypes.POINTER(_Cache)
+    lib.kv_cache_append.argtypes = [CP, P, P, P, I32, P, P, I32, I32, P]
+    lib.kv_pages_quantize_int8.argtypes = [P, P, P, I32, I32, I32, I32, P]
+    lib.attn_prefill_paged.argtypes = [P, P, CP, P, I32, P, I32, I32, I32, F32, I32, I32, P, P, P]
+    lib.attn_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
+    lib.attn_decode_workspace_bytes.restype = SZ
+    lib.attn_decode_paged.argtypes = [P, CP, P, I32, P, I32, I32, F32, I32, P, P, P, SZ, P]
+    for name in ("kv_cache_append", "kv_pages_quantize_int8", "attn_prefill_paged", "attn_decode_paged"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_last_error_detail.argtypes = []
+    lib.pa_last_error_detail.restype = ctypes.c_char_p
+    lib.pa_abi_version.restype = I32
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = load_library()
+        raise PagedAttnError(status, f"{lib.pa_status_string(status).decode()}: "
+                                     f"{lib.pa_last_error_detail().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+@dataclass
+class KVCache:
+    """Caller-owned paged cache: pools [num_pages, page_size, Hkv, D] (float32,
+    bfloat16, or int8 codes with float32 scales [num_pages, Hkv])."""
+    k_pages: torch.Tensor
+    v_pages: torch.Tensor
+    k_scales: Optional[torch.Tensor] = None
+    v_scales: Optional[torch.Tensor] = None
+
+    @property
+    def num_pages(self) -> int:
+        return self.k_pages.shape[0]
+
+    @property
+    def page_size(self) -> int:
+        return self.k_pages.shape[1]
+
+    @property
+    def num_kv_heads(self) -> int:
+        return self.k_pages.shape[2]
+
+    @property
+    def head_dim(self) -> int:
+        return self.k_pages.shape[3]
+
+    @property
+    def dtype(self) -> torch.dtype:
+        return self.k_pages.dtype
+
+    def _struct(self) -> _Cache:
+        _dev(self.k_pages, "k_pages")
+        _dev(self.v_pages, "v_pages", self.k_pages.dtype)
+        if self.k_pages.dim() != 4 or self.v_pages.shape != self.k_pages.shape:
+            raise ValueError("k_pages / v_pages must be [num_pages, page_size, num_kv_heads, head_dim]")
+        if self.k_pages.dtype not in _DTYPE_CODE:
+            raise ValueError(f"unsupported cache dtype {self.k_pages.dtype}")
+        for s in (self.k_scales, self.v_scales):
+            if s is not None:
+                _dev(s, "scales", torch.float32)
+        return _Cache(self.k_pages.data_ptr(), self.v_pages.data_ptr(),
+                      None if self.k_scales is None else self.k_scales.data_ptr(),
+                      None if self.v_scales is None else self.v_scales.data_ptr(),
+                      self.num_pages, self.page_size, self.num_kv_heads, self.head_dim,
+                      _DTYPE_CODE[self.k_pages.dtype])
+
+
+def kv_cache_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, block_table: torch.Tensor,
+                    start_pos: torch.Tensor, cu_new: torch.Tensor, max_new: Optional[int] = None) -> None:
+    """Write rows of k_new / v_new [total_new, Hkv, D] into their page slots."""
+    lib = load_library()
+    cs = cache._struct()
+    _dev(k_new, "k_new", cache.dtype)
+    _dev(v_new, "v_new", cache.dtype)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(start_pos, "start_pos", torch.int32)
+    _dev(cu_new, "cu_new", torch.int32)
+    batch = start_pos.shape[0]
+    max_new = k_new.shape[0] if max_new is None else max_new
+    _check(lib.kv_cache_append(ctypes.byref(cs), _ptr(k_new), _ptr(v_new), _ptr(block_table),
+                               block_table.shape[1], _ptr(start_pos), _ptr(cu_new), batch, max_new, _stream()))
+
+
+def kv_pages_quantize_int8(src: torch.Tensor, codes: Optional[torch.Tensor] = None,
+                           scales: Optional[torch.Tensor] = None):
+    """bf16 pages [N, P, Hkv, D] -> (int8 codes, fp32 scales [N, Hkv])."""
+    lib = load_library()
+    _dev(src, "src", torch.bfloat16)
+    n, p, hkv, d = src.shape
+    codes = torch.empty(src.shape, dtype=torch.int8, device=src.device) if codes is None else codes
+    scales = torch.empty((n, hkv), dtype=torch.float32, device=src.device) if scales is None else scales
+    _dev(codes, "codes", torch.int8)
+    _dev(scales, "scales", torch.float32)
+    _check(lib.kv_pages_quantize_int8(_ptr(src), _ptr(codes), _ptr(scales), n, p, hkv, d, _stream()))
+    return codes, scales
+
+
+def attn_prefill_paged(q: torch.Tensor, cu_q: torch.Tensor, cache: KVCache, block_table: torch.Tensor,
+                       ctx_lens: torch.Tensor, max_q_len: Optional[int] = None,
+                       softmax_scale: Optional[float] = None, causal: bool = True, window_left: int = -1,
+                       out: Optional[torch.Tensor] = None, return_lse: bool = False):
+    """Attention of q [total_q, Hq, D] (ragged by cu_q) against the paged
+    cache.  Returns out (and lse [total_q, Hq] if asked)."""
+    lib = load_library()
+    cs = cache._struct()
+    _dev(q, "q")
+    _dev(cu_q, "cu_q", torch.int32)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(ctx_lens, "ctx_lens", torch.int32)
+    total_q, hq, d = q.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    max_q_len = total_q if max_q_len is None else max_q_len
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib.attn_prefill_paged(_ptr(q), _ptr(cu_q), ctypes.byref(cs), _ptr(block_table), block_table.shape[1],
+                                  _ptr(ctx_lens), ctx_lens.shape[0], max_q_len, hq, scale, int(bool(causal)),
+                                  int(window_left), _ptr(out), _ptr(lse), _stream()))
+    return (out, lse) if return_lse else out
+
+
+def decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           max_pages_per_seq: int, page_size: int) -> int:
+    return int(load_library().attn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                                          max_pages_per_seq, page_size))
+
+
+def attn_decode_paged(q: torch.Tensor, cache: KVCache, block_table: torch.Tensor, ctx_lens: torch.Tensor,
+                      softmax_scale: Optional[float] = None, window_left: int = -1,
+                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      return_lse: bool = False):
+    """One query per sequence, q [B, Hq, D], against its ctx_lens[b] cached
+    keys.  ``workspace`` (uint8, at least decode_workspace_bytes(...)) is
+    allocated if not given."""
+    lib = load_library()
+    cs = cache._struct()
+    _dev(q, "q")
+    _dev(block_table, "block_table", torch.int32)
+    _dev(ctx_lens, "ctx_lens", torch.int32)
+    batch, hq, d = q.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if workspace is None:
+        nbytes = decode_workspace_bytes(batch, hq, cache.num_kv_heads, d, block_table.shape[1], cache.page_size)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib.attn_decode_paged(_ptr(q), ctypes.byref(cs), _ptr(block_table), block_table.shape[1],
+                                 _ptr(ctx_lens), batch, hq, scale, int(window_left), _ptr(out), _ptr(lse),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return (out, lse) if return_lse else out

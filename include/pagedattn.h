@@ -1,0 +1,191 @@
+/*
+ * pagedattn.h - C ABI of libpagedattn.so: exact scaled-dot-product attention
+ * read from a paged KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes, with the web pages it follows (cited by title
+ * and section):
+ *   - "大模型推理优化：KV Cache与FlashAttention实战" (LLM inference optimisation:
+ *     KV Cache and FlashAttention in practice), section 2.1: a query attends to
+ *     every cached key up to and including its own position, with weights
+ *     softmax(q.K^T / sqrt(d)) applied to V; section 5.1: the attention call
+ *     takes a softmax scale (default 1/sqrt(d)), a causal flag and a local
+ *     window.
+ *   - "Flash Attention与Paged KV Cache优化大模型计算效率" (Flash Attention and
+ *     Paged KV Cache), section 2.1: tiles of Q/K/V are processed on chip;
+ *     section 3.2: the cache is cut into fixed-size pages found through a
+ *     page table (logical page -> physical page), each page holding
+ *     (page_size, d_model) values; section 4.1: the prompt goes through
+ *     FlashAttention, generation reads the paged cache.
+ *   - "大模型推理优化实战：KV Cache + Flash Attention，让 Token 生成快 3 倍"
+ *     (3x faster token generation), "KV Cache" section: new K/V are appended
+ *     to the cache before the query attends; "Flash Attention" section: the
+ *     online softmax (running max, running sum, rescaling) makes the tiled
+ *     result exactly the plain one.
+ *   - "LLM推理系统优化：KV缓存管理与动态批处理技术" (KV-cache management and
+ *     dynamic batching), section 2.1: grouped-query attention, query head h
+ *     reads KV head h / (Hq / Hkv); section 3.1: paged KV blocks (256 tokens
+ *     per block); section 3.2: symmetric abs-max group quantisation.
+ *
+ * Conventions shared by every entry point:
+ *   - Memory: every pointer argument is a DEVICE pointer (caller-owned,
+ *     e.g. a torch tensor's data_ptr) unless stated otherwise.  The library
+ *     allocates and frees no device memory; decode's split partials live in
+ *     the caller's workspace.
+ *   - Layout: a KV pool is [num_pages, page_size, num_kv_heads, head_dim],
+ *     row-major (token-major pages, d_model = num_kv_heads * head_dim).  K and
+ *     V have separate pools.  A block table is int32 [batch, max_pages_per_seq]:
+ *     entry [b][n] is the physical page holding tokens [n*P, (n+1)*P) of
+ *     sequence b.  Token t of sequence b is slot t % P of page
+ *     block_table[b][t / P].
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *     stream).  Every call only enqueues work on it: no host sync.
+ *   - Errors: calls return pa_status and never abort.  Arguments the host can
+ *     check are checked before any work is enqueued (PA_ERR_INVALID_ARG,
+ *     PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE); a failed launch returns
+ *     PA_ERR_HIP.  Device-resident integers (block-table entries, lengths,
+ *     prefix sums) are not validated: out-of-range values are undefined
+ *     behaviour.  pa_last_error_detail() gives a message for the last failure
+ *     on the calling thread.
+ *   - Thread safety: no global mutable state apart from a per-thread error
+ *     string and a once-initialised device-property cache.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad scale, ...      */
+  PA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, page_size, dtype  */
+  PA_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed        */
+  PA_ERR_WORKSPACE = 4    /* decode workspace missing or too small             */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,  /* float32 K/V pages, float32 queries and outputs                */
+  PA_BF16 = 1, /* bfloat16 K/V pages, bfloat16 queries and outputs              */
+  PA_I8 = 2    /* int8 K/V codes with fp32 scales; bfloat16 queries and outputs */
+} pa_dtype;
+
+/* A paged KV cache.  The struct itself is read on the host during the call
+ * only; the pointers inside are device pointers owned by the caller.
+ *   k_pages, v_pages : [num_pages, page_size, num_kv_heads, head_dim] of dtype
+ *   k_scales, v_scales: PA_I8 only, fp32 [num_pages, num_kv_heads]; the value
+ *                       of code c in page n, head g is c * scales[n][g]
+ *                       (NULL for other dtypes)
+ *   page_size        : a power of two in [16, 256]
+ *   head_dim         : 64 or 128                                              */
+typedef struct pa_kv_cache {
+  void *k_pages;
+  void *v_pages;
+  float *k_scales;
+  float *v_scales;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* a pa_dtype */
+} pa_kv_cache;
+
+/* kv_cache_append - write new K/V rows into their page slots.
+ * Source: the KV-cache growth step ("KV Cache" section of the 3x-faster page:
+ * the cache grows by appending the new tokens' K/V) through the page table
+ * (section 3.2 of the Flash Attention + Paged KV Cache page).
+ *   k_new, v_new : [cu_new[batch], num_kv_heads, head_dim], cache dtype
+ *                  (PA_F32 or PA_BF16; PA_I8 caches return PA_ERR_UNSUPPORTED)
+ *   block_table  : int32 [batch, max_pages_per_seq]; pages must already be
+ *                  assigned for every written position
+ *   start_pos    : int32 [batch], length of sequence b before this append
+ *   cu_new       : int32 [batch + 1], prefix sums of new-token counts
+ *   max_new      : host int, an upper bound on cu_new[b+1] - cu_new[b]
+ * Row r of sequence b lands at position start_pos[b] + r.  A bit copy. */
+pa_status kv_cache_append(const pa_kv_cache *cache, const void *k_new, const void *v_new,
+                          const int32_t *block_table, int32_t max_pages_per_seq,
+                          const int32_t *start_pos, const int32_t *cu_new, int32_t batch,
+                          int32_t max_new, void *stream);
+
+/* kv_pages_quantize_int8 - symmetric abs-max int8 quantisation of whole pages.
+ * Source: section 3.2 (group quantisation) of the KV-cache management page,
+ * with bits = 8 and one group per (physical page, KV head): P x D values.
+ *   src     : bf16 [num_pages, page_size, num_kv_heads, head_dim]
+ *   codes   : int8, same shape (output)
+ *   scales  : fp32 [num_pages, num_kv_heads] (output)
+ * scale = absmax / 127 in fp32 (1 when absmax is 0); code =
+ * round-half-even(clamp(x / scale, -128, 127)), divisions in IEEE fp32.
+ * Call once per pool (K and V separately). */
+pa_status kv_pages_quantize_int8(const void *src, int8_t *codes, float *scales, int32_t num_pages,
+                                 int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                                 void *stream);
+
+/* attn_prefill_paged - causal (optionally windowed) attention of ragged query
+ * rows against the paged cache, FlashAttention-style (tiles + online
+ * softmax).  Sources: section 2.1 of the KV Cache + FlashAttention page
+ * (definition), its section 5.1 (scale, causal, window), section 2.1 of the
+ * Flash Attention + Paged KV Cache page (tiling), the online-softmax section
+ * of the 3x-faster page, section 2.1 of the KV-cache management page (GQA).
+ *   q          : [cu_q[batch], num_q_heads, head_dim]; bf16 for PA_BF16
+ *                caches, fp32 for PA_F32 caches (PA_I8: unsupported)
+ *   cu_q       : int32 [batch + 1], prefix sums of query counts
+ *   ctx_lens   : int32 [batch], keys of sequence b INCLUDING its queries;
+ *                query row i of sequence b sits at position
+ *                ctx_lens[b] - q_len_b + i (bottom-right alignment)
+ *   max_q_len  : host int, upper bound on q_len_b (sizes the grid)
+ *   softmax_scale: > 0 and finite (callers pass 1/sqrt(head_dim) by default)
+ *   causal     : 0 or 1
+ *   window_left: < 0 for no window; else key j is visible to the query at
+ *                position p only if p - j <= window_left
+ *   out        : [cu_q[batch], num_q_heads, head_dim], dtype of q
+ *   lse        : fp32 [cu_q[batch], num_q_heads] natural-log log-sum-exp of the
+ *                scaled scores, or NULL
+ * num_q_heads must be a multiple of cache->num_kv_heads. */
+pa_status attn_prefill_paged(const void *q, const int32_t *cu_q, const pa_kv_cache *cache,
+                             const int32_t *block_table, int32_t max_pages_per_seq,
+                             const int32_t *ctx_lens, int32_t batch, int32_t max_q_len,
+                             int32_t num_q_heads, float softmax_scale, int32_t causal,
+                             int32_t window_left, void *out, float *lse, void *stream);
+
+/* attn_decode_workspace_bytes - HOST function: bytes of workspace that
+ * attn_decode_paged needs for these sizes (an upper bound; 0 on bad input). */
+size_t attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t max_pages_per_seq, int32_t page_size);
+
+/* attn_decode_paged - one query token per sequence against its whole paged
+ * context, split over the context (split-K) and merged by a second kernel.
+ * Sources: as attn_prefill_paged, with q_len = 1; the split merge uses the
+ * same running-max / running-sum rescaling as the online softmax.
+ *   q        : [batch, num_q_heads, head_dim]; fp32 for PA_F32, else bf16
+ *   ctx_lens : int32 [batch] keys per sequence INCLUDING the new token (>= 1)
+ *   window_left: as for prefill (the query sits at position ctx_lens[b] - 1)
+ *   out      : [batch, num_q_heads, head_dim], dtype of q
+ *   lse      : fp32 [batch, num_q_heads] or NULL
+ *   workspace: device scratch of at least attn_decode_workspace_bytes(...)
+ *              bytes for the same sizes; its contents are undefined after
+ *              the call; calls that share a workspace on different streams
+ *              race. */
+pa_status attn_decode_paged(const void *q, const pa_kv_cache *cache, const int32_t *block_table,
+                            int32_t max_pages_per_seq, const int32_t *ctx_lens, int32_t batch,
+                            int32_t num_q_heads, float softmax_scale, int32_t window_left, void *out,
+                            float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *pa_status_string(pa_status status);
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char *pa_last_error_detail(void);
+
+/* PA_ABI_VERSION of the built library. */
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

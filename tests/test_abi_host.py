@@ -1,0 +1,145 @@
+"""The C-ABI library loads, exports every symbol its header declares, and
+rejects bad arguments with the documented status codes before enqueuing any
+work (so these run without a GPU: no compute call is made)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from flashattention_paged_kv_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ops.LIB_PATH), reason="library not built")
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails its checks first
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:pa_status|size_t|const char \*|int32_t)\s*\*?\s*(\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declarations_are_exported():
+    names = _declared_functions()
+    assert set(names) == set(ops.EXPORTED), names
+    out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+    lib = ops.load_library()
+    for n in names:
+        assert hasattr(lib, n)
+    assert lib.pa_abi_version() == 1
+
+
+def test_status_strings():
+    lib = ops.load_library()
+    assert lib.pa_status_string(0) == b"ok"
+    for s in range(1, 5):
+        assert lib.pa_status_string(s) not in (b"ok", b"unknown status")
+    assert lib.pa_status_string(99) == b"unknown status"
+
+
+def _cache(**kw):
+    c = dict(k_pages=0x1000, v_pages=0x2000, k_scales=None, v_scales=None, num_pages=4, page_size=16,
+             num_kv_heads=2, head_dim=128, dtype=ops.PA_BF16)
+    c.update(kw)
+    return ops._Cache(**c)
+
+
+def _prefill(cache, **kw):
+    lib = ops.load_library()
+    a = dict(q=FAKE, cu_q=FAKE, block_table=FAKE, max_pages=4, ctx=FAKE, batch=1, max_q_len=8, hq=4,
+             scale=0.1, causal=1, window=-1, out=FAKE, lse=None)
+    a.update(kw)
+    return lib.attn_prefill_paged(a["q"], a["cu_q"], ctypes.byref(cache), a["block_table"], a["max_pages"],
+                                  a["ctx"], a["batch"], a["max_q_len"], a["hq"], a["scale"], a["causal"],
+                                  a["window"], a["out"], a["lse"], None)
+
+
+def _decode(cache, **kw):
+    lib = ops.load_library()
+    a = dict(q=FAKE, block_table=FAKE, max_pages=4, ctx=FAKE, batch=2, hq=4, scale=0.1, window=-1, out=FAKE,
+             ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.attn_decode_paged(a["q"], ctypes.byref(cache), a["block_table"], a["max_pages"], a["ctx"],
+                                 a["batch"], a["hq"], a["scale"], a["window"], a["out"], None, a["ws"],
+                                 a["ws_bytes"], None)
+
+
+def _detail():
+    return ops.load_library().pa_last_error_detail().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), 2), (dict(page_size=24), 2), (dict(page_size=512), 2), (dict(page_size=8), 2),
+    (dict(dtype=7), 2), (dict(dtype=ops.PA_I8), 2), (dict(k_pages=None), 1), (dict(num_pages=0), 1),
+    (dict(num_kv_heads=0), 1),
+])
+def test_prefill_rejects_bad_cache(kw, status):
+    assert _prefill(_cache(**kw)) == status
+    assert _detail() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=3), 1), (dict(hq=0), 1), (dict(scale=0.0), 1), (dict(scale=float("inf")), 1),
+    (dict(scale=float("nan")), 1), (dict(scale=-1.0), 1), (dict(causal=2), 1), (dict(q=None), 1),
+    (dict(cu_q=None), 1), (dict(out=None), 1), (dict(block_table=None), 1), (dict(max_pages=0), 1),
+    (dict(batch=-1), 1),
+])
+def test_prefill_rejects_bad_args(kw, status):
+    assert _prefill(_cache(), **kw) == status
+
+
+def test_prefill_empty_batch_is_ok_without_work():
+    assert _prefill(_cache(), batch=0, q=None, out=None) == 0
+    assert _prefill(_cache(), max_q_len=0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=3), 1), (dict(scale=0.0), 1), (dict(q=None), 1), (dict(ws=None), 4), (dict(ws_bytes=16), 4),
+    (dict(hq=2 * 17), 2),
+])
+def test_decode_rejects_bad_args(kw, status):
+    assert _decode(_cache(), **kw) == status
+
+
+def test_decode_int8_needs_scales():
+    assert _decode(_cache(dtype=ops.PA_I8)) == 1
+    assert "scales" in _detail()
+
+
+def test_workspace_size_query():
+    lib = ops.load_library()
+    n = lib.attn_decode_workspace_bytes(64, 64, 8, 128, 32, 256)
+    assert n >= 64 * 64 * (128 + 2) * 4          # at least one split per (sequence, head)
+    assert n % 4 == 0
+    assert lib.attn_decode_workspace_bytes(0, 64, 8, 128, 32, 256) == 0
+    assert lib.attn_decode_workspace_bytes(4, 64, 8, 128, 32, 100) == 0
+    # a workspace one byte short of the query is rejected
+    assert _decode(_cache(num_kv_heads=2, page_size=16), batch=2, hq=4, max_pages=4,
+                   ws_bytes=lib.attn_decode_workspace_bytes(2, 4, 2, 128, 4, 16) - 1) == 4
+
+
+def test_append_rejects_bad_args():
+    lib = ops.load_library()
+    c = _cache(dtype=ops.PA_I8)
+    assert lib.kv_cache_append(ctypes.byref(c), FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 1, None) == 2
+    c = _cache()
+    assert lib.kv_cache_append(ctypes.byref(c), None, FAKE, FAKE, 4, FAKE, FAKE, 1, 1, None) == 1
+    assert lib.kv_cache_append(ctypes.byref(c), FAKE, FAKE, FAKE, 4, FAKE, FAKE, -1, 1, None) == 1
+    assert lib.kv_cache_append(ctypes.byref(c), None, None, None, 4, None, None, 0, 0, None) == 0
+    assert lib.kv_cache_append(None, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 1, None) == 1
+
+
+def test_quantize_rejects_bad_args():
+    lib = ops.load_library()
+    assert lib.kv_pages_quantize_int8(None, FAKE, FAKE, 1, 16, 1, 128, None) == 1
+    assert lib.kv_pages_quantize_int8(FAKE, FAKE, FAKE, 1, 16, 1, 80, None) == 2
+    assert lib.kv_pages_quantize_int8(FAKE, FAKE, FAKE, 1, 48, 1, 128, None) == 2
+    assert lib.kv_pages_quantize_int8(FAKE, FAKE, FAKE, 0, 16, 1, 128, None) == 0

@@ -1,0 +1,225 @@
+"""GPU parity of every entry point against the CPU oracle, on small seeded
+inputs that still span several tiles, pages and splits with ragged tails,
+plus the invariants the pages fix (cached decode = recompute, page shuffles)
+and edge cases (lengths around page and tile boundaries, windows 0/1/127/128,
+GQA group sizes 1/8/16, poisoned slots past the end of each sequence)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flashattention_paged_kv_amd import ops
+from flashattention_paged_kv_amd import workloads as wl
+from gpu_cases import DecodeRun, PrefillRun, bits, check_close, f64, nan_pool, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("page_size", [16, 256])
+def test_append_is_a_bitwise_scatter(dtype, page_size):
+    w = wl.PrefillWorkload("append", (300, 77, 1, 256), 4, 2, 128, page_size, dtype, seed=11, spare_pages=3)
+    say(f"append dtype={dtype} P={page_size}")
+    inp = wl.prefill_inputs(w)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    kp = nan_pool(inp["num_pages"], page_size, 2, 128, tdt)
+    vp = nan_pool(inp["num_pages"], page_size, 2, 128, tdt)
+    before_k, before_v = bits(kp), bits(vp)
+    ops.kv_cache_append(ops.KVCache(kp, vp), inp["k"].cuda(), inp["v"].cuda(), inp["block_table"].cuda(),
+                        inp["start_pos"].cuda(), inp["cu_q"].cuda(), max_new=300)
+    torch.cuda.synchronize()
+    ek, ev = oracle.append_pages(before_k, before_v, bits(inp["k"]), bits(inp["v"]), inp["block_table"].numpy(),
+                                 inp["start_pos"].numpy(), inp["cu_q"].numpy(), page_size)
+    assert np.array_equal(bits(kp), ek) and np.array_equal(bits(vp), ev)
+
+
+@pytest.mark.parametrize("page_size,d", [(16, 128), (256, 128), (32, 64)])
+def test_int8_quantiser_is_bit_exact(page_size, d):
+    say(f"quantise P={page_size} D={d}")
+    x = wl.normal((7, page_size, 3, d), "bf16", 21, 1)
+    x[2, :, 1, :] = 0.0                      # an all-zero group
+    x[4, 3, 0, 5] = 40.0                     # an outlier
+    codes, scales = ops.kv_pages_quantize_int8(x.cuda())
+    torch.cuda.synchronize()
+    ec, es = oracle.quantize_int8_pages(x.float().numpy())
+    assert np.array_equal(codes.cpu().numpy(), ec)
+    assert np.array_equal(bits(scales), es.view(np.int32))
+
+
+PREFILL_CASES = [
+    wl.PrefillWorkload("bf16_d128_g4_p16", (300, 77, 1, 128, 129), 8, 2, 128, 16, "bf16", seed=31, spare_pages=2),
+    wl.PrefillWorkload("bf16_d64_mha_p256", (513,), 4, 4, 64, 256, "bf16", seed=32),
+    wl.PrefillWorkload("bf16_d128_g8_win0", (200, 31), 8, 1, 128, 64, "bf16", seed=33, window_left=0),
+    wl.PrefillWorkload("bf16_d128_g8_win1", (200, 31), 8, 1, 128, 64, "bf16", seed=33, window_left=1),
+    wl.PrefillWorkload("bf16_d128_g8_win127", (400, 31), 8, 1, 128, 64, "bf16", seed=33, window_left=127),
+    wl.PrefillWorkload("bf16_d128_g8_win128", (400, 129), 8, 1, 128, 64, "bf16", seed=33, window_left=128),
+    wl.PrefillWorkload("bf16_d128_win_big", (300,), 2, 2, 128, 16, "bf16", seed=34, window_left=5000),
+    wl.PrefillWorkload("bf16_noncausal", (100, 65), 2, 2, 128, 16, "bf16", seed=35, causal=False),
+    wl.PrefillWorkload("f32_d64_p16", (128, 45), 2, 1, 64, 16, "f32", seed=36),
+    wl.PrefillWorkload("f32_d128_win3", (70,), 2, 2, 128, 32, "f32", seed=37, window_left=3),
+]
+
+
+@pytest.mark.parametrize("w", PREFILL_CASES, ids=lambda w: w.name)
+def test_prefill_matches_oracle(w):
+    say(f"prefill {w}")
+    run = PrefillRun(w)
+    out, lse = run.run()
+    torch.cuda.synchronize()
+    ref, ref_lse = run.oracle()
+    check_close(out, ref, w.dtype, "out")
+    err = np.abs(f64(lse) - ref_lse).max()
+    say(f"  lse max|d|={err:.3e}")
+    assert err <= (1e-4 if w.dtype == "f32" else 1e-3)
+
+
+def test_chunked_prefill_rows_at_the_end_of_a_context():
+    """q_len < ctx: the queries are the last rows of a longer cached context
+    (bottom-right causal alignment)."""
+    w = wl.PrefillWorkload("chunk", (700, 260), 8, 2, 128, 16, "bf16", seed=38)
+    say("chunked prefill")
+    run = PrefillRun(w)
+    q_lens = [130, 1]
+    cu = [0]
+    rows = []
+    for b, (n, ql) in enumerate(zip(w.seq_lens, q_lens)):
+        start = int(run.inp["cu_q"][b])
+        rows.append(run.inp["q"][start + n - ql:start + n])
+        cu.append(cu[-1] + ql)
+    q = torch.cat(rows)
+    cu_t = torch.tensor(cu, dtype=torch.int32)
+    out = ops.attn_prefill_paged(q.cuda(), cu_t.cuda(), run.cache, run.bt, run.ctx, max_q_len=max(q_lens))
+    kp, vp = run.oracle_pools()
+    ref, _ = oracle.attention_paged(f64(q), cu, kp, vp, run.inp["block_table"].numpy(), run.inp["ctx_lens"].numpy(),
+                                    w.page_size)
+    check_close(out, ref, "bf16", "chunked out")
+
+
+DECODE_CASES = [
+    wl.DecodeWorkload("bf16_g8_p16_edges", 10, 0, 0, 16, 2, 128, 16, "bf16", seed=41, spare_pages=2,
+                      ctx_lens=(1, 15, 16, 17, 255, 256, 257, 1000, 3000, 5000)),
+    wl.DecodeWorkload("bf16_g8_p256", 6, 1, 3000, 64, 8, 128, 256, "bf16", seed=42),
+    wl.DecodeWorkload("bf16_d64_g1_p32", 5, 1, 2000, 4, 4, 64, 32, "bf16", seed=43),
+    wl.DecodeWorkload("bf16_g16", 3, 1, 1500, 16, 1, 128, 64, "bf16", seed=44),
+    wl.DecodeWorkload("bf16_win0", 4, 1, 900, 16, 2, 128, 16, "bf16", seed=45, window_left=0),
+    wl.DecodeWorkload("bf16_win1", 4, 1, 900, 16, 2, 128, 16, "bf16", seed=45, window_left=1),
+    wl.DecodeWorkload("bf16_win127", 4, 1, 900, 16, 2, 128, 16, "bf16", seed=45, window_left=127),
+    wl.DecodeWorkload("bf16_win128", 4, 1, 900, 16, 2, 128, 256, "bf16", seed=45, window_left=128),
+    wl.DecodeWorkload("i8_g4_p16", 7, 0, 0, 8, 2, 128, 16, "i8", seed=46, spare_pages=2,
+                      ctx_lens=(1, 16, 17, 33, 300, 2049, 4100)),
+    wl.DecodeWorkload("i8_g8_p256_win200", 4, 1, 3000, 64, 8, 128, 256, "i8", seed=47, window_left=200),
+    wl.DecodeWorkload("i8_d64", 3, 1, 2500, 8, 1, 64, 128, "i8", seed=48),
+    wl.DecodeWorkload("f32_d64", 3, 1, 500, 1, 1, 64, 16, "f32", seed=49),
+    wl.DecodeWorkload("f32_d128_g2_win9", 3, 1, 300, 4, 2, 128, 32, "f32", seed=50, window_left=9),
+]
+
+
+@pytest.mark.parametrize("w", DECODE_CASES, ids=lambda w: w.name)
+def test_decode_matches_oracle(w):
+    say(f"decode {w.name} ctx={wl.decode_ctx_lens(w).tolist()}")
+    run = DecodeRun(w)
+    out, lse = run.run()
+    torch.cuda.synchronize()
+    (ref, ref_lse), _ = run.oracle()
+    check_close(out, ref, "f32" if w.kv_dtype == "f32" else "bf16", "out")
+    err = np.abs(f64(lse) - ref_lse).max()
+    say(f"  lse max|d|={err:.3e}")
+    assert err <= (1e-4 if w.kv_dtype == "f32" else 1e-3)
+
+
+def test_tiny_fp32_prefill_then_16_decode_steps():
+    """fp32, 1 head, D=64, 128-token causal prefill then 16 single-token
+    decode steps appending to a cache of 16-token pages with a permuted block
+    table; every step against the oracle at 1e-4."""
+    base = wl.TINY_FP32
+    n_total = 128 + wl.TINY_FP32_DECODE_STEPS
+    w = wl.PrefillWorkload(base.name, (n_total,), 1, 1, 64, 16, "f32", seed=base.seed)
+    say("tiny fp32 prefill + 16 decode steps")
+    inp = wl.prefill_inputs(w)
+    dev = "cuda"
+    kp = nan_pool(inp["num_pages"], 16, 1, 64, torch.float32)
+    vp = nan_pool(inp["num_pages"], 16, 1, 64, torch.float32)
+    cache = ops.KVCache(kp, vp)
+    bt = inp["block_table"].to(dev)
+    q, k, v = inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev)
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32, device=dev)
+    ops.kv_cache_append(cache, k[:128], v[:128], bt, i32([0]), i32([0, 128]))
+    out = ops.attn_prefill_paged(q[:128], i32([0, 128]), cache, bt, i32([128]), max_q_len=128)
+    dec = []
+    for t in range(128, n_total):
+        ops.kv_cache_append(cache, k[t:t + 1], v[t:t + 1], bt, i32([t]), i32([0, 1]))
+        dec.append(ops.attn_decode_paged(q[t:t + 1], cache, bt, i32([t + 1])))
+    torch.cuda.synchronize()
+    kpo, vpo = oracle.append_pages(np.full(kp.shape, np.nan), np.full(vp.shape, np.nan), f64(inp["k"]),
+                                   f64(inp["v"]), inp["block_table"].numpy(), [0], [0, n_total], 16)
+    ref, _ = oracle.attention_paged(f64(inp["q"]), [0, n_total], kpo, vpo, inp["block_table"].numpy(), [n_total], 16)
+    check_close(out, ref[:128], "f32", "prefill")
+    check_close(torch.cat(dec), ref[128:], "f32", "decode steps")
+
+
+def test_decode_equals_last_prefill_row():
+    w = wl.PrefillWorkload("dec_eq_pre", (300,), 8, 2, 128, 16, "bf16", seed=51)
+    say("decode == last prefill row")
+    run = PrefillRun(w)
+    out = run.run(return_lse=False)
+    dec = ops.attn_decode_paged(run.q[-1:].contiguous(), run.cache, run.bt, run.ctx)
+    torch.cuda.synchronize()
+    d = (dec[0].double() - out[-1].double()).abs().max().item()
+    say(f"  max|decode - prefill row| = {d:.3e}")
+    assert d <= 2e-2
+
+
+def _shuffle(pool, bt, seed):
+    n = pool.shape[0]
+    perm = torch.from_numpy(np.random.default_rng(seed).permutation(n)).to(pool.device)
+    new = torch.empty_like(pool)
+    new[perm] = pool                         # old page i -> new page perm[i]
+    bt2 = torch.where(bt >= 0, perm[bt.clamp(min=0).long()].int(), bt)
+    return new, bt2
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_decode_page_shuffle_is_bitwise_identical(kv):
+    w = wl.DecodeWorkload("shuffle", 5, 1, 3000, 16, 2, 128, 16, kv, seed=52)
+    say(f"decode page shuffle {kv}")
+    run = DecodeRun(w)
+    out1 = run.run(return_lse=False)
+    c = run.cache
+    k2, bt2 = _shuffle(c.k_pages, run.bt, 1)
+    v2, _ = _shuffle(c.v_pages, run.bt, 1)
+    ks2 = vs2 = None
+    if kv == "i8":
+        ks2, _ = _shuffle(c.k_scales, run.bt, 1)
+        vs2, _ = _shuffle(c.v_scales, run.bt, 1)
+    out2 = ops.attn_decode_paged(run.q, ops.KVCache(k2, v2, ks2, vs2), bt2, run.ctx)
+    out3 = run.run(return_lse=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out1), bits(out2))
+    assert np.array_equal(bits(out1), bits(out3))      # run-to-run determinism
+
+
+def test_prefill_page_shuffle_is_bitwise_identical():
+    w = wl.PrefillWorkload("pshuffle", (333, 64), 8, 2, 128, 16, "bf16", seed=53)
+    say("prefill page shuffle")
+    run = PrefillRun(w)
+    out1 = run.run(return_lse=False)
+    k2, bt2 = _shuffle(run.k_pool, run.bt, 2)
+    v2, _ = _shuffle(run.v_pool, run.bt, 2)
+    out2 = ops.attn_prefill_paged(run.q, run.cu, ops.KVCache(k2, v2), bt2, run.ctx, max_q_len=333)
+    out3 = run.run(return_lse=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out1), bits(out2))
+    assert np.array_equal(bits(out1), bits(out3))
+
+
+def test_decode_split_override_gives_same_result_within_tolerance(monkeypatch):
+    w = wl.DecodeWorkload("splits", 3, 2000, 4000, 16, 2, 128, 16, "bf16", seed=54)
+    run = DecodeRun(w)
+    base = run.run(return_lse=False)
+    monkeypatch.setenv("PAGEDATTN_SPLIT_TOKENS", "128")
+    say("decode with 128-key splits")
+    small = run.run(return_lse=False)
+    torch.cuda.synchronize()
+    (ref, _), _ = run.oracle()
+    check_close(small, ref, "bf16", "128-key splits")
+    assert (small.double() - base.double()).abs().max().item() <= 2e-2
