@@ -74,8 +74,12 @@ pa_status check_scale(float s) {
   return PA_OK;
 }
 
-size_t decode_ws_bytes(int batch, int hq, int d, int max_splits) {
-  return (size_t)batch * hq * max_splits * ((size_t)d + 2) * sizeof(float);
+// Decode workspace: partial (O, m, l) for batch * Hkv + nwg slots of G query
+// heads each, then batch + 1 int32 prefix sums.
+size_t decode_ws_bytes(int batch, int hq, int hkv, int d, int nwg) {
+  const size_t slots = (size_t)batch * hkv + nwg;
+  const size_t g = (size_t)(hq / hkv);
+  return slots * g * ((size_t)d + 2) * sizeof(float) + ((size_t)batch + 1) * sizeof(int32_t);
 }
 
 }  // namespace
@@ -184,12 +188,11 @@ pa_status attn_prefill_paged(const void *q, const int32_t *cu_q, const pa_kv_cac
 size_t attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t max_pages_per_seq, int32_t page_size) {
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_pages_per_seq <= 0 ||
-      log2_exact(page_size) < 0)
+      log2_exact(page_size) < 0 || num_q_heads % num_kv_heads != 0)
     return 0;
-  const int split = pa::decode_split_tokens(batch, num_kv_heads, max_pages_per_seq, page_size);
-  const long long max_tokens = (long long)max_pages_per_seq * page_size;
-  const int max_splits = (int)((max_tokens + split - 1) / split);
-  return decode_ws_bytes(batch, num_q_heads, head_dim, max_splits);
+  const int nwg = pa::decode_grid_size();
+  if (nwg <= 0) return 0;
+  return decode_ws_bytes(batch, num_q_heads, num_kv_heads, head_dim, nwg);
 }
 
 pa_status attn_decode_paged(const void *q, const pa_kv_cache *cache, const int32_t *block_table,
@@ -231,10 +234,9 @@ pa_status attn_decode_paged(const void *q, const pa_kv_cache *cache, const int32
     return hip_status(pa::launch_prefill(a, (hipStream_t)stream), "attn_decode_paged launch");
   }
 
-  const int split = pa::decode_split_tokens(batch, cache->num_kv_heads, max_pages_per_seq, cache->page_size);
-  const long long max_tokens = (long long)max_pages_per_seq * cache->page_size;
-  const int max_splits = (int)((max_tokens + split - 1) / split);
-  const size_t need = decode_ws_bytes(batch, num_q_heads, cache->head_dim, max_splits);
+  const int nwg = pa::decode_grid_size();
+  if (nwg <= 0) return fail(PA_ERR_HIP, "cannot query the current device");
+  const size_t need = decode_ws_bytes(batch, num_q_heads, cache->num_kv_heads, cache->head_dim, nwg);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(PA_ERR_WORKSPACE, "decode needs %zu workspace bytes (got %zu)", need, workspace_bytes);
   pa::DecodeArgs a;
@@ -250,10 +252,11 @@ pa_status attn_decode_paged(const void *q, const pa_kv_cache *cache, const int32
   a.window_left = window_left < 0 ? -1 : window_left;
   a.out = out;
   a.lse = lse;
+  const size_t slots_g = ((size_t)batch * cache->num_kv_heads + nwg) * group;
   a.ws_o = (float *)workspace;
-  a.ws_ml = a.ws_o + (size_t)batch * num_q_heads * max_splits * cache->head_dim;
-  a.split_tokens = split;
-  a.max_splits = max_splits;
+  a.ws_ml = a.ws_o + slots_g * cache->head_dim;
+  a.ws_prefix = (int32_t *)(a.ws_ml + slots_g * 2);
+  a.nwg = nwg;
   return hip_status(pa::launch_decode(a, (hipStream_t)stream), "attn_decode_paged launch");
 }
 

@@ -11,18 +11,30 @@
 // page's Flash Attention section is applied per wave, then across the waves of
 // a workgroup, then across splits; all three merges are the same algebra.
 //
-// Work split: one workgroup = (sequence b, KV head hk, split s of
-// split_tokens consecutive keys); all G = Hq/Hkv query heads of hk are handled
-// together so each K/V byte is read from HBM once.  Each of the 4 waves takes
-// every 4th 32-key tile of the split.
+// Work split (balanced for ragged context lengths): the keys of every
+// (sequence b, KV head hk) pair form a segment of 32-key tiles; all segments
+// laid end to end make one list of T tiles.  A fixed grid of N workgroups
+// (a few per CU) cuts the list into N equal ranges, [jT/N, (j+1)T/N) for
+// workgroup j, so every workgroup streams the same number of bytes whatever
+// the length mix.  A range is cut further at segment boundaries into pieces;
+// for each piece the workgroup's 4 waves take every 4th tile, merge their
+// running (m, l, O) through LDS and write one partial to slot (segment + j),
+// which is unique because both the segments and the ranges are in list
+// order.  All G = Hq/Hkv query heads of hk are handled together so each K/V
+// byte is read from HBM once.  The merge kernel finds the workgroups that
+// touched a segment from the same arithmetic and combines their partials.
 //
 // Per 32-key tile a wave computes S^T = K . Q^T with v_mfma_f32_16x16x32_bf16
 // (keys on the M side, query heads on the N side, zero-padded to 16), the
 // online softmax on the S^T registers, then O^T += V^T . P^T with V staged
 // through LDS and read back transposed by ds_read_b64_tr_b16 (ds_read_b64_tr_b8
-// for int8, converted to exact bf16 integers).  K/V tiles are loaded with
-// 16-byte global loads one tile ahead of the one being computed.
+// for int8, converted to exact bf16 integers).  Loads are 16-byte buffer
+// loads from one page per 16-key block; the next tile is in flight while a
+// tile is computed.
 #include <math.h>
+#include <stdlib.h>
+
+#include <atomic>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -31,31 +43,56 @@ namespace pa {
 
 constexpr int kDecWaves = 4;
 constexpr int kDecTile = 32;            // keys per wave iteration
-constexpr int kMaxSplitPages = 520;     // split_tokens / page_size + 1
+constexpr int kDecWgsPerCu = 3;         // resident split workgroups per CU (register bound)
 
-int decode_split_tokens(int batch, int num_kv_heads, int max_pages_per_seq, int page_size) {
-  // Aim for about 4096 workgroups at the largest possible contexts (about
-  // 16 per CU), with splits a power of two between 256 and 8192 keys that
-  // is a multiple of the page size.
-  const long long upper = (long long)batch * num_kv_heads * max_pages_per_seq * page_size;
-  long long want = upper / 4096;
-  int s = 256;
-  while (s < want && s < 8192) s <<= 1;
-  if (s < page_size) s = page_size;
-  if (const char *env = getenv("PAGEDATTN_SPLIT_TOKENS")) {
-    int v = atoi(env);
-    if (v >= 128 && v <= 8192 && (v & (v - 1)) == 0 && v >= page_size) s = v;
+// kDecWgsPerCu workgroups per CU of the current device (the split kernel's
+// occupancy, so the whole grid is resident at once), cached per device.  PAGEDATTN_DECODE_WGS overrides it (tests use
+// it to exercise other partitions of the same work).
+int decode_grid_size() {
+  if (const char *env = getenv("PAGEDATTN_DECODE_WGS")) {
+    const int v = atoi(env);
+    if (v >= 1 && v <= 65536) return v;
   }
-  return s;
+  // Without a queryable device (host-only use of the argument checks) the
+  // size is that of an MI355X: 256 CUs.
+  constexpr int kDefaultCus = 256;
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kDecWgsPerCu * kDefaultCus;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = kDefaultCus;
+    v = cus;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return kDecWgsPerCu * v;
+}
+
+// Tiles of 32 keys that a decode query at position ctx - 1 reads: from the
+// tile holding the first visible key to the tile holding the last.
+__device__ __forceinline__ int seg_tiles(int ctx, int window_left) {
+  const int lo = window_left >= 0 ? max(0, ctx - 1 - window_left) : 0;
+  return (ctx + kDecTile - 1) / kDecTile - lo / kDecTile;
+}
+
+// Workgroups that actually take tiles: at least kMinTilesPerWg tiles each,
+// so small problems are not spread thinner than the waves of one group.
+constexpr int kMinTilesPerWg = 8;
+__device__ __forceinline__ int active_wgs(long long total, int launched) {
+  const long long want = (total + kMinTilesPerWg - 1) / kMinTilesPerWg;
+  return (int)max(1LL, min((long long)launched, want));
 }
 
 template <int D, bool I8>
 struct DecodeCfg {
   static constexpr int kEsz = I8 ? 1 : 2;
-  static constexpr int kCpr = D * kEsz / 16;               // 16-byte chunks per cache row
-  static constexpr int kVLoads = kDecTile * kCpr / 64;     // V loads per lane per tile
-  static constexpr int kKPerBlock = I8 ? D / 64 : D / 32;  // K loads per lane per 16-key block
-  static constexpr int kKLoads = 2 * kKPerBlock;
+  // A lane holds 2 keys of a tile (one per 16-key block kb) and, for each,
+  // kChunks 16-byte pieces of the row: dims 32j + 8g .. +7 (bf16) or
+  // 64j + 16g .. +15 (int8), j < kChunks, g = lane / 16.
+  static constexpr int kChunks = I8 ? D / 64 : D / 32;
+  static constexpr int kLoads = 2 * kChunks;               // per lane per tile, for K and for V
   static constexpr int kVRow = I8 ? D + 16 : 2 * D + 32;   // staged V row bytes (bank spread)
   static constexpr int kNdb = D / 16;                      // 16-dim output blocks
   static constexpr int kNst = D / 32;                      // 32-dim QK k-steps
@@ -66,263 +103,389 @@ struct DecodeCfg {
 
 template <int D, bool I8>
 struct TileRegs {
-  uint4 k[DecodeCfg<D, I8>::kKLoads];
-  uint4 v[DecodeCfg<D, I8>::kVLoads];
+  uint4 k[DecodeCfg<D, I8>::kLoads];
+  uint4 v[DecodeCfg<D, I8>::kLoads];
 };
 
-// Position (0..31) inside the tile of S^T row i (0..3) of 16-key block kb held
-// by lane group g.  bf16: block kb = keys 16kb..16kb+15.  int8: lane group g
-// holds the 8 consecutive keys 8g..8g+7 so that one ds_read_b64_tr_b8 gives a
-// lane its V^T operand.
+// LDS row of tile key k (0..31) in the staged V tile.  bf16: row = key.
+// int8: keys are permuted so that rows 8g .. 8g+7 hold the 8 keys whose
+// probabilities lane group g carries (16kb + 4g + r, kb = 0..1, r = 0..3):
+// one ds_read_b64_tr_b8 of 8 consecutive rows then gives a lane its V^T
+// operand in that key order.
 template <bool I8>
-__device__ __forceinline__ int tile_key(int kb, int g, int i) {
-  return I8 ? 8 * g + 4 * kb + i : 16 * kb + 4 * g + i;
+__device__ __forceinline__ int v_row(int k) {
+  return I8 ? 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3) : k;
 }
 
-template <int D, bool I8>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor over [base, base + bytes) (gfx9 raw buffer, stride 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// NB: tiles in flight per wave (register buffers); WPC: resident workgroups
+// per CU the register budget is sized for (the grid is WPC per CU).
+template <int D, bool I8, int NB, int WPC>
+__global__ __launch_bounds__(256, WPC) void decode_split_kernel(DecodeArgs a, const int32_t *__restrict__ block_table,
+                                                               const float *__restrict__ k_scales,
+                                                               const float *__restrict__ v_scales) {
   using C = DecodeCfg<D, I8>;
   __shared__ __align__(16) unsigned char smem[C::kSmem];
-  __shared__ int s_pages[kMaxSplitPages];
+  __shared__ int s_wave_sum[kDecWaves];
+  __shared__ int s_first[2];
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int r16 = lane & 15;
-  const int split = blockIdx.x;
-  const int hk = blockIdx.y;
-  const int b = blockIdx.z;
-  const int ctx = a.ctx_lens[b];
-  const int S = a.split_tokens;
-  const int lo = a.window_left >= 0 ? max(0, ctx - 1 - a.window_left) : 0;
-  const int k_begin = max(split * S, lo);
-  const int k_end = min((split + 1) * S, ctx);
-  if (k_begin >= k_end) return;
-
-  const int P = a.c.page_size;
-  const int lp = a.c.log2_page;
+  const int j = blockIdx.x;
   const int hkv = a.c.num_kv_heads;
-  const int pg0 = k_begin >> lp;
-  const int pg1 = (k_end - 1) >> lp;
-  for (int i = threadIdx.x; i <= pg1 - pg0; i += blockDim.x)
-    s_pages[i] = a.block_table[(size_t)b * a.max_pages + pg0 + i];
+  const int W = a.window_left;
+
+  // --- Plan: tiles per sequence (same for every KV head), their prefix
+  // sums and the total, by a block scan over the batch.  Thread t owns the
+  // sequences [t*per, (t+1)*per).
+  const int per = (a.batch + blockDim.x - 1) / blockDim.x;
+  const int b_lo = min(a.batch, (int)threadIdx.x * per);
+  const int b_hi = min(a.batch, b_lo + per);
+  int mine = 0;
+  for (int bb = b_lo; bb < b_hi; ++bb) mine += seg_tiles(a.ctx_lens[bb], W);
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) s_wave_sum[w] = incl;
+  __syncthreads();
+  int before = 0, per_head_total = 0;
+#pragma unroll
+  for (int i = 0; i < kDecWaves; ++i) {
+    const int v = s_wave_sum[i];
+    before += i < w ? v : 0;
+    per_head_total += v;
+  }
+  const int excl = before + incl - mine;  // per-head tiles of sequences < b_lo
+  const long long total = (long long)hkv * per_head_total;
+  const int nwg = active_wgs(total, a.nwg);
+  if (j == 0) {
+    // The merge kernel reads the per-sequence prefix sums from here.
+    int acc = excl;
+    for (int bb = b_lo; bb < b_hi; ++bb) {
+      a.ws_prefix[bb] = acc;
+      acc += seg_tiles(a.ctx_lens[bb], W);
+    }
+    if (threadIdx.x == 0) a.ws_prefix[a.batch] = per_head_total;
+  }
+  if (j >= nwg) return;  // uniform across the workgroup
+  const long long start = (long long)j * total / nwg;
+  const long long end = (long long)(j + 1) * total / nwg;
+  // The thread whose sequences hold list position `start` finds it.
+  if ((long long)hkv * excl <= start && start < (long long)hkv * (excl + mine)) {
+    int acc = excl;
+    for (int bb = b_lo; bb < b_hi; ++bb) {
+      const int n = seg_tiles(a.ctx_lens[bb], W);
+      if (start < (long long)hkv * (acc + n)) {
+        s_first[0] = bb;
+        s_first[1] = acc;
+        break;
+      }
+      acc += n;
+    }
+  }
   __syncthreads();
 
-  const size_t row_bytes = (size_t)hkv * D * C::kEsz;
-  const char *kbase = (const char *)a.c.k + (size_t)hk * D * C::kEsz;
-  const char *vbase = (const char *)a.c.v + (size_t)hk * D * C::kEsz;
-  // Keys outside [k_begin, k_end) are clamped to a page of this split, so the
-  // address stays inside an assigned page; their data is masked or zeroed.
-  auto page_of = [&](int key) {
-    const int kc = min(max(key, k_begin), k_end - 1);
-    return s_pages[(kc >> lp) - pg0];
-  };
-  auto row_ptr = [&](const char *base, int key) {
-    return base + ((size_t)page_of(key) * P + (key & (P - 1))) * row_bytes;
-  };
-
-  // Q^T operand: lane (head column r16, k-group g).
   const int G = a.group;
   const bool head_ok = r16 < G;
-  const __bf16 *qrow = (const __bf16 *)a.q + ((size_t)b * a.num_q_heads + hk * G + (head_ok ? r16 : 0)) * D;
-  bf16x8 bq[C::kNst];
-#pragma unroll
-  for (int st = 0; st < C::kNst; ++st) {
-    const int dim = I8 ? 64 * (st >> 1) + 16 * g + 8 * (st & 1) : 32 * st + 8 * g;
-    uint4 raw = head_ok ? *reinterpret_cast<const uint4 *>(qrow + dim) : make_uint4(0, 0, 0, 0);
-    bq[st] = __builtin_bit_cast(bf16x8, raw);
-  }
-
-  auto load_tile = [&](int t, TileRegs<D, I8> &R) {
-    const int key0 = t * kDecTile;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int r = r16;
-      const int key = key0 + (I8 ? 8 * (r >> 2) + 4 * kb + (r & 3) : 16 * kb + r);
-      const char *rp = row_ptr(kbase, key);
-#pragma unroll
-      for (int j = 0; j < C::kKPerBlock; ++j) {
-        const int dim = I8 ? 64 * j + 16 * g : 32 * j + 8 * g;
-        R.k[kb * C::kKPerBlock + j] = *reinterpret_cast<const uint4 *>(rp + dim * C::kEsz);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::kVLoads; ++i) {
-      const int c = i * 64 + lane;
-      const char *rp = row_ptr(vbase, key0 + c / C::kCpr);
-      R.v[i] = *reinterpret_cast<const uint4 *>(rp + (c % C::kCpr) * 16);
-    }
-  };
-
-  float m = -INFINITY;
-  float lsum = 0.f;
-  f32x4 o[C::kNdb];
-#pragma unroll
-  for (int db = 0; db < C::kNdb; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int t0 = k_begin / kDecTile;
-  const int t1 = (k_end + kDecTile - 1) / kDecTile;
+  const uint32_t row_bytes = (uint32_t)hkv * D * C::kEsz;
+  const int lp = a.c.log2_page;
+  const uint32_t page_bytes = row_bytes << lp;
   unsigned char *vs = smem + w * kDecTile * C::kVRow;
-  TileRegs<D, I8> cur, nxt;
-  int t = t0 + w;
-  if (t < t1) load_tile(t, cur);
-  for (; t < t1; t += kDecWaves) {
-    const int key0 = t * kDecTile;
-    if (t + kDecWaves < t1) load_tile(t + kDecWaves, nxt);
 
-    // Stage this tile's V rows (zero outside [k_begin, k_end): those slots
-    // may hold anything, and 0 * NaN would poison the sum).
+  int b = s_first[0];
+  int nb = seg_tiles(a.ctx_lens[b], W);
+  const int r0 = (int)(start - (long long)hkv * s_first[1]);
+  int hk = r0 / nb;
+  int tloc = r0 - hk * nb;
+  long long remaining = end - start;
+
+  while (remaining > 0) {
+    const int len = (int)min((long long)(nb - tloc), remaining);
+    const int ctx = a.ctx_lens[b];
+    const int lo = W >= 0 ? max(0, ctx - 1 - W) : 0;
+    const int t_first = lo / kDecTile + tloc;  // first tile of this piece
+    const int k_begin = max(lo, t_first * kDecTile);
+    const int k_end = min(ctx, (t_first + len) * kDecTile);
+    const int n_w = (len - w + kDecWaves - 1) / kDecWaves;  // this wave's tiles
+    const uint32_t head_off = (uint32_t)hk * D * C::kEsz;
+    const int32_t *bt = block_table + (size_t)b * a.max_pages;
+
+    // Q^T operand: lane (head column r16, k-group g), same dim order as K.
+    const __bf16 *qrow = (const __bf16 *)a.q + ((size_t)b * a.num_q_heads + hk * G + (head_ok ? r16 : 0)) * D;
+    bf16x8 bq[C::kNst];
 #pragma unroll
-    for (int i = 0; i < C::kVLoads; ++i) {
-      const int c = i * 64 + lane;
-      const int row = c / C::kCpr;
-      const int key = key0 + row;
-      const uint4 val = (key >= k_begin && key < k_end) ? cur.v[i] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4 *>(vs + row * C::kVRow + (c % C::kCpr) * 16) = val;
+    for (int st = 0; st < C::kNst; ++st) {
+      const int dim = I8 ? 64 * (st >> 1) + 16 * g + 8 * (st & 1) : 32 * st + 8 * g;
+      uint4 raw = head_ok ? *reinterpret_cast<const uint4 *>(qrow + dim) : make_uint4(0, 0, 0, 0);
+      bq[st] = __builtin_bit_cast(bf16x8, raw);
     }
 
-    // S^T = K . Q^T for the two 16-key blocks.
-    f32x4 sacc[2];
+    // Addressing of the 16-key block kb of this wave's i-th tile.  Indices
+    // past the wave's last tile re-read that tile (already in cache; the
+    // registers are never consumed), so every load is unconditional and the
+    // compiler's wait counts stay exact.  Keys outside [k_begin, k_end) read
+    // the nearest valid row, which always lies in the block's own page
+    // (clamped block start; P >= 16), so the page id is wave-uniform.  Loads
+    // go through a buffer descriptor over that page (hardware range check;
+    // also keeps the loads opaque to load merging across the loop).
+    const int lo16 = k_begin & ~15;
+    const int hi16 = (k_end - 1) & ~15;
+    auto blk = [&](int i, int kb, const void *pool, uint32_t &off) {
+      const int t = t_first + w + kDecWaves * min(i, n_w - 1);
+      const int bs = min(max(t * kDecTile + 16 * kb, lo16), hi16);
+      const int key = min(max(t * kDecTile + 16 * kb + r16, k_begin), k_end - 1);
+      const size_t pbase = (size_t)bt[bs >> lp] * page_bytes + head_off;
+      off = (uint32_t)(key & ((1 << lp) - 1)) * row_bytes + 16 * g;
+      return make_rsrc((const char *)pool + pbase, page_bytes - head_off);
+    };
+    auto load_half = [&](int i, const void *pool, uint4 *dst) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 2; ++kb) {
+        uint32_t off;
+        const __amdgpu_buffer_rsrc_t r = blk(i, kb, pool, off);
 #pragma unroll
-      for (int st = 0; st < C::kNst; ++st) {
-        bf16x8 ka;
-        if constexpr (I8) {
-          const uint4 raw = cur.k[kb * C::kKPerBlock + (st >> 1)];
-          ka = (st & 1) ? i8x8_to_bf16x8(raw.z, raw.w) : i8x8_to_bf16x8(raw.x, raw.y);
-        } else {
-          ka = __builtin_bit_cast(bf16x8, cur.k[kb * C::kKPerBlock + st]);
+        for (int jj = 0; jj < C::kChunks; ++jj) dst[kb * C::kChunks + jj] = buf_load16(r, off + 64 * jj);
+      }
+    };
+
+    float m = -INFINITY;
+    float lsum = 0.f;
+    f32x4 o[C::kNdb];
+#pragma unroll
+    for (int db = 0; db < C::kNdb; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Register buffers recycled half by half: V(i) is staged to LDS and its
+    // registers take V(i + NB); K(i) feeds the QK product and its
+    // registers take K(i + NB).  NB tiles are in flight while a tile is
+    // computed.  The loop runs a multiple of NB steps; a step past the wave's last tile re-reads that tile and masks
+    // every key, which leaves (m, l, O) exactly unchanged.
+    auto step = [&](int i, TileRegs<D, I8> &R) {
+      const int key0 = (t_first + w + kDecWaves * i) * kDecTile;
+      // Stage V rows for the transposed reads.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < C::kChunks; ++jj)
+          *reinterpret_cast<uint4 *>(vs + v_row<I8>(16 * kb + r16) * C::kVRow + 64 * jj + 16 * g) =
+              R.v[kb * C::kChunks + jj];
+      load_half(i + NB, a.c.v, R.v);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the K wait
+
+      // S^T = K . Q^T for the two 16-key blocks (keys on M, heads on N).
+      f32x4 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < C::kNst; ++st) {
+          bf16x8 ka;
+          if constexpr (I8) {
+            const uint4 raw = R.k[kb * C::kChunks + (st >> 1)];
+            ka = (st & 1) ? i8x8_to_bf16x8(raw.z, raw.w) : i8x8_to_bf16x8(raw.x, raw.y);
+          } else {
+            ka = __builtin_bit_cast(bf16x8, R.k[kb * C::kChunks + st]);
+          }
+          sacc[kb] = mfma16(ka, bq[st], sacc[kb]);
         }
-        sacc[kb] = mfma16(ka, bq[st], sacc[kb]);
       }
-    }
+      load_half(i + NB, a.c.k, R.k);
+      __builtin_amdgcn_sched_barrier(0);
 
-    float sl = a.scale_log2;
-    float vsc = 1.f;
-    if constexpr (I8) {
-      const int page = page_of(key0 + 8 * g);
-      sl *= a.c.k_scales[(size_t)page * hkv + hk];
-      vsc = a.c.v_scales[(size_t)page * hkv + hk];
-    }
-    const bool edge = key0 < k_begin || key0 + kDecTile > k_end;
-    float x[2][4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = key0 + tile_key<I8>(kb, g, i);
-        float v = sacc[kb][i] * sl;
-        if (edge && (key < k_begin || key >= k_end)) v = -INFINITY;
-        x[kb][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = wave_max_xor(mx, 16);
-    mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(m, mx);  // finite: every tile holds a visible key
-    const float corr = fast_exp2(m - m_new);
-    float ps = 0.f;
-    bf16x8 bp;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(x[kb][i] - m_new);
-        ps += p;
-        bp[kb * 4 + i] = (__bf16)(p * vsc);
-      }
-    lsum = lsum * corr + ps;
-    m = m_new;
-
-    // O^T += V^T . P^T, V^T read transposed from the staged rows.
-#pragma unroll
-    for (int db = 0; db < C::kNdb; ++db) {
-      bf16x8 va;
+      // Scale (with the page's K scale for int8), mask, online softmax.
+      float sl[2] = {a.scale_log2, a.scale_log2};
+      float vsc[2] = {1.f, 1.f};
       if constexpr (I8) {
-        const unsigned char *p1 = vs + (8 * g + (r16 >> 1)) * C::kVRow + db * 16 + 8 * (r16 & 1);
-        const i32x2 raw = lds_read_tr8(p1);
-        va = i8x8_to_bf16x8((uint32_t)raw[0], (uint32_t)raw[1]);
-      } else {
-        const unsigned char *p1 = vs + (4 * g + (r16 >> 2)) * C::kVRow + (db * 16 + 4 * (r16 & 3)) * 2;
-        va = cat(lds_read_tr16(p1), lds_read_tr16(p1 + 16 * C::kVRow));
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int bs = min(max(key0 + 16 * kb, lo16), hi16);
+          const int page = bt[bs >> lp];
+          sl[kb] *= k_scales[(size_t)page * hkv + hk];
+          vsc[kb] = v_scales[(size_t)page * hkv + hk];
+        }
       }
-      o[db] *= corr;
-      o[db] = mfma16(va, bp, o[db]);
-    }
-    cur = nxt;
-  }
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
+      float x[2][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = key0 + 16 * kb + 4 * g + r;
+          const bool vis = key >= k_begin && key < k_end;
+          x[kb][r] = vis ? sacc[kb][r] * sl[kb] : -INFINITY;
+          mx = fmaxf(mx, x[kb][r]);
+        }
+      mx = max_xor32(max_xor16(mx));
+      const float m_new = fmaxf(m, mx);
+      // Rescale only when some head's running max grew (otherwise the factor
+      // is exp2(0) = 1 for every lane).
+      if (__any(m_new > m)) {
+        const float corr = fast_exp2(m - m_new);
+        lsum *= corr;
+#pragma unroll
+        for (int db = 0; db < C::kNdb; ++db) o[db] *= corr;
+        m = m_new;
+      }
+      // m is -inf only before the first visible key, and a wave's first
+      // tile always holds one, so the exponents below are of finite numbers
+      // or -inf (masked keys -> 0).
+      float ps = 0.f;
+      bf16x8 bp;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(x[kb][r] - m);
+          ps += p;
+          bp[kb * 4 + r] = (__bf16)(p * vsc[kb]);
+        }
+      lsum += ps;
 
-  // Merge the 4 waves' (m, l, O) through LDS.
-  __syncthreads();
-  float *wo = reinterpret_cast<float *>(smem);
-  float *wm = wo + kDecWaves * 16 * D;
-  float *wl = wm + kDecWaves * 16;
-  if (head_ok) {
+      // O^T += V^T . P^T, V^T read transposed from the staged rows.
 #pragma unroll
-    for (int db = 0; db < C::kNdb; ++db)
+      for (int db = 0; db < C::kNdb; ++db) {
+        bf16x8 va;
+        if constexpr (I8) {
+          const unsigned char *p1 = vs + (8 * g + (r16 >> 1)) * C::kVRow + db * 16 + 8 * (r16 & 1);
+          const i32x2 raw = lds_read_tr8(p1);
+          va = i8x8_to_bf16x8((uint32_t)raw[0], (uint32_t)raw[1]);
+        } else {
+          const unsigned char *p1 = vs + (4 * g + (r16 >> 2)) * C::kVRow + (db * 16 + 4 * (r16 & 3)) * 2;
+          va = cat(lds_read_tr16(p1), lds_read_tr16(p1 + 16 * C::kVRow));
+        }
+        o[db] = mfma16(va, bp, o[db]);
+      }
+    };
+
+    // The first loads are issued even by a wave without tiles (they read
+    // valid rows of the piece), so the wait counts are the same on every path.
+    // Issue order is pinned (sched_barrier) so that waiting for one tile
+    // never waits for a later one.
+    TileRegs<D, I8> R[NB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wo[(w * 16 + r16) * D + db * 16 + 4 * g + i] = o[db][i];
-    if (g == 0) {
-      wm[w * 16 + r16] = m;
-      wl[w * 16 + r16] = lsum;
+    for (int u = 0; u < NB; ++u) {
+      load_half(u, a.c.v, R[u].v);
+      __builtin_amdgcn_sched_barrier(0);
+      load_half(u, a.c.k, R[u].k);
+      __builtin_amdgcn_sched_barrier(0);
     }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-    const int c = e / D;
-    const int d = e % D;
-    float big_m = -INFINITY;
+    for (int i = 0; i < n_w; i += NB) {
 #pragma unroll
-    for (int ww = 0; ww < kDecWaves; ++ww) big_m = fmaxf(big_m, wm[ww * 16 + c]);
-    float big_l = 0.f, acc = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kDecWaves; ++ww) {
-      const float f = fast_exp2(wm[ww * 16 + c] - big_m);
-      big_l += wl[ww * 16 + c] * f;
-      acc += wo[(ww * 16 + c) * D + d] * f;
+      for (int u = 0; u < NB; ++u) step(i + u, R[u]);
     }
-    const size_t idx = ((size_t)b * a.num_q_heads + hk * G + c) * a.max_splits + split;
-    a.ws_o[idx * D + d] = acc;
-    if (d == 0) {
-      a.ws_ml[idx * 2] = big_m;
-      a.ws_ml[idx * 2 + 1] = big_l;
+    lsum = sum_xor32(sum_xor16(lsum));
+
+    // Merge the 4 waves' (m, l, O) through LDS (a wave without tiles has
+    // m = -inf, l = 0, O = 0 and drops out) and write this piece's partial.
+    __syncthreads();
+    float *wo = reinterpret_cast<float *>(smem);
+    float *wm = wo + kDecWaves * 16 * D;
+    float *wl = wm + kDecWaves * 16;
+    if (head_ok) {
+#pragma unroll
+      for (int db = 0; db < C::kNdb; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wo[(w * 16 + r16) * D + db * 16 + 4 * g + r] = o[db][r];
+      if (g == 0) {
+        wm[w * 16 + r16] = m;
+        wl[w * 16 + r16] = lsum;
+      }
+    }
+    __syncthreads();
+    const size_t slot = (size_t)b * hkv + hk + j;
+    for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+      const int c = e / D;
+      const int d = e - c * D;
+      float big_m = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < kDecWaves; ++ww) big_m = fmaxf(big_m, wm[ww * 16 + c]);
+      float big_l = 0.f, acc = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kDecWaves; ++ww) {
+        const float mw = wm[ww * 16 + c];
+        const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - big_m);
+        big_l += wl[ww * 16 + c] * f;
+        acc += wo[(ww * 16 + c) * D + d] * f;
+      }
+      a.ws_o[(slot * G + c) * D + d] = acc;
+      if (d == 0) {
+        a.ws_ml[(slot * G + c) * 2] = big_m;
+        a.ws_ml[(slot * G + c) * 2 + 1] = big_l;
+      }
+    }
+    __syncthreads();  // the LDS is staged into again by the next piece
+
+    remaining -= len;
+    tloc = 0;
+    if (++hk == hkv && remaining > 0) {
+      hk = 0;
+      ++b;
+      nb = seg_tiles(a.ctx_lens[b], W);
     }
   }
 }
 
-// Merge the splits of one (sequence, query head): M = max m_s,
-// L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M) / L.
+// Merge the partials of one (sequence, KV head) segment for its G query
+// heads: M = max m_s, L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M) / L,
+// accumulated in one pass with the same running rescale as the online
+// softmax.  The workgroups that touched the segment are those whose list
+// ranges contain its first and last tiles and every one in between.  A
+// thread owns 4 consecutive dims of one query head.
 template <int D>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
-  const int h = blockIdx.x;
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
+  const int hk = blockIdx.x;
   const int b = blockIdx.y;
-  const int ctx = a.ctx_lens[b];
-  const int S = a.split_tokens;
-  const int lo = a.window_left >= 0 ? max(0, ctx - 1 - a.window_left) : 0;
-  const int s_lo = lo / S;
-  const int s_hi = (ctx - 1) / S;
-  const size_t base = ((size_t)b * a.num_q_heads + h) * a.max_splits;
-  float big_m = -INFINITY;
-  for (int s = s_lo; s <= s_hi; ++s) big_m = fmaxf(big_m, a.ws_ml[(base + s) * 2]);
-  constexpr int kPer = D / 64;
-  float acc[kPer] = {};
-  float big_l = 0.f;
-  for (int s = s_lo; s <= s_hi; ++s) {
-    const float f = fast_exp2(a.ws_ml[(base + s) * 2] - big_m);
-    big_l += a.ws_ml[(base + s) * 2 + 1] * f;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) acc[j] += a.ws_o[(base + s) * D + threadIdx.x + 64 * j] * f;
+  const int hkv = a.c.num_kv_heads;
+  const int G = a.group;
+  const long long total = (long long)hkv * a.ws_prefix[a.batch];
+  const int nwg = active_wgs(total, a.nwg);
+  const int nb = seg_tiles(a.ctx_lens[b], a.window_left);
+  const long long f0 = (long long)hkv * a.ws_prefix[b] + (long long)hk * nb;
+  const long long f1 = f0 + nb - 1;
+  // Workgroup holding list position f: the largest j with j*total/nwg <= f.
+  const int j_lo = (int)(((f0 + 1) * nwg - 1) / total);
+  const int j_hi = (int)(((f1 + 1) * nwg - 1) / total);
+  const size_t seg = (size_t)b * hkv + hk;
+  for (int e = 4 * threadIdx.x; e < G * D; e += 4 * blockDim.x) {
+    const int c = e / D;
+    const int d = e - c * D;
+    float m = -INFINITY, l = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int jj = j_lo; jj <= j_hi; ++jj) {
+      const size_t idx = (seg + jj) * G + c;
+      const float2 ml = *reinterpret_cast<const float2 *>(a.ws_ml + idx * 2);
+      const f32x4 ov = *reinterpret_cast<const f32x4 *>(a.ws_o + idx * D + d);
+      const float m_new = fmaxf(m, ml.x);
+      const float f_old = fast_exp2(m - m_new);  // 0 on the first piece
+      const float f_new = fast_exp2(ml.x - m_new);
+      l = l * f_old + ml.y * f_new;
+      acc = acc * f_old + ov * f_new;
+      m = m_new;
+    }
+    const float inv = 1.f / l;
+    const uint32_t lo = f32_to_bf16_bits(acc[0] * inv) | ((uint32_t)f32_to_bf16_bits(acc[1] * inv) << 16);
+    const uint32_t hi = f32_to_bf16_bits(acc[2] * inv) | ((uint32_t)f32_to_bf16_bits(acc[3] * inv) << 16);
+    const size_t orow = ((size_t)b * a.num_q_heads + hk * G + c) * D;
+    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + orow + d) = make_uint2(lo, hi);
+    if (a.lse != nullptr && d == 0)
+      a.lse[(size_t)b * a.num_q_heads + hk * G + c] = (m + __log2f(l)) * kLn2;
   }
-  const float inv = 1.f / big_l;
-  uint16_t *out = (uint16_t *)a.out + ((size_t)b * a.num_q_heads + h) * D;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) out[threadIdx.x + 64 * j] = f32_to_bf16_bits(acc[j] * inv);
-  if (a.lse != nullptr && threadIdx.x == 0)
-    a.lse[(size_t)b * a.num_q_heads + h] = (big_m + __log2f(big_l)) * kLn2;
 }
 
 // fp32 caches: one wave per (query row, head), keys one per lane, the same
@@ -410,21 +573,23 @@ hipError_t launch_rowwise_f32(const PrefillArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, bool I8>
+template <int D, bool I8, int NB, int WPC>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
-  dim3 grid(a.max_splits, a.c.num_kv_heads, a.batch);
-  hipLaunchKernelGGL((decode_split_kernel<D, I8>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_split_kernel<D, I8, NB, WPC>), dim3(a.nwg), dim3(256), 0, s, a, a.block_table,
+                     a.c.k_scales, a.c.v_scales);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(a.num_q_heads, a.batch), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(a.c.num_kv_heads, a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
   const bool i8 = a.c.dtype == 2;
-  if (a.c.head_dim == 64) return i8 ? launch_decode_t<64, true>(a, s) : launch_decode_t<64, false>(a, s);
-  return i8 ? launch_decode_t<128, true>(a, s) : launch_decode_t<128, false>(a, s);
+  // Tiles in flight per wave: 1 for bf16 (16 KB), 2 for int8 (8 KB each).
+  if (a.c.head_dim == 64)
+    return i8 ? launch_decode_t<64, true, 2, kDecWgsPerCu>(a, s) : launch_decode_t<64, false, 1, kDecWgsPerCu>(a, s);
+  return i8 ? launch_decode_t<128, true, 2, kDecWgsPerCu>(a, s) : launch_decode_t<128, false, 1, kDecWgsPerCu>(a, s);
 }
 
 }  // namespace pa

@@ -79,14 +79,15 @@ struct DecodeArgs {
   int window_left;
   void *out;
   float *lse;
-  float *ws_o;         // [batch, Hq, max_splits, head_dim]
-  float *ws_ml;        // [batch, Hq, max_splits, 2]  (max in log2 units, sum)
-  int split_tokens;    // keys per split: a multiple of 128 and of page_size
-  int max_splits;
+  float *ws_o;         // [slots, G, head_dim] partial outputs (unnormalised)
+  float *ws_ml;        // [slots, G, 2] partial (max in log2 units, sum)
+  int32_t *ws_prefix;  // [batch + 1] tiles per KV head before sequence b; total last
+  int nwg;             // workgroups launched; slots = batch * Hkv + nwg
 };
 
-// Decode split geometry used by both the workspace query and the call.
-int decode_split_tokens(int batch, int num_kv_heads, int max_pages_per_seq, int page_size);
+// Decode grid size (workgroups) on the current device, used by both the
+// workspace query and the call.
+int decode_grid_size();
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);

@@ -212,14 +212,20 @@ def test_prefill_page_shuffle_is_bitwise_identical():
     assert np.array_equal(bits(out1), bits(out3))
 
 
-def test_decode_split_override_gives_same_result_within_tolerance(monkeypatch):
-    w = wl.DecodeWorkload("splits", 3, 2000, 4000, 16, 2, 128, 16, "bf16", seed=54)
+@pytest.mark.parametrize("wgs", ["1", "7", "64", "5000"])
+def test_decode_other_grid_sizes_match_oracle(monkeypatch, wgs):
+    """The balanced decode partition cuts the (sequence, KV head, tile) list
+    into as many equal ranges as there are workgroups; any grid size must
+    give the same attention within tolerance (pieces, partial slots and the
+    merge all move with it)."""
+    w = wl.DecodeWorkload("grids", 5, 0, 0, 16, 2, 128, 16, "bf16", seed=54,
+                          ctx_lens=(1, 33, 700, 4000, 2500))
     run = DecodeRun(w)
     base = run.run(return_lse=False)
-    monkeypatch.setenv("PAGEDATTN_SPLIT_TOKENS", "128")
-    say("decode with 128-key splits")
-    small = run.run(return_lse=False)
+    monkeypatch.setenv("PAGEDATTN_DECODE_WGS", wgs)
+    say(f"decode with {wgs} workgroups")
+    other = run.run(return_lse=False)
     torch.cuda.synchronize()
     (ref, _), _ = run.oracle()
-    check_close(small, ref, "bf16", "128-key splits")
-    assert (small.double() - base.double()).abs().max().item() <= 2e-2
+    check_close(other, ref, "bf16", f"{wgs} workgroups")
+    assert (other.double() - base.double()).abs().max().item() <= 2e-2
