@@ -479,8 +479,8 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
       m = m_new;
     }
     const float inv = 1.f / l;
-    const uint32_t lo = f32_to_bf16_bits(acc[0] * inv) | ((uint32_t)f32_to_bf16_bits(acc[1] * inv) << 16);
-    const uint32_t hi = f32_to_bf16_bits(acc[2] * inv) | ((uint32_t)f32_to_bf16_bits(acc[3] * inv) << 16);
+    const uint32_t lo = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    const uint32_t hi = pack_bf16x2(acc[2] * inv, acc[3] * inv);
     const size_t orow = ((size_t)b * a.num_q_heads + hk * G + c) * D;
     *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + orow + d) = make_uint2(lo, hi);
     if (a.lse != nullptr && d == 0)

@@ -11,17 +11,29 @@
 // query head h reading KV head h / G ("LLM推理系统优化：KV缓存管理与动态批处理
 // 技术" section 2.1).
 //
-// Work split: one workgroup of 4 waves = 128 query rows of one (sequence,
-// query head); wave w owns rows 32w..32w+31.  Query tiles are launched last
-// tile first, so the longest causal rows start earliest.  For each 64-key
-// tile, K and V rows are gathered from their pages into LDS; each wave
-// computes S^T = K . Q^T (v_mfma_f32_32x32x16_bf16, keys on M, its 32 query
-// rows on N, Q^T held in registers for the whole loop), applies the mask and
-// the online softmax to the S^T registers (one query per lane column, so only
-// one cross-lane max per tile), and accumulates O^T += V^T . P^T with V^T read
-// transposed from LDS by ds_read_b64_tr_b16 and P^T taken straight from the
-// S^T registers (rounded to bf16).  exp is computed as exp2 with log2(e)
-// folded into the scale.
+// Work split.  Query rows are cut into 128-row tiles; a tile's work is the
+// list of 64-key tiles it can see.  One workgroup of 8 waves takes the pair
+// of query tiles (p, n-1-p) of one (sequence, query head): under a causal
+// mask their key-tile counts add up to the same total for every p, so all
+// workgroups carry equal work.  The workgroup is two engines of 4 waves.
+// The pair's work list (tile p's key tiles, then tile n-1-p's) is consumed
+// from both ends, engine 0 forward and engine 1 backward, so each engine
+// does half; the one query tile the engines meet in is merged in LDS at the
+// end with the same rescaling algebra as the online softmax.  Each engine
+// has its own double-buffered K/V tiles in LDS and prefetches the next key
+// tile into registers while it computes the current one: one barrier per
+// step for the whole workgroup (both engines run the same number of steps).
+//
+// Per step a wave (32 query rows) computes S^T = K . Q^T with
+// v_mfma_f32_32x32x16_bf16 (keys on M, its rows on N, Q^T in registers),
+// the mask and the online softmax on the S^T registers (one query per lane
+// column: one cross-lane max per tile), and O^T += V^T . P^T with V^T read
+// transposed from LDS by ds_read_b64_tr_b16 and P^T straight from the S^T
+// registers (rounded to bf16).  exp is exp2 with log2(e) folded into the
+// scale.  The running output is rescaled only when a row's maximum grows by
+// more than 2^8 over its reference (the exponent reference may lag the true
+// maximum by at most that much: probabilities stay <= 256, and O and l share
+// the reference, so the result is the same attention).
 #include <math.h>
 
 #include "pa_device.h"
@@ -31,48 +43,87 @@ namespace pa {
 
 hipError_t launch_rowwise_f32(const PrefillArgs &a, hipStream_t s);
 
-constexpr int kPfRows = 128;
-constexpr int kPfKeys = 64;
+constexpr int kPfRows = 128;         // query rows per query tile (4 waves x 32)
+constexpr int kPfKeys = 64;          // keys per key tile
+constexpr int kPfEngineThreads = 256;
+constexpr float kPfSlack = 8.f;      // log2 of the largest probability allowed
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
-  constexpr int kKRow = 2 * D + 16;  // staged K row bytes (bank spread for b128 reads)
-  constexpr int kVRow = 2 * D + 64;  // staged V row bytes (bank spread for transpose reads)
-  constexpr int kCpr = D / 8;        // 16-byte chunks per row
-  constexpr int kNs = D / 16;        // QK k-steps
-  constexpr int kNdb = D / 32;       // O^T 32-dim blocks
-  __shared__ __align__(16) unsigned char ks[kPfKeys * kKRow];
-  __shared__ __align__(16) unsigned char vs[kPfKeys * kVRow];
+struct PfCfg {
+  static constexpr int kKRow = 2 * D + 16;   // staged K row bytes (bank spread for b128 reads)
+  static constexpr int kVRow = 2 * D + 64;   // staged V row bytes (bank spread for transpose reads)
+  static constexpr int kCpr = D / 8;         // 16-byte chunks per row
+  static constexpr int kNs = D / 16;         // QK k-steps
+  static constexpr int kNdb = D / 32;        // O^T 32-dim blocks
+  static constexpr int kKBuf = kPfKeys * kKRow;
+  static constexpr int kVBuf = kPfKeys * kVRow;
+  static constexpr int kEngine = 2 * (kKBuf + kVBuf);                   // two K/V buffers
+  static constexpr int kLoads = kPfKeys * kCpr / kPfEngineThreads;      // per thread per tile, K and V each
+  // Final merge: a lane's O^T values, then its (m, l).
+  static constexpr int kMergeLane = 16 * kNdb + 4;
+  static_assert(4 * 64 * kMergeLane * 4 <= kEngine, "merge area must fit one engine's buffers");
+};
 
+template <int D>
+__global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a) {
+  using C = PfCfg<D>;
+  __shared__ __align__(16) unsigned char smem[2 * C::kEngine];
+
+  const int eng = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);  // 0: forward, 1: backward
+  const int tid = threadIdx.x & (kPfEngineThreads - 1);
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int h = blockIdx.x;
-  const int qt = gridDim.y - 1 - blockIdx.y;
-  const int b = blockIdx.z;
-  const int q0 = a.cu_q[b];
-  const int q_len = a.cu_q[b + 1] - q0;
-  if (qt * kPfRows >= q_len) return;
-  const int ctx = a.ctx_lens[b];
-  const int off = ctx - q_len;
-  const int hk = h / a.group;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);             // wave inside the engine
   const int col = lane & 31;
   const int g = lane >> 5;
-  const int qrow = qt * kPfRows + w * 32 + col;
-  const int pos = off + qrow;
+  const int gam = lane >> 4;
+  const int tp = lane & 15;
+
+  const int pair = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  // Sequence geometry is the same for every lane: readfirstlane keeps it
+  // (and every tile decision derived from it) in scalar registers.
+  const int q0 = __builtin_amdgcn_readfirstlane(a.cu_q[b]);
+  const int q_len = __builtin_amdgcn_readfirstlane(a.cu_q[b + 1]) - q0;
+  const int n_qt = (q_len + kPfRows - 1) / kPfRows;
+  if (pair >= (n_qt + 1) / 2) return;  // uniform
+  const int ctx = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
+  const int off = ctx - q_len;
+  const int hk = h / a.group;
   const int W = a.window_left;
   const int causal = a.causal;
 
-  // Q^T operand: lane (query column col, k-group g), dims 16s + 8g .. +7.
-  const __bf16 *qp = (const __bf16 *)a.q + ((size_t)(q0 + min(qrow, q_len - 1)) * a.num_q_heads + h) * D;
-  bf16x8 bq[kNs];
-#pragma unroll
-  for (int s = 0; s < kNs; ++s) bq[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp + 16 * s + 8 * g));
+  // Visible key tiles [lo, hi) of query tile qt.
+  auto tile_range = [&](int qt, int &lo, int &hi) {
+    const int p_first = off + qt * kPfRows;
+    const int p_last = off + min(qt * kPfRows + kPfRows - 1, q_len - 1);
+    const int k_lo = W >= 0 ? max(0, p_first - W) : 0;
+    const int k_hi = causal ? min(p_last + 1, ctx) : ctx;
+    lo = k_lo / kPfKeys;
+    hi = (k_hi + kPfKeys - 1) / kPfKeys;
+  };
+  const int qa = pair;
+  const int qb = n_qt - 1 - pair;
+  int lo_a, hi_a, lo_b = 0, hi_b = 0;
+  tile_range(qa, lo_a, hi_a);
+  if (qb != qa) tile_range(qb, lo_b, hi_b);
+  const int na = hi_a - lo_a;
+  const int total = na + (hi_b - lo_b);
+  const int half = (total + 1) / 2;
+  const int n_mine = eng == 0 ? half : total - half;
+  // Work item i of the pair's list -> (query tile, key tile).
+  auto item = [&](int i, int &qt, int &kt) {
+    if (i < na) {
+      qt = qa;
+      kt = lo_a + i;
+    } else {
+      qt = qb;
+      kt = lo_b + (i - na);
+    }
+  };
+  auto my_item = [&](int t, int &qt, int &kt) { item(eng == 0 ? t : total - 1 - t, qt, kt); };
 
-  const int p_first = off + qt * kPfRows;
-  const int p_last = off + min(qt * kPfRows + kPfRows - 1, q_len - 1);
-  const int k_lo = W >= 0 ? max(0, p_first - W) : 0;
-  const int k_hi = causal ? min(p_last + 1, ctx) : ctx;  // exclusive
-
+  unsigned char *ebase = smem + eng * C::kEngine;
   const int P = a.c.page_size;
   const int lp = a.c.log2_page;
   const size_t row_bytes = (size_t)a.c.num_kv_heads * D * 2;
@@ -80,32 +131,84 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   const char *vbase = (const char *)a.c.v + (size_t)hk * D * 2;
   const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
 
-  float m = -INFINITY;
-  float lsum = 0.f;
-  f32x16 o[kNdb];
+  // Prefetch of one key tile: thread `tid` moves chunks tid + 256 i (row =
+  // chunk / kCpr).  Keys at or beyond ctx are not read (their slots may hold
+  // anything) and stage as zeros; they are masked.
+  uint4 pk[C::kLoads], pv[C::kLoads];
+  auto load_tile = [&](int kt) {
 #pragma unroll
-  for (int db = 0; db < kNdb; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-
-  const int gam = lane >> 4;
-  const int tp = lane & 15;
-  for (int key0 = (k_lo / kPfKeys) * kPfKeys; key0 < k_hi; key0 += kPfKeys) {
-    __syncthreads();
-    for (int c = threadIdx.x; c < kPfKeys * kCpr; c += blockDim.x) {
-      const int row = c / kCpr;
-      const int ch = c % kCpr;
-      const int key = key0 + row;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < C::kLoads; ++i) {
+      const int c = tid + kPfEngineThreads * i;
+      const int key = kt * kPfKeys + c / C::kCpr;
+      pk[i] = make_uint4(0, 0, 0, 0);
+      pv[i] = make_uint4(0, 0, 0, 0);
       if (key < ctx) {
-        const size_t ro = ((size_t)bt[key >> lp] * P + (key & (P - 1))) * row_bytes + ch * 16;
-        kv = *reinterpret_cast<const uint4 *>(kbase + ro);
-        vv = *reinterpret_cast<const uint4 *>(vbase + ro);
+        const size_t ro = ((size_t)bt[key >> lp] * P + (key & (P - 1))) * row_bytes + (c % C::kCpr) * 16;
+        pk[i] = *reinterpret_cast<const uint4 *>(kbase + ro);
+        pv[i] = *reinterpret_cast<const uint4 *>(vbase + ro);
       }
-      *reinterpret_cast<uint4 *>(ks + row * kKRow + ch * 16) = kv;
-      *reinterpret_cast<uint4 *>(vs + row * kVRow + ch * 16) = vv;
     }
-    __syncthreads();
+  };
+  auto store_tile = [&](int buf) {
+    unsigned char *ks = ebase + buf * (C::kKBuf + C::kVBuf);
+    unsigned char *vs = ks + C::kKBuf;
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+      const int c = tid + kPfEngineThreads * i;
+      const int row = c / C::kCpr;
+      const int ch = c % C::kCpr;
+      *reinterpret_cast<uint4 *>(ks + row * C::kKRow + ch * 16) = pk[i];
+      *reinterpret_cast<uint4 *>(vs + row * C::kVRow + ch * 16) = pv[i];
+    }
+  };
+
+  // Per-wave state of the query tile being worked on.
+  int qt_cur = -1;
+  bf16x8 bq[C::kNs];
+  float m = -INFINITY;  // exponent reference of this lane's row (log2 units)
+  float lsum = 0.f;     // this lane's half of the row sum
+  f32x16 o[C::kNdb];
+
+  auto start = [&](int qt) {
+    const int qrow = qt * kPfRows + w * 32 + col;
+    const __bf16 *qp = (const __bf16 *)a.q + ((size_t)(q0 + min(qrow, q_len - 1)) * a.num_q_heads + h) * D;
+#pragma unroll
+    for (int s = 0; s < C::kNs; ++s)
+      bq[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp + 16 * s + 8 * g));
+    m = -INFINITY;
+    lsum = 0.f;
+#pragma unroll
+    for (int db = 0; db < C::kNdb; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  };
+  // Normalise and store this wave's rows of query tile qt.
+  auto finish = [&](int qt, float m_row, float l_half, const f32x16 *acc) {
+    const int qrow = qt * kPfRows + w * 32 + col;
+    const float ltot = l_half + __shfl_xor(l_half, 32, 64);
+    if (qrow < q_len) {
+      const float inv = 1.f / ltot;
+      uint16_t *orow = (uint16_t *)a.out + ((size_t)(q0 + qrow) * a.num_q_heads + h) * D;
+#pragma unroll
+      for (int db = 0; db < C::kNdb; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = pack_bf16x2(acc[db][4 * j] * inv, acc[db][4 * j + 1] * inv);
+          const uint32_t hi = pack_bf16x2(acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv);
+          *reinterpret_cast<uint2 *>(orow + db * 32 + j * 8 + g * 4) = make_uint2(lo, hi);
+        }
+      if (a.lse != nullptr && g == 0)
+        a.lse[(size_t)(q0 + qrow) * a.num_q_heads + h] = (m_row + __log2f(ltot)) * kLn2;
+    }
+  };
+
+  auto compute = [&](int qt, int kt, int buf) {
+    const unsigned char *ks = ebase + buf * (C::kKBuf + C::kVBuf);
+    const unsigned char *vs = ks + C::kKBuf;
+    const int key0 = kt * kPfKeys;
+    const int pos = off + qt * kPfRows + w * 32 + col;
+    const int p_first = off + qt * kPfRows;
+    const int p_last = off + min(qt * kPfRows + kPfRows - 1, q_len - 1);
 
     // S^T = K . Q^T: two 32-key blocks.
     f32x16 sacc[2];
@@ -114,89 +217,152 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
-      for (int s = 0; s < kNs; ++s) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(ks + (kb * 32 + col) * kKRow + (16 * s + 8 * g) * 2);
+      for (int s = 0; s < C::kNs; ++s) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(ks + (kb * 32 + col) * C::kKRow + (16 * s + 8 * g) * 2);
         sacc[kb] = mfma32(ka, bq[s], sacc[kb]);
       }
     }
 
-    // Mask (only tiles that cross a boundary) and online softmax.
+    // Mask (only tiles that cross a boundary) and online softmax.  This
+    // lane's row sees keys [klo, khi].
     const bool edge = (causal && key0 + kPfKeys - 1 > p_first) || (W >= 0 && key0 < p_last - W) ||
                       (key0 + kPfKeys > ctx);
-    float x[2][16];
+    const int khi = causal ? min(pos, ctx - 1) : ctx - 1;
+    const int klo = W >= 0 ? pos - W : 0;
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = key0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
         float v = sacc[kb][i] * a.scale_log2;
         if (edge) {
-          const bool vis = key < ctx && (!causal || key <= pos) && (W < 0 || pos - key <= W);
-          v = vis ? v : -INFINITY;
+          const int key = key0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+          v = (key >= klo) & (key <= khi) ? v : -INFINITY;
         }
-        x[kb][i] = v;
+        sacc[kb][i] = v;
         mx = fmaxf(mx, v);
       }
-    mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(m, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // row has seen no key yet
-    const float corr = fast_exp2(m - m_use);
+    mx = max_xor32(mx);
+    if (__any(mx > m + kPfSlack)) {
+      // New reference for every lane of the wave (a lane whose max did not
+      // grow keeps a factor of 1).  A row without a visible key yet keeps
+      // m = -inf and factor 1.
+      const float m_new = fmaxf(m, mx);
+      const float corr = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
+      lsum *= corr;
+#pragma unroll
+      for (int db = 0; db < C::kNdb; ++db) o[db] *= corr;
+      m = m_new;
+    }
+    const float m_use = m == -INFINITY ? 0.f : m;
     float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        x[kb][i] = fast_exp2(x[kb][i] - m_use);
-        ps += x[kb][i];
+        sacc[kb][i] = fast_exp2(sacc[kb][i] - m_use);
+        ps += sacc[kb][i];
       }
-    lsum = lsum * corr + ps;
-    m = m_new;
-#pragma unroll
-    for (int db = 0; db < kNdb; ++db) o[db] *= corr;
+    lsum += ps;
 
     // O^T += V^T . P^T over four 16-key steps.
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int kb = t >> 1;
-      const int half = t & 1;
+      const int hf = t & 1;
       bf16x8 bp;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) bp[e] = (__bf16)x[kb][8 * half + e];
-      const int r0 = kb * 32 + half * 16 + g * 4;
+      for (int e = 0; e < 8; ++e) bp[e] = (__bf16)sacc[kb][8 * hf + e];
+      const int r0 = kb * 32 + hf * 16 + g * 4;
 #pragma unroll
-      for (int db = 0; db < kNdb; ++db) {
-        const unsigned char *p1 = vs + (r0 + (tp >> 2)) * kVRow + (db * 32 + 16 * (gam & 1) + 4 * (tp & 3)) * 2;
-        const bf16x8 va = cat(lds_read_tr16(p1), lds_read_tr16(p1 + 8 * kVRow));
+      for (int db = 0; db < C::kNdb; ++db) {
+        const unsigned char *p1 = vs + (r0 + (tp >> 2)) * C::kVRow + (db * 32 + 16 * (gam & 1) + 4 * (tp & 3)) * 2;
+        const bf16x8 va = cat(lds_read_tr16(p1), lds_read_tr16(p1 + 8 * C::kVRow));
         o[db] = mfma32(va, bp, o[db]);
       }
     }
+  };
+
+  // Both engines run `half` steps so that they meet every barrier; an engine
+  // with fewer items idles in its last step.
+  if (n_mine > 0) {
+    int qt, kt;
+    my_item(0, qt, kt);
+    load_tile(kt);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < half; ++t) {
+    const bool active = t < n_mine;
+    const bool has_next = t + 1 < n_mine;
+    if (has_next) {
+      int qt_n, kt_n;
+      my_item(t + 1, qt_n, kt_n);
+      load_tile(kt_n);
+    }
+    if (active) {
+      int qt, kt;
+      my_item(t, qt, kt);
+      if (qt != qt_cur) {
+        if (qt_cur >= 0) finish(qt_cur, m, lsum, o);
+        start(qt);
+        qt_cur = qt;
+      }
+      compute(qt, kt, t & 1);
+    }
+    if (has_next) store_tile((t + 1) & 1);
+    __syncthreads();
   }
 
-  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
-  if (qrow < q_len) {
-    const float inv = 1.f / ltot;
-    uint16_t *orow = (uint16_t *)a.out + ((size_t)(q0 + qrow) * a.num_q_heads + h) * D;
+  // The query tile of items half-1 and half, if they are the same, has a
+  // partial result in each engine: engine 0 hands its (m, l, O) to engine 1
+  // through LDS (the K/V buffers are free now) and engine 1 merges.
+  int qt_f = -1, qt_s = -2, kt_tmp;
+  item(half - 1, qt_f, kt_tmp);
+  if (half < total) item(half, qt_s, kt_tmp);
+  const bool shared = qt_f == qt_s;
+  if (!shared) {
+    if (qt_cur >= 0) finish(qt_cur, m, lsum, o);
+    return;
+  }
+  float *mrg = reinterpret_cast<float *>(smem) + (size_t)(w * 64 + lane) * C::kMergeLane;
+  if (eng == 0) {
 #pragma unroll
-    for (int db = 0; db < kNdb; ++db)
+    for (int db = 0; db < C::kNdb; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = f32_to_bf16_bits(o[db][4 * j] * inv) | ((uint32_t)f32_to_bf16_bits(o[db][4 * j + 1] * inv) << 16);
-        const uint32_t hi = f32_to_bf16_bits(o[db][4 * j + 2] * inv) | ((uint32_t)f32_to_bf16_bits(o[db][4 * j + 3] * inv) << 16);
-        *reinterpret_cast<uint2 *>(orow + db * 32 + j * 8 + g * 4) = make_uint2(lo, hi);
+      for (int i = 0; i < 16; i += 4)
+        *reinterpret_cast<f32x4 *>(mrg + 16 * db + i) = f32x4{o[db][i], o[db][i + 1], o[db][i + 2], o[db][i + 3]};
+    mrg[16 * C::kNdb] = m;
+    mrg[16 * C::kNdb + 1] = lsum;
+  }
+  __syncthreads();
+  if (eng == 1) {
+    const float m0 = mrg[16 * C::kNdb];
+    const float l0 = mrg[16 * C::kNdb + 1];
+    const float mm = fmaxf(m0, m);
+    const float f0 = m0 == -INFINITY ? 0.f : fast_exp2(m0 - mm);
+    const float f1 = m == -INFINITY ? 0.f : fast_exp2(m - mm);
+#pragma unroll
+    for (int db = 0; db < C::kNdb; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; i += 4) {
+        const f32x4 v0 = *reinterpret_cast<const f32x4 *>(mrg + 16 * db + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[db][i + e] = o[db][i + e] * f1 + v0[e] * f0;
       }
-    if (a.lse != nullptr && g == 0) a.lse[(size_t)(q0 + qrow) * a.num_q_heads + h] = (m + __log2f(ltot)) * kLn2;
+    finish(qt_cur, mm, lsum * f1 + l0 * f0, o);
   }
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
   if (a.batch == 0 || a.max_q_len == 0) return hipSuccess;
   if (a.c.dtype == 0) return launch_rowwise_f32(a, s);
-  dim3 grid(a.num_q_heads, (a.max_q_len + kPfRows - 1) / kPfRows, a.batch);
+  const int n_qt = (a.max_q_len + kPfRows - 1) / kPfRows;
+  dim3 grid((n_qt + 1) / 2, a.num_q_heads, a.batch);
   if (a.c.head_dim == 64)
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(2 * kPfEngineThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(2 * kPfEngineThreads), 0, s, a);
   return hipGetLastError();
 }
 
