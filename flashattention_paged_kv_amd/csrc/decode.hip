@@ -117,18 +117,6 @@ __device__ __forceinline__ int v_row(int k) {
   return I8 ? 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3) : k;
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor over [base, base + bytes) (gfx9 raw buffer, stride 0).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 // NB: tiles in flight per wave (register buffers); WPC: resident workgroups
 // per CU the register budget is sized for (the grid is WPC per CU).
 template <int D, bool I8, int NB, int WPC>

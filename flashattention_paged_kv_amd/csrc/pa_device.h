@@ -97,6 +97,19 @@ __device__ __forceinline__ float sum_xor32(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor over [base, base + bytes) (gfx9 raw buffer, stride 0):
+// loads through it are range-checked by the hardware (out of range -> 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Pack 8 signed int8 (in two dwords) into 8 exact bf16 values.
 __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   bf16x8 r;

@@ -15,14 +15,18 @@
 // list of 64-key tiles it can see.  One workgroup of 8 waves takes the pair
 // of query tiles (p, n-1-p) of one (sequence, query head): under a causal
 // mask their key-tile counts add up to the same total for every p, so all
-// workgroups carry equal work.  The workgroup is two engines of 4 waves.
-// The pair's work list (tile p's key tiles, then tile n-1-p's) is consumed
-// from both ends, engine 0 forward and engine 1 backward, so each engine
-// does half; the one query tile the engines meet in is merged in LDS at the
-// end with the same rescaling algebra as the online softmax.  Each engine
-// has its own double-buffered K/V tiles in LDS and prefetches the next key
-// tile into registers while it computes the current one: one barrier per
-// step for the whole workgroup (both engines run the same number of steps).
+// workgroups carry equal work.  The workgroup is two engines of 4 waves that
+// each take half of the pair's key tiles: engine 0 all of the earlier tile
+// and the top of the later one, engine 1 the bottom of the later one, both
+// ascending, so that the two engines read the same key tile at the same
+// step while both are in the shared prefix.  The query tile split between
+// them is merged in LDS at the end with the same rescaling algebra as the
+// online softmax.  Each engine has its own double-buffered K/V tiles in LDS
+// and prefetches the next key tile into registers while it computes the
+// current one: one barrier per step for the whole workgroup (both engines
+// run the same number of steps).  Workgroup ids are remapped so that the
+// pairs of one query head run on the same XCD (shared L2) and stream its
+// K/V tiles together.
 //
 // Per step a wave (32 query rows) computes S^T = K . Q^T with
 // v_mfma_f32_32x32x16_bf16 (keys on M, its rows on N, Q^T in registers),
@@ -64,7 +68,8 @@ struct PfCfg {
   static_assert(4 * 64 * kMergeLane * 4 <= kEngine, "merge area must fit one engine's buffers");
 };
 
-template <int D>
+// BIG_PAGE: page_size >= 64, so each 64-key tile lies in one page.
+template <int D, bool BIG_PAGE>
 __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a) {
   using C = PfCfg<D>;
   __shared__ __align__(16) unsigned char smem[2 * C::kEngine];
@@ -78,9 +83,18 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a) {
   const int gam = lane >> 4;
   const int tp = lane & 15;
 
-  const int pair = blockIdx.x;
-  const int h = blockIdx.y;
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+  // L2): consecutive ids are remapped so that the pairs of one query head run
+  // on one XCD and stream that head's K/V tiles together.
+  int pair = blockIdx.x;
+  int h = blockIdx.y;
   const int b = blockIdx.z;
+  if ((gridDim.y & 7) == 0) {
+    const int k = blockIdx.x + gridDim.x * blockIdx.y;  // id inside this sequence
+    const int k8 = k >> 3;
+    h = (k & 7) + 8 * (k8 / gridDim.x);
+    pair = k8 % gridDim.x;
+  }
   // Sequence geometry is the same for every lane: readfirstlane keeps it
   // (and every tile decision derived from it) in scalar registers.
   const int q0 = __builtin_amdgcn_readfirstlane(a.cu_q[b]);
@@ -103,25 +117,48 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a) {
     hi = (k_hi + kPfKeys - 1) / kPfKeys;
   };
   const int qa = pair;
-  const int qb = n_qt - 1 - pair;
+  const int qb = n_qt - 1 - pair;  // == qa for the middle tile of an odd count
   int lo_a, hi_a, lo_b = 0, hi_b = 0;
   tile_range(qa, lo_a, hi_a);
   if (qb != qa) tile_range(qb, lo_b, hi_b);
+  // Split of the pair's key tiles between the engines, half each.  With
+  // na <= nb (always under a causal mask, tile qa being the earlier one):
+  // engine 0 takes all of qa, then the top of qb's tiles; engine 1 takes the
+  // bottom of qb's tiles.  Both ascend, so under a causal mask (both ranges
+  // start at key 0) the engines read the same key tile at the same step.
+  // Otherwise (na > nb, or the middle tile of an odd count, nb = 0): engine 0
+  // takes the bottom of qa; engine 1 takes all of qb, then the top of qa.
+  // Either way the query tile split between the engines (if any) is the last
+  // one each engine works on.
   const int na = hi_a - lo_a;
-  const int total = na + (hi_b - lo_b);
+  const int nb = hi_b - lo_b;
+  const int total = na + nb;
   const int half = (total + 1) / 2;
-  const int n_mine = eng == 0 ? half : total - half;
-  // Work item i of the pair's list -> (query tile, key tile).
-  auto item = [&](int i, int &qt, int &kt) {
-    if (i < na) {
-      qt = qa;
-      kt = lo_a + i;
+  const int n1 = total - half;
+  const bool case_a = na <= nb;
+  const int n_mine = eng == 0 ? half : n1;
+  auto my_item = [&](int t, int &qt, int &kt) {
+    if (case_a) {
+      if (eng == 0 && t < na) {
+        qt = qa;
+        kt = lo_a + t;
+      } else {
+        qt = qb;
+        kt = lo_b + (eng == 0 ? n1 + (t - na) : t);
+      }
     } else {
-      qt = qb;
-      kt = lo_b + (i - na);
+      if (eng == 0) {
+        qt = qa;
+        kt = lo_a + t;
+      } else if (t < nb) {
+        qt = qb;
+        kt = lo_b + t;
+      } else {
+        qt = qa;
+        kt = lo_a + half + (t - nb);
+      }
     }
   };
-  auto my_item = [&](int t, int &qt, int &kt) { item(eng == 0 ? t : total - 1 - t, qt, kt); };
 
   unsigned char *ebase = smem + eng * C::kEngine;
   const int P = a.c.page_size;
@@ -131,34 +168,56 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a) {
   const char *vbase = (const char *)a.c.v + (size_t)hk * D * 2;
   const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
 
-  // Prefetch of one key tile: thread `tid` moves chunks tid + 256 i (row =
-  // chunk / kCpr).  Keys at or beyond ctx are not read (their slots may hold
-  // anything) and stage as zeros; they are masked.
+  // Prefetch of one key tile: thread `tid` moves chunks tid + 256 i, i.e.
+  // row tid / kCpr + i * kRowsPerPass, chunk tid % kCpr.  BIG_PAGE (P >= 64):
+  // the tile sits in one page, so one buffer descriptor (page base, uniform)
+  // with a per-lane offset and a scalar offset per i addresses every load.
+  // Otherwise each row looks its page up.  Keys at or beyond ctx are not
+  // read (their slots may hold anything) and stage as zeros; they are masked.
+  constexpr int kRowsPerPass = kPfEngineThreads / C::kCpr;
+  const int lrow = tid / C::kCpr;
+  const int lch = tid % C::kCpr;
+  const uint32_t lane_goff = (uint32_t)lrow * (uint32_t)row_bytes + lch * 16;
   uint4 pk[C::kLoads], pv[C::kLoads];
   auto load_tile = [&](int kt) {
+    const int key0 = kt * kPfKeys;
+    if constexpr (BIG_PAGE) {
+      const size_t tile_off = ((size_t)bt[key0 >> lp] * P + (key0 & (P - 1))) * row_bytes;  // uniform
+      const uint32_t span = (uint32_t)(kPfKeys * row_bytes);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + tile_off, span);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + tile_off, span);
 #pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int c = tid + kPfEngineThreads * i;
-      const int key = kt * kPfKeys + c / C::kCpr;
-      pk[i] = make_uint4(0, 0, 0, 0);
-      pv[i] = make_uint4(0, 0, 0, 0);
-      if (key < ctx) {
-        const size_t ro = ((size_t)bt[key >> lp] * P + (key & (P - 1))) * row_bytes + (c % C::kCpr) * 16;
-        pk[i] = *reinterpret_cast<const uint4 *>(kbase + ro);
-        pv[i] = *reinterpret_cast<const uint4 *>(vbase + ro);
+      for (int i = 0; i < C::kLoads; ++i) {
+        const int soff = i * kRowsPerPass * (int)row_bytes;
+        const bool in = key0 + lrow + i * kRowsPerPass < ctx;
+        const u32x4 kx = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)lane_goff, soff, 0);
+        const u32x4 vx = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)lane_goff, soff, 0);
+        pk[i] = in ? make_uint4(kx.x, kx.y, kx.z, kx.w) : make_uint4(0, 0, 0, 0);
+        pv[i] = in ? make_uint4(vx.x, vx.y, vx.z, vx.w) : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::kLoads; ++i) {
+        const int key = key0 + lrow + i * kRowsPerPass;
+        pk[i] = make_uint4(0, 0, 0, 0);
+        pv[i] = make_uint4(0, 0, 0, 0);
+        if (key < ctx) {
+          const size_t ro = ((size_t)bt[key >> lp] * P + (key & (P - 1))) * row_bytes + lch * 16;
+          pk[i] = *reinterpret_cast<const uint4 *>(kbase + ro);
+          pv[i] = *reinterpret_cast<const uint4 *>(vbase + ro);
+        }
       }
     }
   };
+  const uint32_t lane_koff = (uint32_t)lrow * C::kKRow + lch * 16;
+  const uint32_t lane_voff = (uint32_t)lrow * C::kVRow + lch * 16;
   auto store_tile = [&](int buf) {
     unsigned char *ks = ebase + buf * (C::kKBuf + C::kVBuf);
     unsigned char *vs = ks + C::kKBuf;
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
-      const int c = tid + kPfEngineThreads * i;
-      const int row = c / C::kCpr;
-      const int ch = c % C::kCpr;
-      *reinterpret_cast<uint4 *>(ks + row * C::kKRow + ch * 16) = pk[i];
-      *reinterpret_cast<uint4 *>(vs + row * C::kVRow + ch * 16) = pv[i];
+      *reinterpret_cast<uint4 *>(ks + lane_koff + i * kRowsPerPass * C::kKRow) = pk[i];
+      *reinterpret_cast<uint4 *>(vs + lane_voff + i * kRowsPerPass * C::kVRow) = pv[i];
     }
   };
 
@@ -168,6 +227,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a) {
   float m = -INFINITY;  // exponent reference of this lane's row (log2 units)
   float lsum = 0.f;     // this lane's half of the row sum
   f32x16 o[C::kNdb];
+  bf16x8 bp[4];         // P^T of the tile between its QK and PV phases
 
   auto start = [&](int qt) {
     const int qrow = qt * kPfRows + w * 32 + col;
@@ -202,15 +262,14 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a) {
     }
   };
 
-  auto compute = [&](int qt, int kt, int buf) {
+  // QK phase of a tile: S^T = K . Q^T, mask, online softmax, P^T -> bp.
+  auto qk_phase = [&](int qt, int kt, int buf) {
     const unsigned char *ks = ebase + buf * (C::kKBuf + C::kVBuf);
-    const unsigned char *vs = ks + C::kKBuf;
     const int key0 = kt * kPfKeys;
     const int pos = off + qt * kPfRows + w * 32 + col;
     const int p_first = off + qt * kPfRows;
     const int p_last = off + min(qt * kPfRows + kPfRows - 1, q_len - 1);
 
-    // S^T = K . Q^T: two 32-key blocks.
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -221,28 +280,32 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(ks + (kb * 32 + col) * C::kKRow + (16 * s + 8 * g) * 2);
         sacc[kb] = mfma32(ka, bq[s], sacc[kb]);
       }
+      __builtin_amdgcn_sched_barrier(0);  // bound the K fragments held in registers
     }
 
-    // Mask (only tiles that cross a boundary) and online softmax.  This
-    // lane's row sees keys [klo, khi].
+    // Mask (only tiles that cross a boundary; this lane's row sees keys
+    // [klo, khi]) on the raw scores; the scale (> 0) is applied inside the
+    // exponent, after the max.
     const bool edge = (causal && key0 + kPfKeys - 1 > p_first) || (W >= 0 && key0 < p_last - W) ||
                       (key0 + kPfKeys > ctx);
-    const int khi = causal ? min(pos, ctx - 1) : ctx - 1;
-    const int klo = W >= 0 ? pos - W : 0;
-    float mx = -INFINITY;
+    if (edge) {
+      const int khi = causal ? min(pos, ctx - 1) : ctx - 1;
+      const int klo = W >= 0 ? pos - W : 0;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v = sacc[kb][i] * a.scale_log2;
-        if (edge) {
+        for (int i = 0; i < 16; ++i) {
           const int key = key0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-          v = (key >= klo) & (key <= khi) ? v : -INFINITY;
+          sacc[kb][i] = ((key >= klo) & (key <= khi)) ? sacc[kb][i] : -INFINITY;
         }
-        sacc[kb][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = max_xor32(mx);
+    }
+    float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      mx0 = fmaxf(mx0, sacc[0][i]);
+      mx1 = fmaxf(mx1, sacc[1][i]);
+    }
+    const float mx = max_xor32(fmaxf(mx0, mx1)) * a.scale_log2;
     if (__any(mx > m + kPfSlack)) {
       // New reference for every lane of the wave (a lane whose max did not
       // grow keeps a factor of 1).  A row without a visible key yet keeps
@@ -254,73 +317,89 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a) {
       for (int db = 0; db < C::kNdb; ++db) o[db] *= corr;
       m = m_new;
     }
-    const float m_use = m == -INFINITY ? 0.f : m;
-    float ps = 0.f;
+    const float neg_m = m == -INFINITY ? 0.f : -m;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        sacc[kb][i] = fast_exp2(sacc[kb][i] - m_use);
-        ps += sacc[kb][i];
+        const float p = fast_exp2(fmaf(sacc[kb][i], a.scale_log2, neg_m));
+        ps[i & 3] += p;
+        sacc[kb][i] = p;
       }
-    lsum += ps;
+    lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bp[t][e] = (__bf16)sacc[t >> 1][8 * (t & 1) + e];
+  };
 
-    // O^T += V^T . P^T over four 16-key steps.
+  // PV phase of a tile: O^T += V^T . P^T over four 16-key steps.
+  auto pv_phase = [&](int buf) {
+    const unsigned char *vs = ebase + buf * (C::kKBuf + C::kVBuf) + C::kKBuf;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int kb = t >> 1;
-      const int hf = t & 1;
-      bf16x8 bp;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bp[e] = (__bf16)sacc[kb][8 * hf + e];
-      const int r0 = kb * 32 + hf * 16 + g * 4;
+      const int r0 = (t >> 1) * 32 + (t & 1) * 16 + g * 4;
 #pragma unroll
       for (int db = 0; db < C::kNdb; ++db) {
         const unsigned char *p1 = vs + (r0 + (tp >> 2)) * C::kVRow + (db * 32 + 16 * (gam & 1) + 4 * (tp & 3)) * 2;
         const bf16x8 va = cat(lds_read_tr16(p1), lds_read_tr16(p1 + 8 * C::kVRow));
-        o[db] = mfma32(va, bp, o[db]);
+        o[db] = mfma32(va, bp[t], o[db]);
       }
+      __builtin_amdgcn_sched_barrier(0);  // bound the V fragments held in registers
     }
   };
 
-  // Both engines run `half` steps so that they meet every barrier; an engine
-  // with fewer items idles in its last step.
+  // Ping-pong schedule in half-steps h.  Engine e runs the QK phase of its
+  // tile t at h = 2t + e and the PV phase at h = 2t + 1 + e, so at every
+  // half-step one engine is in its softmax (VALU) while the other multiplies
+  // (MFMA) on the same SIMDs; one barrier per half-step.  Tile t lives in
+  // LDS buffer t % 2.  Tile t+1 is stored to LDS at the end of QK(t) (its
+  // buffer was last read by PV(t-1)); tile t+2's loads are issued at the
+  // start of PV(t), two half-steps before they are needed.
   if (n_mine > 0) {
     int qt, kt;
     my_item(0, qt, kt);
     load_tile(kt);
     store_tile(0);
+    if (n_mine > 1) {
+      my_item(1, qt, kt);
+      load_tile(kt);
+    }
   }
   __syncthreads();
-  for (int t = 0; t < half; ++t) {
-    const bool active = t < n_mine;
-    const bool has_next = t + 1 < n_mine;
-    if (has_next) {
-      int qt_n, kt_n;
-      my_item(t + 1, qt_n, kt_n);
-      load_tile(kt_n);
-    }
-    if (active) {
-      int qt, kt;
-      my_item(t, qt, kt);
-      if (qt != qt_cur) {
-        if (qt_cur >= 0) finish(qt_cur, m, lsum, o);
-        start(qt);
-        qt_cur = qt;
+  const int n_half = 2 * half + 1;
+  for (int hs = 0; hs < n_half; ++hs) {
+    const int ph = hs - eng;
+    const int t = ph >> 1;
+    if (ph >= 0 && t < n_mine) {
+      if ((ph & 1) == 0) {
+        int qt, kt;
+        my_item(t, qt, kt);
+        if (qt != qt_cur) {
+          if (qt_cur >= 0) finish(qt_cur, m, lsum, o);
+          start(qt);
+          qt_cur = qt;
+        }
+        qk_phase(qt, kt, t & 1);
+        if (t + 1 < n_mine) store_tile((t + 1) & 1);
+      } else {
+        if (t + 2 < n_mine) {
+          int qt_n, kt_n;
+          my_item(t + 2, qt_n, kt_n);
+          load_tile(kt_n);
+        }
+        pv_phase(t & 1);
       }
-      compute(qt, kt, t & 1);
     }
-    if (has_next) store_tile((t + 1) & 1);
     __syncthreads();
   }
 
-  // The query tile of items half-1 and half, if they are the same, has a
+  // The query tile split between the engines (qb in the first case, qa in
+  // the second; none if the split falls on the boundary, half == na) has a
   // partial result in each engine: engine 0 hands its (m, l, O) to engine 1
   // through LDS (the K/V buffers are free now) and engine 1 merges.
-  int qt_f = -1, qt_s = -2, kt_tmp;
-  item(half - 1, qt_f, kt_tmp);
-  if (half < total) item(half, qt_s, kt_tmp);
-  const bool shared = qt_f == qt_s;
+  const bool shared = half != na;
   if (!shared) {
     if (qt_cur >= 0) finish(qt_cur, m, lsum, o);
     return;
@@ -359,10 +438,15 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
   if (a.c.dtype == 0) return launch_rowwise_f32(a, s);
   const int n_qt = (a.max_q_len + kPfRows - 1) / kPfRows;
   dim3 grid((n_qt + 1) / 2, a.num_q_heads, a.batch);
-  if (a.c.head_dim == 64)
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(2 * kPfEngineThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(2 * kPfEngineThreads), 0, s, a);
+  const dim3 block(2 * kPfEngineThreads);
+  const bool big = a.c.page_size >= kPfKeys;
+  if (a.c.head_dim == 64) {
+    if (big) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, s, a);
+  } else {
+    if (big) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
