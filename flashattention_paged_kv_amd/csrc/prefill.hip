@@ -69,8 +69,10 @@ struct PfCfg {
 };
 
 // BIG_PAGE: page_size >= 64, so each 64-key tile lies in one page.
+// block_table is a.block_table, passed again as a restrict pointer so that
+// uniform page-id reads are scalar loads.
 template <int D, bool BIG_PAGE>
-__global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, const int32_t *__restrict__ block_table) {
   using C = PfCfg<D>;
   __shared__ __align__(16) unsigned char smem[2 * C::kEngine];
 
@@ -168,58 +170,53 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a) {
   const char *vbase = (const char *)a.c.v + (size_t)hk * D * 2;
   const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
 
-  // Prefetch of one key tile: thread `tid` moves chunks tid + 256 i, i.e.
-  // row tid / kCpr + i * kRowsPerPass, chunk tid % kCpr.  BIG_PAGE (P >= 64):
-  // the tile sits in one page, so one buffer descriptor (page base, uniform)
-  // with a per-lane offset and a scalar offset per i addresses every load.
-  // Otherwise each row looks its page up.  Keys at or beyond ctx are not
-  // read (their slots may hold anything) and stage as zeros; they are masked.
+  // Prefetch of one key tile, K and V separately: thread `tid` moves chunks
+  // tid + 256 i, i.e. row tid / kCpr + i * kRowsPerPass, chunk tid % kCpr.
+  // BIG_PAGE (P >= 64): the tile sits in one page (one scalar page-id load)
+  // and is read through a buffer descriptor whose range ends at the last key
+  // of the context, so rows at or beyond ctx read as zeros (their slots may
+  // hold anything; they are masked).  Otherwise each row looks its page up.
   constexpr int kRowsPerPass = kPfEngineThreads / C::kCpr;
   const int lrow = tid / C::kCpr;
   const int lch = tid % C::kCpr;
   const uint32_t lane_goff = (uint32_t)lrow * (uint32_t)row_bytes + lch * 16;
-  uint4 pk[C::kLoads], pv[C::kLoads];
-  auto load_tile = [&](int kt) {
+  auto load_half = [&](int kt, const char *base, uint4 *dst) {
     const int key0 = kt * kPfKeys;
     if constexpr (BIG_PAGE) {
-      const size_t tile_off = ((size_t)bt[key0 >> lp] * P + (key0 & (P - 1))) * row_bytes;  // uniform
-      const uint32_t span = (uint32_t)(kPfKeys * row_bytes);
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + tile_off, span);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + tile_off, span);
+      const size_t tile_off = ((size_t)block_table[(size_t)b * a.max_pages + (key0 >> lp)] * P + (key0 & (P - 1))) *
+                              row_bytes;  // uniform
+      const uint32_t span = (uint32_t)(min(kPfKeys, ctx - key0) * row_bytes);
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(base + tile_off, span);
 #pragma unroll
-      for (int i = 0; i < C::kLoads; ++i) {
-        const int soff = i * kRowsPerPass * (int)row_bytes;
-        const bool in = key0 + lrow + i * kRowsPerPass < ctx;
-        const u32x4 kx = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)lane_goff, soff, 0);
-        const u32x4 vx = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)lane_goff, soff, 0);
-        pk[i] = in ? make_uint4(kx.x, kx.y, kx.z, kx.w) : make_uint4(0, 0, 0, 0);
-        pv[i] = in ? make_uint4(vx.x, vx.y, vx.z, vx.w) : make_uint4(0, 0, 0, 0);
-      }
+      for (int i = 0; i < C::kLoads; ++i)
+        dst[i] = buf_load16(r, lane_goff + (uint32_t)(i * kRowsPerPass) * (uint32_t)row_bytes);
     } else {
 #pragma unroll
       for (int i = 0; i < C::kLoads; ++i) {
         const int key = key0 + lrow + i * kRowsPerPass;
-        pk[i] = make_uint4(0, 0, 0, 0);
-        pv[i] = make_uint4(0, 0, 0, 0);
+        dst[i] = make_uint4(0, 0, 0, 0);
         if (key < ctx) {
           const size_t ro = ((size_t)bt[key >> lp] * P + (key & (P - 1))) * row_bytes + lch * 16;
-          pk[i] = *reinterpret_cast<const uint4 *>(kbase + ro);
-          pv[i] = *reinterpret_cast<const uint4 *>(vbase + ro);
+          dst[i] = *reinterpret_cast<const uint4 *>(base + ro);
         }
       }
     }
   };
   const uint32_t lane_koff = (uint32_t)lrow * C::kKRow + lch * 16;
   const uint32_t lane_voff = (uint32_t)lrow * C::kVRow + lch * 16;
-  auto store_tile = [&](int buf) {
-    unsigned char *ks = ebase + buf * (C::kKBuf + C::kVBuf);
-    unsigned char *vs = ks + C::kKBuf;
+  auto kbuf = [&](int buf) { return ebase + buf * (C::kKBuf + C::kVBuf); };
+  auto vbuf = [&](int buf) { return ebase + buf * (C::kKBuf + C::kVBuf) + C::kKBuf; };
+  auto store_k = [&](int buf, const uint4 *src) {
 #pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      *reinterpret_cast<uint4 *>(ks + lane_koff + i * kRowsPerPass * C::kKRow) = pk[i];
-      *reinterpret_cast<uint4 *>(vs + lane_voff + i * kRowsPerPass * C::kVRow) = pv[i];
-    }
+    for (int i = 0; i < C::kLoads; ++i)
+      *reinterpret_cast<uint4 *>(kbuf(buf) + lane_koff + i * kRowsPerPass * C::kKRow) = src[i];
   };
+  auto store_v = [&](int buf, const uint4 *src) {
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i)
+      *reinterpret_cast<uint4 *>(vbuf(buf) + lane_voff + i * kRowsPerPass * C::kVRow) = src[i];
+  };
+  uint4 pk[C::kLoads], pv[C::kLoads];  // K / V of a tile in flight
 
   // Per-wave state of the query tile being worked on.
   int qt_cur = -1;
@@ -264,7 +261,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a) {
 
   // QK phase of a tile: S^T = K . Q^T, mask, online softmax, P^T -> bp.
   auto qk_phase = [&](int qt, int kt, int buf) {
-    const unsigned char *ks = ebase + buf * (C::kKBuf + C::kVBuf);
+    const unsigned char *ks = kbuf(buf);
     const int key0 = kt * kPfKeys;
     const int pos = off + qt * kPfRows + w * 32 + col;
     const int p_first = off + qt * kPfRows;
@@ -329,14 +326,19 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a) {
       }
     lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) bp[t][e] = (__bf16)sacc[t >> 1][8 * (t & 1) + e];
+      // Materialise P here, in the QK half-step: left alone, the compiler
+      // sinks the exponentials to their use after the barrier, which would
+      // put the softmax on the same half-step as this engine's PV MFMAs.
+      __asm__ volatile("" : "+v"(bp[t]));
+    }
   };
 
   // PV phase of a tile: O^T += V^T . P^T over four 16-key steps.
   auto pv_phase = [&](int buf) {
-    const unsigned char *vs = ebase + buf * (C::kKBuf + C::kVBuf) + C::kKBuf;
+    const unsigned char *vs = vbuf(buf);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int r0 = (t >> 1) * 32 + (t & 1) * 16 + g * 4;
@@ -350,49 +352,67 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a) {
     }
   };
 
-  // Ping-pong schedule in half-steps h.  Engine e runs the QK phase of its
-  // tile t at h = 2t + e and the PV phase at h = 2t + 1 + e, so at every
-  // half-step one engine is in its softmax (VALU) while the other multiplies
-  // (MFMA) on the same SIMDs; one barrier per half-step.  Tile t lives in
-  // LDS buffer t % 2.  Tile t+1 is stored to LDS at the end of QK(t) (its
-  // buffer was last read by PV(t-1)); tile t+2's loads are issued at the
-  // start of PV(t), two half-steps before they are needed.
+  // Ping-pong schedule in half-steps h (one barrier each).  Engine e runs
+  // the QK phase of its tile t at h = 2t + e and the PV phase at
+  // h = 2t + 1 + e, so at every half-step one engine is in its softmax
+  // (VALU) while the other multiplies (MFMA) on the same SIMDs.  Tile t lives in
+  // LDS buffer t % 2.  K(t+1) is loaded during PV(t-1) and stored at the
+  // start of QK(t) (its buffer was last read by QK(t-1)); V(t+1) is loaded
+  // during QK(t) and stored at the start of PV(t) (last read by PV(t-1)).
+  // So only one half of a tile is in registers at any time.
   if (n_mine > 0) {
     int qt, kt;
     my_item(0, qt, kt);
-    load_tile(kt);
-    store_tile(0);
+    load_half(kt, kbase, pk);
+    load_half(kt, vbase, pv);
+    store_k(0, pk);
+    store_v(0, pv);
     if (n_mine > 1) {
       my_item(1, qt, kt);
-      load_tile(kt);
+      load_half(kt, kbase, pk);
     }
   }
   __syncthreads();
-  const int n_half = 2 * half + 1;
-  for (int hs = 0; hs < n_half; ++hs) {
-    const int ph = hs - eng;
-    const int t = ph >> 1;
-    if (ph >= 0 && t < n_mine) {
-      if ((ph & 1) == 0) {
-        int qt, kt;
-        my_item(t, qt, kt);
-        if (qt != qt_cur) {
-          if (qt_cur >= 0) finish(qt_cur, m, lsum, o);
-          start(qt);
-          qt_cur = qt;
-        }
-        qk_phase(qt, kt, t & 1);
-        if (t + 1 < n_mine) store_tile((t + 1) & 1);
-      } else {
-        if (t + 2 < n_mine) {
-          int qt_n, kt_n;
-          my_item(t + 2, qt_n, kt_n);
-          load_tile(kt_n);
-        }
-        pv_phase(t & 1);
-      }
+  // One step of tile t: QK phase, barrier, PV phase, barrier.  Engine 0
+  // starts at half-step 0, engine 1 one barrier later; each engine's loop is
+  // straight-line so that its registers keep one assignment.  Both engines
+  // pass 2 * half + 1 barriers in total.
+  auto step = [&](int t) {
+    int qt, kt;
+    my_item(t, qt, kt);
+    if (qt != qt_cur) {
+      if (qt_cur >= 0) finish(qt_cur, m, lsum, o);
+      start(qt);
+      qt_cur = qt;
     }
+    const bool more = t + 1 < n_mine;
+    if (more) {
+      int qt_n, kt_n;
+      my_item(t + 1, qt_n, kt_n);
+      store_k((t + 1) & 1, pk);
+      load_half(kt_n, vbase, pv);
+    }
+    qk_phase(qt, kt, t & 1);
     __syncthreads();
+    if (more) store_v((t + 1) & 1, pv);
+    if (t + 2 < n_mine) {
+      int qt_n, kt_n;
+      my_item(t + 2, qt_n, kt_n);
+      load_half(kt_n, kbase, pk);
+    }
+    pv_phase(t & 1);
+    __syncthreads();
+  };
+  if (eng == 0) {
+    for (int t = 0; t < half; ++t) step(t);
+    __syncthreads();
+  } else {
+    __syncthreads();
+    for (int t = 0; t < n_mine; ++t) step(t);
+    for (int t = n_mine; t < half; ++t) {
+      __syncthreads();
+      __syncthreads();
+    }
   }
 
   // The query tile split between the engines (qb in the first case, qa in
@@ -441,11 +461,11 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
   const dim3 block(2 * kPfEngineThreads);
   const bool big = a.c.page_size >= kPfKeys;
   if (a.c.head_dim == 64) {
-    if (big) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, s, a);
+    if (big) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, s, a, a.block_table);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, s, a, a.block_table);
   } else {
-    if (big) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, s, a);
+    if (big) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, s, a, a.block_table);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, s, a, a.block_table);
   }
   return hipGetLastError();
 }
