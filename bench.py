@@ -20,7 +20,6 @@ events around back-to-back launches on the stream the library launches on
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -49,21 +48,18 @@ def causal_pairs(n: int, window_left: int = -1) -> int:
     return full * (full + 1) // 2 + (n - full) * w1
 
 
-def _kernel_source_sha(name: str) -> str:
-    p = os.path.join(ROOT, "flashattention_paged_kv_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
-
-
-def _traffic(kernel: str, source: str, per_launch_units: float):
-    """HBM bytes per launch from committed rocprofv3 counter runs, only if the
-    kernel source is unchanged since they were taken."""
+def _traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs (scaled by
+    the copy calibration), only while the kernel's sources are unchanged
+    since they were taken; else None."""
+    from flashattention_paged_kv_amd.profiling import source_hash
     try:
-        t = json.load(open(TRAFFIC_FILE))[kernel]
+        t = json.load(open(TRAFFIC_FILE))[f"{kernel}:{workload}"]
     except (OSError, KeyError, ValueError):
         return None
-    if t.get("source_sha") != _kernel_source_sha(source):
+    if t.get("source_hash") != source_hash(kernel):
         return None
-    return t["hbm_bytes_per_launch"]
+    return round(t["hbm_bytes_per_launch"])
 
 
 def _time_loop(fn, steps: int, warmup: int) -> float:
@@ -112,7 +108,7 @@ def bench_prefill(w: wl.PrefillWorkload, steps: int, warmup: int) -> dict:
                 tflops_step=flops / (ms_step * 1e-3) / 1e12, tflops_kernel=achieved, kv_bytes=kv_bytes,
                 roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                               frac=round(achieved / PEAK_BF16_TFLOPS, 4),
-                              traffic=_traffic("prefill_bf16_kernel", "prefill.hip", 1)))
+                              traffic=_traffic("prefill_bf16_kernel", w.name)))
 
 
 def bench_decode(w: wl.DecodeWorkload, steps: int, warmup: int) -> dict:
@@ -159,7 +155,7 @@ def bench_decode(w: wl.DecodeWorkload, steps: int, warmup: int) -> dict:
                 gbs_step=kv_bytes / (ms_step * 1e-3) / 1e9, gbs_kernel=gbs, sum_ctx=int(ctx_np.sum()),
                 roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                               frac=round(gbs / PEAK_HBM_GBS, 4),
-                              traffic=_traffic("decode_split_kernel", "decode.hip", 1)))
+                              traffic=_traffic("decode_split_kernel", w.name)))
 
 
 def cpu_baseline(w: wl.PrefillWorkload, budget_s: float = 15.0) -> dict:
@@ -202,6 +198,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=None, help="bench a single named workload instead")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run device copies of BYTES bytes (the known-size kernel that scales "
+                         "the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library runs on a single device (no collectives); "
@@ -211,6 +210,15 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "copies": max(1, args.steps)}), flush=True)
+        return 0
     ops.load_library()
 
     if args.workload:

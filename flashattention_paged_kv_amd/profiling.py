@@ -1,0 +1,133 @@
+"""Summaries of rocprofv3 output for the benchmark's kernels (host tool; it
+never touches the GPU).
+
+    # kernel durations (from `rocprofv3 --kernel-trace --stats -f csv`)
+    python -m flashattention_paged_kv_amd.profiling stats KT_kernel_stats.csv \\
+        --cmd "<the rocprofv3 command>" --title "..." --out profiles/<name>.md
+
+    # HBM traffic per launch (from `rocprofv3 --pmc FETCH_SIZE` and
+    # `--pmc WRITE_SIZE` runs of the benchmark and of its copy calibration)
+    python -m flashattention_paged_kv_amd.profiling traffic \\
+        --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv \\
+        --copy-bytes N --kernel decode_split_kernel --out profiles/traffic.json
+
+FETCH_SIZE / WRITE_SIZE are read in KiB per dispatch.  On a partitioned
+device they need not see every memory channel, so each is scaled by the
+ratio known-bytes / counter for a plain device copy of N bytes (the
+`__amd_rocclr_copyBuffer` dispatches of `bench.py --copy-calibration N`).
+The traffic file records a hash of the kernel's sources; `bench.py` only
+reports traffic while the sources are unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+from collections import defaultdict
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(_HERE, "csrc")
+
+# Kernel name fragment -> source files whose text defines it.
+KERNEL_SOURCES = {
+    "prefill_bf16_kernel": ("prefill.hip", "pa_device.h", "pa_internal.h"),
+    "decode_split_kernel": ("decode.hip", "pa_device.h", "pa_internal.h"),
+    "decode_reduce_kernel": ("decode.hip", "pa_device.h", "pa_internal.h"),
+    "append_kernel": ("append.hip", "pa_device.h", "pa_internal.h"),
+}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _short(name: str) -> str:
+    for k in KERNEL_SOURCES:
+        if k in name:
+            return name.split("(")[0].replace("void ", "")
+    return name if len(name) <= 60 else name[:57] + "..."
+
+
+def stats_markdown(stats_csv: str, cmd: str, title: str) -> str:
+    rows = list(csv.DictReader(open(stats_csv)))
+    out = [f"# {title}", "", "Command (from the repository root, on one MI355X):", "", "```", cmd, "```", "",
+           "| kernel | calls | avg µs | min µs | max µs |", "|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    return "\n".join(out) + "\n"
+
+
+def counter_per_dispatch(path: str, counter: str) -> dict:
+    """Mean value of `counter` per dispatch, by kernel name."""
+    vals = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: statistics.fmean(v) for k, v in vals.items()}
+
+
+def _pick(d: dict, fragment: str) -> float:
+    hits = [v for k, v in d.items() if fragment in k]
+    if not hits:
+        raise SystemExit(f"no dispatch of a kernel named like {fragment!r}")
+    return statistics.fmean(hits)
+
+
+def traffic(args) -> dict:
+    fetch = counter_per_dispatch(args.fetch, "FETCH_SIZE")
+    write = counter_per_dispatch(args.write, "WRITE_SIZE")
+    cfetch = _pick(counter_per_dispatch(args.copy_fetch, "FETCH_SIZE"), "copyBuffer")
+    cwrite = _pick(counter_per_dispatch(args.copy_write, "WRITE_SIZE"), "copyBuffer")
+    f_scale = args.copy_bytes / (cfetch * 1024.0)
+    w_scale = args.copy_bytes / (cwrite * 1024.0)
+    rd = _pick(fetch, args.kernel) * 1024.0 * f_scale
+    wr = _pick(write, args.kernel) * 1024.0 * w_scale
+    return dict(kernel=args.kernel, source_hash=source_hash(args.kernel), workload=args.workload,
+                read_bytes_per_launch=rd, write_bytes_per_launch=wr, hbm_bytes_per_launch=rd + wr,
+                fetch_scale=f_scale, write_scale=w_scale, copy_bytes=args.copy_bytes)
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(prog="python -m flashattention_paged_kv_amd.profiling")
+    sub = ap.add_subparsers(dest="action", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("stats_csv")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--title", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    for n in ("fetch", "write", "copy-fetch", "copy-write"):
+        t.add_argument("--" + n, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--kernel", required=True, choices=sorted(KERNEL_SOURCES))
+    t.add_argument("--workload", required=True)
+    t.add_argument("--out", required=True)
+    args = ap.parse_args(argv)
+    if args.action == "stats":
+        with open(args.out, "w") as f:
+            f.write(stats_markdown(args.stats_csv, args.cmd, args.title))
+        return 0
+    rec = traffic(args)
+    data = {}
+    if os.path.exists(args.out):
+        with open(args.out) as f:
+            data = json.load(f)
+    data[f"{args.kernel}:{args.workload}"] = rec
+    with open(args.out, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
