@@ -110,7 +110,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   const int causal = a.causal;
 
   // Visible key tiles [lo, hi) of query tile qt.
-  auto tile_range = [&](int qt, int &lo, int &hi) {
+  auto tile_range = [=](int qt, int &lo, int &hi) __attribute__((always_inline)) {
     const int p_first = off + qt * kPfRows;
     const int p_last = off + min(qt * kPfRows + kPfRows - 1, q_len - 1);
     const int k_lo = W >= 0 ? max(0, p_first - W) : 0;
@@ -137,29 +137,34 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   const int total = na + nb;
   const int half = (total + 1) / 2;
   const int n1 = total - half;
-  const bool case_a = na <= nb;
   const int n_mine = eng == 0 ? half : n1;
-  auto my_item = [&](int t, int &qt, int &kt) {
-    if (case_a) {
-      if (eng == 0 && t < na) {
-        qt = qa;
-        kt = lo_a + t;
-      } else {
-        qt = qb;
-        kt = lo_b + (eng == 0 ? n1 + (t - na) : t);
-      }
+  // This engine's items as two runs of consecutive key tiles: item t < s1
+  // is (q1, k1 + t), item t >= s1 is (q2, k2 + t - s1).
+  int s1, q1, k1, q2, k2;
+  if (na <= nb) {
+    if (eng == 0) {
+      s1 = na, q1 = qa, k1 = lo_a, q2 = qb, k2 = lo_b + n1;
     } else {
-      if (eng == 0) {
-        qt = qa;
-        kt = lo_a + t;
-      } else if (t < nb) {
-        qt = qb;
-        kt = lo_b + t;
-      } else {
-        qt = qa;
-        kt = lo_a + half + (t - nb);
-      }
+      s1 = 0, q1 = qb, k1 = lo_b, q2 = qb, k2 = lo_b;
     }
+  } else {
+    if (eng == 0) {
+      s1 = 0, q1 = qa, k1 = lo_a, q2 = qa, k2 = lo_a;
+    } else {
+      s1 = nb, q1 = qb, k1 = lo_b, q2 = qa, k2 = lo_a + half;
+    }
+  }
+  // Written as offsets from the second run so that the choice between runs
+  // is a choice between a value and zero (kept in scalar registers).
+  const int run1 = __builtin_amdgcn_readfirstlane(s1);
+  const int qt2 = __builtin_amdgcn_readfirstlane(q2);
+  const int dq = __builtin_amdgcn_readfirstlane(q1 - q2);
+  const int kt2 = __builtin_amdgcn_readfirstlane(k2 - s1);
+  const int dk = __builtin_amdgcn_readfirstlane(k1 - (k2 - s1));
+  auto my_item = [=](int t, int &qt, int &kt) __attribute__((always_inline)) {
+    const bool first = t < run1;
+    qt = qt2 + (first ? dq : 0);
+    kt = t + kt2 + (first ? dk : 0);
   };
 
   unsigned char *ebase = smem + eng * C::kEngine;
@@ -180,7 +185,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   const int lrow = tid / C::kCpr;
   const int lch = tid % C::kCpr;
   const uint32_t lane_goff = (uint32_t)lrow * (uint32_t)row_bytes + lch * 16;
-  auto load_half = [&](int kt, const char *base, uint4 *dst) {
+  auto load_half = [&](int kt, const char *base, uint4 *dst) __attribute__((always_inline)) {
     const int key0 = kt * kPfKeys;
     if constexpr (BIG_PAGE) {
       const size_t tile_off = ((size_t)block_table[(size_t)b * a.max_pages + (key0 >> lp)] * P + (key0 & (P - 1))) *
@@ -204,34 +209,44 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   };
   const uint32_t lane_koff = (uint32_t)lrow * C::kKRow + lch * 16;
   const uint32_t lane_voff = (uint32_t)lrow * C::kVRow + lch * 16;
-  auto kbuf = [&](int buf) { return ebase + buf * (C::kKBuf + C::kVBuf); };
-  auto vbuf = [&](int buf) { return ebase + buf * (C::kKBuf + C::kVBuf) + C::kKBuf; };
-  auto store_k = [&](int buf, const uint4 *src) {
+  auto kbuf = [&](int buf) __attribute__((always_inline)) { return ebase + buf * (C::kKBuf + C::kVBuf); };
+  auto vbuf = [&](int buf) __attribute__((always_inline)) { return ebase + buf * (C::kKBuf + C::kVBuf) + C::kKBuf; };
+  auto store_k = [&](int buf, const uint4 *src) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i)
       *reinterpret_cast<uint4 *>(kbuf(buf) + lane_koff + i * kRowsPerPass * C::kKRow) = src[i];
   };
-  auto store_v = [&](int buf, const uint4 *src) {
+  auto store_v = [&](int buf, const uint4 *src) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i)
       *reinterpret_cast<uint4 *>(vbuf(buf) + lane_voff + i * kRowsPerPass * C::kVRow) = src[i];
   };
   uint4 pk[C::kLoads], pv[C::kLoads];  // K / V of a tile in flight
 
-  // Per-wave state of the query tile being worked on.
-  int qt_cur = -1;
+  // Per-wave state.  qt_q: the query tile whose Q^T is in bq; qt_o: the
+  // query tile that (m, lsum, o) belong to.
+  int qt_q = -1, qt_o = -1;
   bf16x8 bq[C::kNs];
   float m = -INFINITY;  // exponent reference of this lane's row (log2 units)
   float lsum = 0.f;     // this lane's half of the row sum
   f32x16 o[C::kNdb];
-  bf16x8 bp[4];         // P^T of the tile between its QK and PV phases
+  f32x16 sacc[2];       // S^T of a tile between its GEMM and softmax phases
+  bf16x8 bp[4];         // P^T of a tile between its softmax phase and the next GEMM phase
 
-  auto start = [&](int qt) {
+  auto load_q = [&](int qt) __attribute__((always_inline)) {
     const int qrow = qt * kPfRows + w * 32 + col;
     const __bf16 *qp = (const __bf16 *)a.q + ((size_t)(q0 + min(qrow, q_len - 1)) * a.num_q_heads + h) * D;
 #pragma unroll
     for (int s = 0; s < C::kNs; ++s)
       bq[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp + 16 * s + 8 * g));
+    // Complete the Q loads on this (rare) path: otherwise the wait counters
+    // merged where the paths join treat Q as possibly in flight, and the QK
+    // MFMAs of every tile wait for all loads issued before them, including
+    // the prefetch of the next K/V tile.
+#pragma unroll
+    for (int s = 0; s < C::kNs; ++s) __asm__ volatile("" : "+v"(bq[s]));
+  };
+  auto reset_o = [&]() __attribute__((always_inline)) {
     m = -INFINITY;
     lsum = 0.f;
 #pragma unroll
@@ -240,7 +255,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
   };
   // Normalise and store this wave's rows of query tile qt.
-  auto finish = [&](int qt, float m_row, float l_half, const f32x16 *acc) {
+  auto finish = [&](int qt, float m_row, float l_half, const f32x16 *acc) __attribute__((always_inline)) {
     const int qrow = qt * kPfRows + w * 32 + col;
     const float ltot = l_half + __shfl_xor(l_half, 32, 64);
     if (qrow < q_len) {
@@ -259,15 +274,9 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     }
   };
 
-  // QK phase of a tile: S^T = K . Q^T, mask, online softmax, P^T -> bp.
-  auto qk_phase = [&](int qt, int kt, int buf) {
+  // S^T = K . Q^T for the two 32-key blocks of the tile in LDS buffer `buf`.
+  auto qk_mfma = [&](int buf) __attribute__((always_inline)) {
     const unsigned char *ks = kbuf(buf);
-    const int key0 = kt * kPfKeys;
-    const int pos = off + qt * kPfRows + w * 32 + col;
-    const int p_first = off + qt * kPfRows;
-    const int p_last = off + min(qt * kPfRows + kPfRows - 1, q_len - 1);
-
-    f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -277,9 +286,33 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
         const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(ks + (kb * 32 + col) * C::kKRow + (16 * s + 8 * g) * 2);
         sacc[kb] = mfma32(ka, bq[s], sacc[kb]);
       }
+      // Keep the product in this (GEMM) half-step: left alone, the compiler
+      // sinks it to its first use after the barrier.
+      __asm__ volatile("" : "+v"(sacc[kb]));
       __builtin_amdgcn_sched_barrier(0);  // bound the K fragments held in registers
     }
-
+  };
+  // O^T += V^T . P^T over four 16-key steps, V from LDS buffer `buf`.
+  auto pv_mfma = [&](int buf) __attribute__((always_inline)) {
+    const unsigned char *vs = vbuf(buf);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r0 = (t >> 1) * 32 + (t & 1) * 16 + g * 4;
+#pragma unroll
+      for (int db = 0; db < C::kNdb; ++db) {
+        const unsigned char *p1 = vs + (r0 + (tp >> 2)) * C::kVRow + (db * 32 + 16 * (gam & 1) + 4 * (tp & 3)) * 2;
+        const bf16x8 va = cat(lds_read_tr16(p1), lds_read_tr16(p1 + 8 * C::kVRow));
+        o[db] = mfma32(va, bp[t], o[db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // bound the V fragments held in registers
+    }
+  };
+  // Mask and online softmax of tile (qt, kt) on sacc; P^T -> bp.
+  auto softmax = [&](int qt, int kt) __attribute__((always_inline)) {
+    const int key0 = kt * kPfKeys;
+    const int pos = off + qt * kPfRows + w * 32 + col;
+    const int p_first = off + qt * kPfRows;
+    const int p_last = off + min(qt * kPfRows + kPfRows - 1, q_len - 1);
     // Mask (only tiles that cross a boundary; this lane's row sees keys
     // [klo, khi]) on the raw scores; the scale (> 0) is applied inside the
     // exponent, after the max.
@@ -329,37 +362,21 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) bp[t][e] = (__bf16)sacc[t >> 1][8 * (t & 1) + e];
-      // Materialise P here, in the QK half-step: left alone, the compiler
-      // sinks the exponentials to their use after the barrier, which would
-      // put the softmax on the same half-step as this engine's PV MFMAs.
+      // Materialise P in this (softmax) half-step, like S above.
       __asm__ volatile("" : "+v"(bp[t]));
     }
   };
 
-  // PV phase of a tile: O^T += V^T . P^T over four 16-key steps.
-  auto pv_phase = [&](int buf) {
-    const unsigned char *vs = vbuf(buf);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int r0 = (t >> 1) * 32 + (t & 1) * 16 + g * 4;
-#pragma unroll
-      for (int db = 0; db < C::kNdb; ++db) {
-        const unsigned char *p1 = vs + (r0 + (tp >> 2)) * C::kVRow + (db * 32 + 16 * (gam & 1) + 4 * (tp & 3)) * 2;
-        const bf16x8 va = cat(lds_read_tr16(p1), lds_read_tr16(p1 + 8 * C::kVRow));
-        o[db] = mfma32(va, bp[t], o[db]);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // bound the V fragments held in registers
-    }
-  };
-
-  // Ping-pong schedule in half-steps h (one barrier each).  Engine e runs
-  // the QK phase of its tile t at h = 2t + e and the PV phase at
-  // h = 2t + 1 + e, so at every half-step one engine is in its softmax
-  // (VALU) while the other multiplies (MFMA) on the same SIMDs.  Tile t lives in
-  // LDS buffer t % 2.  K(t+1) is loaded during PV(t-1) and stored at the
-  // start of QK(t) (its buffer was last read by QK(t-1)); V(t+1) is loaded
-  // during QK(t) and stored at the start of PV(t) (last read by PV(t-1)).
-  // So only one half of a tile is in registers at any time.
+  // Ping-pong schedule in half-steps (one workgroup barrier each).  For its
+  // tile t an engine runs a GEMM phase G(t) = [PV of tile t-1, QK of tile t]
+  // (MFMA) and then a softmax phase S(t) (VALU); after its last tile, G(n) =
+  // PV of tile n-1 alone.  Engine 1 runs one half-step behind engine 0, so on
+  // every SIMD one wave's softmax overlaps the other wave's MFMAs.  Tile t
+  // lives in LDS buffer t % 2.  Its K and V are loaded into registers at the
+  // start of G(t-1) and stored at the end of S(t-1): a whole step of load
+  // latency.  By then the buffer's previous tile t-2 has been read (its K by
+  // G(t-2), its V by G(t-1)), and the next reads, G(t) for K and G(t+1) for
+  // V, come after the next barrier.
   if (n_mine > 0) {
     int qt, kt;
     my_item(0, qt, kt);
@@ -367,53 +384,67 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     load_half(kt, vbase, pv);
     store_k(0, pk);
     store_v(0, pv);
-    if (n_mine > 1) {
-      my_item(1, qt, kt);
-      load_half(kt, kbase, pk);
-    }
   }
   __syncthreads();
-  // One step of tile t: QK phase, barrier, PV phase, barrier.  Engine 0
-  // starts at half-step 0, engine 1 one barrier later; each engine's loop is
-  // straight-line so that its registers keep one assignment.  Both engines
-  // pass 2 * half + 1 barriers in total.
-  auto step = [&](int t) {
+  auto gemm_phase = [&](int t) __attribute__((always_inline)) {
+    if (t + 1 < n_mine) {
+      int qt, kt;
+      my_item(t + 1, qt, kt);
+      load_half(kt, kbase, pk);
+      load_half(kt, vbase, pv);
+    }
+    if (t >= 1) pv_mfma((t - 1) & 1);
+    if (t < n_mine) {
+      int qt, kt;
+      my_item(t, qt, kt);
+      if (qt != qt_q) {
+        load_q(qt);
+        qt_q = qt;
+      }
+      qk_mfma(t & 1);
+    }
+  };
+  auto softmax_phase = [&](int t) __attribute__((always_inline)) {
     int qt, kt;
     my_item(t, qt, kt);
-    if (qt != qt_cur) {
-      if (qt_cur >= 0) finish(qt_cur, m, lsum, o);
-      start(qt);
-      qt_cur = qt;
+    if (qt != qt_o) {
+      if (qt_o >= 0) finish(qt_o, m, lsum, o);
+      reset_o();
+      qt_o = qt;
     }
-    const bool more = t + 1 < n_mine;
-    if (more) {
-      int qt_n, kt_n;
-      my_item(t + 1, qt_n, kt_n);
+    softmax(qt, kt);
+    if (t + 1 < n_mine) {
       store_k((t + 1) & 1, pk);
-      load_half(kt_n, vbase, pv);
+      store_v((t + 1) & 1, pv);
     }
-    qk_phase(qt, kt, t & 1);
-    __syncthreads();
-    if (more) store_v((t + 1) & 1, pv);
-    if (t + 2 < n_mine) {
-      int qt_n, kt_n;
-      my_item(t + 2, qt_n, kt_n);
-      load_half(kt_n, kbase, pk);
-    }
-    pv_phase(t & 1);
-    __syncthreads();
   };
+  // Engine 0 passes 2 * half + 1 barriers in its loop, engine 1 one leading
+  // barrier and 2 * n1 + 1 in its loop; the engine with fewer pads one at
+  // the end (half - n1 is 0 or 1).  Each engine's loop is its own
+  // straight-line code so that its registers keep one assignment.
   if (eng == 0) {
-    for (int t = 0; t < half; ++t) step(t);
+    for (int t = 0; t < n_mine; ++t) {
+      gemm_phase(t);
+      __syncthreads();
+      softmax_phase(t);
+      __syncthreads();
+    }
+    gemm_phase(n_mine);
     __syncthreads();
+    if (half == n1) __syncthreads();
   } else {
     __syncthreads();
-    for (int t = 0; t < n_mine; ++t) step(t);
-    for (int t = n_mine; t < half; ++t) {
+    for (int t = 0; t < n_mine; ++t) {
+      gemm_phase(t);
       __syncthreads();
+      softmax_phase(t);
       __syncthreads();
     }
+    gemm_phase(n_mine);
+    __syncthreads();
+    if (half > n1) __syncthreads();
   }
+  const int qt_cur = qt_o;
 
   // The query tile split between the engines (qb in the first case, qa in
   // the second; none if the split falls on the boundary, half == na) has a
