@@ -74,12 +74,12 @@ pa_status check_scale(float s) {
   return PA_OK;
 }
 
-// Decode workspace: partial (O, m, l) for batch * Hkv + nwg slots of G query
-// heads each, then batch + 1 int32 prefix sums.
+// Decode workspace: partial (O, m, l) for batch * Hkv / hpw + nwg slots of
+// hpw KV heads x G query heads each, then batch + 1 int32 prefix sums.
 size_t decode_ws_bytes(int batch, int hq, int hkv, int d, int nwg) {
-  const size_t slots = (size_t)batch * hkv + nwg;
+  const size_t heads = (size_t)batch * hkv + (size_t)nwg * pa::decode_heads_per_wg(hkv);
   const size_t g = (size_t)(hq / hkv);
-  return slots * g * ((size_t)d + 2) * sizeof(float) + ((size_t)batch + 1) * sizeof(int32_t);
+  return heads * g * ((size_t)d + 2) * sizeof(float) + ((size_t)batch + 1) * sizeof(int32_t);
 }
 
 }  // namespace
@@ -252,11 +252,13 @@ pa_status attn_decode_paged(const void *q, const pa_kv_cache *cache, const int32
   a.window_left = window_left < 0 ? -1 : window_left;
   a.out = out;
   a.lse = lse;
-  const size_t slots_g = ((size_t)batch * cache->num_kv_heads + nwg) * group;
+  const int hpw = pa::decode_heads_per_wg(cache->num_kv_heads);
+  const size_t slots_g = ((size_t)batch * cache->num_kv_heads + (size_t)nwg * hpw) * group;
   a.ws_o = (float *)workspace;
   a.ws_ml = a.ws_o + slots_g * cache->head_dim;
   a.ws_prefix = (int32_t *)(a.ws_ml + slots_g * 2);
   a.nwg = nwg;
+  a.hpw = hpw;
   return hip_status(pa::launch_decode(a, (hipStream_t)stream), "attn_decode_paged launch");
 }
 

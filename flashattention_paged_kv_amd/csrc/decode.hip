@@ -41,9 +41,9 @@
 
 namespace pa {
 
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = 8;
 constexpr int kDecTile = 32;            // keys per wave iteration
-constexpr int kDecWgsPerCu = 3;         // resident split workgroups per CU (register bound)
+constexpr int kDecWgsPerCu = 1;         // resident split workgroups per CU (register bound)
 
 // kDecWgsPerCu workgroups per CU of the current device (the split kernel's
 // occupancy, so the whole grid is resident at once), cached per device.  PAGEDATTN_DECODE_WGS overrides it (tests use
@@ -120,9 +120,10 @@ __device__ __forceinline__ int v_row(int k) {
 // NB: tiles in flight per wave (register buffers); WPC: resident workgroups
 // per CU the register budget is sized for (the grid is WPC per CU).
 template <int D, bool I8, int NB, int WPC>
-__global__ __launch_bounds__(256, WPC) void decode_split_kernel(DecodeArgs a, const int32_t *__restrict__ block_table,
-                                                               const float *__restrict__ k_scales,
-                                                               const float *__restrict__ v_scales) {
+__global__ __launch_bounds__(kDecWaves * 64, kDecWaves / 4 * WPC) void decode_split_kernel(DecodeArgs a,
+                                                                         const int32_t *__restrict__ block_table,
+                                                                         const float *__restrict__ k_scales,
+                                                                         const float *__restrict__ v_scales) {
   using C = DecodeCfg<D, I8>;
   __shared__ __align__(16) unsigned char smem[C::kSmem];
   __shared__ int s_wave_sum[kDecWaves];
@@ -134,11 +135,16 @@ __global__ __launch_bounds__(256, WPC) void decode_split_kernel(DecodeArgs a, co
   const int r16 = lane & 15;
   const int j = blockIdx.x;
   const int hkv = a.c.num_kv_heads;
+  const int hpw = a.hpw;            // KV heads per workgroup (a power of two dividing hkv, <= kDecWaves)
+  const int ngr = hkv / hpw;        // head groups
+  const int wph = kDecWaves / hpw;  // waves per head
+  const int hh = w % hpw;           // this wave's head inside the group
+  const int sub = w / hpw;          // and its share of that head's tiles
   const int W = a.window_left;
 
-  // --- Plan: tiles per sequence (same for every KV head), their prefix
-  // sums and the total, by a block scan over the batch.  Thread t owns the
-  // sequences [t*per, (t+1)*per).
+  // --- Plan: tiles per sequence (the same for every head group), their
+  // prefix sums and the total, by a block scan over the batch.  Thread t
+  // owns the sequences [t*per, (t+1)*per).
   const int per = (a.batch + blockDim.x - 1) / blockDim.x;
   const int b_lo = min(a.batch, (int)threadIdx.x * per);
   const int b_hi = min(a.batch, b_lo + per);
@@ -152,15 +158,15 @@ __global__ __launch_bounds__(256, WPC) void decode_split_kernel(DecodeArgs a, co
   }
   if (lane == 63) s_wave_sum[w] = incl;
   __syncthreads();
-  int before = 0, per_head_total = 0;
+  int before = 0, per_group_total = 0;
 #pragma unroll
   for (int i = 0; i < kDecWaves; ++i) {
     const int v = s_wave_sum[i];
     before += i < w ? v : 0;
-    per_head_total += v;
+    per_group_total += v;
   }
-  const int excl = before + incl - mine;  // per-head tiles of sequences < b_lo
-  const long long total = (long long)hkv * per_head_total;
+  const int excl = before + incl - mine;  // per-group tiles of sequences < b_lo
+  const long long total = (long long)ngr * per_group_total;
   const int nwg = active_wgs(total, a.nwg);
   if (j == 0) {
     // The merge kernel reads the per-sequence prefix sums from here.
@@ -169,17 +175,17 @@ __global__ __launch_bounds__(256, WPC) void decode_split_kernel(DecodeArgs a, co
       a.ws_prefix[bb] = acc;
       acc += seg_tiles(a.ctx_lens[bb], W);
     }
-    if (threadIdx.x == 0) a.ws_prefix[a.batch] = per_head_total;
+    if (threadIdx.x == 0) a.ws_prefix[a.batch] = per_group_total;
   }
   if (j >= nwg) return;  // uniform across the workgroup
   const long long start = (long long)j * total / nwg;
   const long long end = (long long)(j + 1) * total / nwg;
   // The thread whose sequences hold list position `start` finds it.
-  if ((long long)hkv * excl <= start && start < (long long)hkv * (excl + mine)) {
+  if ((long long)ngr * excl <= start && start < (long long)ngr * (excl + mine)) {
     int acc = excl;
     for (int bb = b_lo; bb < b_hi; ++bb) {
       const int n = seg_tiles(a.ctx_lens[bb], W);
-      if (start < (long long)hkv * (acc + n)) {
+      if (start < (long long)ngr * (acc + n)) {
         s_first[0] = bb;
         s_first[1] = acc;
         break;
@@ -198,9 +204,9 @@ __global__ __launch_bounds__(256, WPC) void decode_split_kernel(DecodeArgs a, co
 
   int b = s_first[0];
   int nb = seg_tiles(a.ctx_lens[b], W);
-  const int r0 = (int)(start - (long long)hkv * s_first[1]);
-  int hk = r0 / nb;
-  int tloc = r0 - hk * nb;
+  const int r0 = (int)(start - (long long)ngr * s_first[1]);
+  int hg = r0 / nb;
+  int tloc = r0 - hg * nb;
   long long remaining = end - start;
 
   while (remaining > 0) {
@@ -210,7 +216,8 @@ __global__ __launch_bounds__(256, WPC) void decode_split_kernel(DecodeArgs a, co
     const int t_first = lo / kDecTile + tloc;  // first tile of this piece
     const int k_begin = max(lo, t_first * kDecTile);
     const int k_end = min(ctx, (t_first + len) * kDecTile);
-    const int n_w = (len - w + kDecWaves - 1) / kDecWaves;  // this wave's tiles
+    const int n_w = (len - sub + wph - 1) / wph;  // this wave's tiles
+    const int hk = hg * hpw + hh;
     const uint32_t head_off = (uint32_t)hk * D * C::kEsz;
     const int32_t *bt = block_table + (size_t)b * a.max_pages;
 
@@ -235,7 +242,7 @@ __global__ __launch_bounds__(256, WPC) void decode_split_kernel(DecodeArgs a, co
     const int lo16 = k_begin & ~15;
     const int hi16 = (k_end - 1) & ~15;
     auto blk = [&](int i, int kb, const void *pool, uint32_t &off) {
-      const int t = t_first + w + kDecWaves * min(i, n_w - 1);
+      const int t = t_first + sub + wph * min(i, n_w - 1);
       const int bs = min(max(t * kDecTile + 16 * kb, lo16), hi16);
       const int key = min(max(t * kDecTile + 16 * kb + r16, k_begin), k_end - 1);
       const size_t pbase = (size_t)bt[bs >> lp] * page_bytes + head_off;
@@ -261,10 +268,11 @@ __global__ __launch_bounds__(256, WPC) void decode_split_kernel(DecodeArgs a, co
     // Register buffers recycled half by half: V(i) is staged to LDS and its
     // registers take V(i + NB); K(i) feeds the QK product and its
     // registers take K(i + NB).  NB tiles are in flight while a tile is
-    // computed.  The loop runs a multiple of NB steps; a step past the wave's last tile re-reads that tile and masks
-    // every key, which leaves (m, l, O) exactly unchanged.
+    // computed.  The loop runs a multiple of NB steps; a step past the
+    // wave's last tile re-reads that tile and masks every key, which leaves
+    // (m, l, O) exactly unchanged.
     auto step = [&](int i, TileRegs<D, I8> &R) {
-      const int key0 = (t_first + w + kDecWaves * i) * kDecTile;
+      const int key0 = (t_first + sub + wph * i) * kDecTile;
       // Stage V rows for the transposed reads.
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -378,8 +386,9 @@ __global__ __launch_bounds__(256, WPC) void decode_split_kernel(DecodeArgs a, co
     }
     lsum = sum_xor32(sum_xor16(lsum));
 
-    // Merge the 4 waves' (m, l, O) through LDS (a wave without tiles has
-    // m = -inf, l = 0, O = 0 and drops out) and write this piece's partial.
+    // Merge the waves of each head (wph of them; a wave without tiles has
+    // m = -inf, l = 0, O = 0 and drops out) through LDS and write this
+    // piece's partial for each of the group's heads.
     __syncthreads();
     float *wo = reinterpret_cast<float *>(smem);
     float *wm = wo + kDecWaves * 16 * D;
@@ -395,60 +404,65 @@ __global__ __launch_bounds__(256, WPC) void decode_split_kernel(DecodeArgs a, co
       }
     }
     __syncthreads();
-    const size_t slot = (size_t)b * hkv + hk + j;
-    for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-      const int c = e / D;
-      const int d = e - c * D;
+    const size_t slot = (size_t)b * ngr + hg + j;
+    for (int e = threadIdx.x; e < hpw * G * D; e += blockDim.x) {
+      const int eh = e / (G * D);
+      const int rem = e - eh * G * D;
+      const int c = rem / D;
+      const int d = rem - c * D;
       float big_m = -INFINITY;
-#pragma unroll
-      for (int ww = 0; ww < kDecWaves; ++ww) big_m = fmaxf(big_m, wm[ww * 16 + c]);
+      for (int s = 0; s < wph; ++s) big_m = fmaxf(big_m, wm[(eh + hpw * s) * 16 + c]);
       float big_l = 0.f, acc = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < kDecWaves; ++ww) {
+      for (int s = 0; s < wph; ++s) {
+        const int ww = eh + hpw * s;
         const float mw = wm[ww * 16 + c];
         const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - big_m);
         big_l += wl[ww * 16 + c] * f;
         acc += wo[(ww * 16 + c) * D + d] * f;
       }
-      a.ws_o[(slot * G + c) * D + d] = acc;
+      const size_t idx = (slot * hpw + eh) * G + c;
+      a.ws_o[idx * D + d] = acc;
       if (d == 0) {
-        a.ws_ml[(slot * G + c) * 2] = big_m;
-        a.ws_ml[(slot * G + c) * 2 + 1] = big_l;
+        a.ws_ml[idx * 2] = big_m;
+        a.ws_ml[idx * 2 + 1] = big_l;
       }
     }
     __syncthreads();  // the LDS is staged into again by the next piece
-
     remaining -= len;
     tloc = 0;
-    if (++hk == hkv && remaining > 0) {
-      hk = 0;
+    if (++hg == ngr && remaining > 0) {
+      hg = 0;
       ++b;
       nb = seg_tiles(a.ctx_lens[b], W);
     }
   }
 }
 
-// Merge the partials of one (sequence, KV head) segment for its G query
-// heads: M = max m_s, L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M) / L,
+// Merge the partials of one (sequence, KV head) for its G query heads:
+// M = max m_s, L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M) / L,
 // accumulated in one pass with the same running rescale as the online
-// softmax.  The workgroups that touched the segment are those whose list
-// ranges contain its first and last tiles and every one in between.  A
-// thread owns 4 consecutive dims of one query head.
+// softmax.  The workgroups that touched the head's segment (sequence, head
+// group) are those whose list ranges contain its first and last tiles and
+// every one in between.  A thread owns 4 consecutive dims of one query head.
 template <int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   const int hk = blockIdx.x;
   const int b = blockIdx.y;
   const int hkv = a.c.num_kv_heads;
+  const int hpw = a.hpw;
+  const int ngr = hkv / hpw;
+  const int hg = hk / hpw;
+  const int hh = hk - hg * hpw;
   const int G = a.group;
-  const long long total = (long long)hkv * a.ws_prefix[a.batch];
+  const long long total = (long long)ngr * a.ws_prefix[a.batch];
   const int nwg = active_wgs(total, a.nwg);
   const int nb = seg_tiles(a.ctx_lens[b], a.window_left);
-  const long long f0 = (long long)hkv * a.ws_prefix[b] + (long long)hk * nb;
+  const long long f0 = (long long)ngr * a.ws_prefix[b] + (long long)hg * nb;
   const long long f1 = f0 + nb - 1;
   // Workgroup holding list position f: the largest j with j*total/nwg <= f.
   const int j_lo = (int)(((f0 + 1) * nwg - 1) / total);
   const int j_hi = (int)(((f1 + 1) * nwg - 1) / total);
-  const size_t seg = (size_t)b * hkv + hk;
+  const size_t seg = (size_t)b * ngr + hg;
   for (int e = 4 * threadIdx.x; e < G * D; e += 4 * blockDim.x) {
     const int c = e / D;
     const int d = e - c * D;
@@ -456,7 +470,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
     for (int jj = j_lo; jj <= j_hi; ++jj) {
-      const size_t idx = (seg + jj) * G + c;
+      const size_t idx = ((seg + jj) * hpw + hh) * G + c;
       const float2 ml = *reinterpret_cast<const float2 *>(a.ws_ml + idx * 2);
       const f32x4 ov = *reinterpret_cast<const f32x4 *>(a.ws_o + idx * D + d);
       const float m_new = fmaxf(m, ml.x);
@@ -563,7 +577,7 @@ hipError_t launch_rowwise_f32(const PrefillArgs &a, hipStream_t s) {
 
 template <int D, bool I8, int NB, int WPC>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_split_kernel<D, I8, NB, WPC>), dim3(a.nwg), dim3(256), 0, s, a, a.block_table,
+  hipLaunchKernelGGL((decode_split_kernel<D, I8, NB, WPC>), dim3(a.nwg), dim3(kDecWaves * 64), 0, s, a, a.block_table,
                      a.c.k_scales, a.c.v_scales);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -82,12 +82,21 @@ struct DecodeArgs {
   float *ws_o;         // [slots, G, head_dim] partial outputs (unnormalised)
   float *ws_ml;        // [slots, G, 2] partial (max in log2 units, sum)
   int32_t *ws_prefix;  // [batch + 1] tiles per KV head before sequence b; total last
-  int nwg;             // workgroups launched; slots = batch * Hkv + nwg
+  int nwg;             // workgroups launched
+  int hpw;             // KV heads per split workgroup; slots = batch * Hkv / hpw + nwg, hpw heads each
 };
 
 // Decode grid size (workgroups) on the current device, used by both the
 // workspace query and the call.
 int decode_grid_size();
+// KV heads a decode split workgroup handles together: the largest power of
+// two <= 8 that divides hkv (its waves then read whole contiguous rows of
+// those heads).
+inline int decode_heads_per_wg(int hkv) {
+  int h = 8;
+  while (hkv % h != 0) h >>= 1;
+  return h;
+}
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
