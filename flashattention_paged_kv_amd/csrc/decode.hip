@@ -11,18 +11,22 @@
 // page's Flash Attention section is applied per wave, then across the waves of
 // a workgroup, then across splits; all three merges are the same algebra.
 //
-// Work split (balanced for ragged context lengths): the keys of every
-// (sequence b, KV head hk) pair form a segment of 32-key tiles; all segments
-// laid end to end make one list of T tiles.  A fixed grid of N workgroups
-// (a few per CU) cuts the list into N equal ranges, [jT/N, (j+1)T/N) for
-// workgroup j, so every workgroup streams the same number of bytes whatever
-// the length mix.  A range is cut further at segment boundaries into pieces;
-// for each piece the workgroup's 4 waves take every 4th tile, merge their
-// running (m, l, O) through LDS and write one partial to slot (segment + j),
-// which is unique because both the segments and the ranges are in list
-// order.  All G = Hq/Hkv query heads of hk are handled together so each K/V
-// byte is read from HBM once.  The merge kernel finds the workgroups that
-// touched a segment from the same arithmetic and combines their partials.
+// Work split (balanced for ragged context lengths): a split workgroup has 8
+// waves and handles hpw KV heads together (the largest power of two <= 8
+// dividing Hkv); wave w takes head w % hpw and every (8 / hpw)-th tile of
+// it, so with 8 KV heads the workgroup reads whole contiguous token rows.
+// The keys of every (sequence b, head group) pair form a segment of 32-key
+// tiles; all segments laid end to end make one list of T tiles.  A fixed
+// grid of N workgroups (one per CU) cuts the list into N equal ranges,
+// [jT/N, (j+1)T/N) for workgroup j, so every workgroup streams the same
+// number of bytes whatever the length mix.  A range is cut further at
+// segment boundaries into pieces; for each piece the waves of each head
+// merge their running (m, l, O) through LDS and write one partial per head
+// to slot (segment + j), which is unique because both the segments and the
+// ranges are in list order.  All G = Hq/Hkv query heads of a KV head are
+// handled together so each K/V byte is read from HBM once.  The merge
+// kernel finds the workgroups that touched a segment from the same
+// arithmetic and combines their partials.
 //
 // Per 32-key tile a wave computes S^T = K . Q^T with v_mfma_f32_16x16x32_bf16
 // (keys on the M side, query heads on the N side, zero-padded to 16), the

@@ -22,18 +22,20 @@
 // step while both are in the shared prefix.  The query tile split between
 // them is merged in LDS at the end with the same rescaling algebra as the
 // online softmax.  Each engine has its own double-buffered K/V tiles in LDS
-// and prefetches the next key tile into registers while it computes the
-// current one: one barrier per step for the whole workgroup (both engines
-// run the same number of steps).  Workgroup ids are remapped so that the
-// pairs of one query head run on the same XCD (shared L2) and stream its
-// K/V tiles together.
+// and loads the next key tile into registers a whole step ahead.  Workgroup
+// ids are remapped so that the pairs of one query head run on the same XCD
+// (shared L2) and stream its K/V tiles together.
 //
-// Per step a wave (32 query rows) computes S^T = K . Q^T with
-// v_mfma_f32_32x32x16_bf16 (keys on M, its rows on N, Q^T in registers),
-// the mask and the online softmax on the S^T registers (one query per lane
-// column: one cross-lane max per tile), and O^T += V^T . P^T with V^T read
-// transposed from LDS by ds_read_b64_tr_b16 and P^T straight from the S^T
-// registers (rounded to bf16).  exp is exp2 with log2(e) folded into the
+// Per key tile a wave (32 query rows) runs a GEMM phase and a softmax phase,
+// each ended by a workgroup barrier, with engine 1 one phase behind engine
+// 0 so that on every SIMD one wave's softmax (VALU) overlaps the other
+// wave's MFMAs.  The GEMM phase computes O^T += V^T . P^T of the previous
+// tile (V^T read transposed from LDS by ds_read_b64_tr_b16, P^T from
+// registers) and S^T = K . Q^T of this tile, both with
+// v_mfma_f32_32x32x16_bf16 (keys on M, the wave's rows on N, Q^T in
+// registers).  The softmax phase applies the mask and the online softmax on
+// the S^T registers (one query per lane column: one cross-lane max per
+// tile) and rounds P^T to bf16.  exp is exp2 with log2(e) folded into the
 // scale.  The running output is rescaled only when a row's maximum grows by
 // more than 2^8 over its reference (the exponent reference may lag the true
 // maximum by at most that much: probabilities stay <= 256, and O and l share
