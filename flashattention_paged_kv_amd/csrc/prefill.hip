@@ -277,36 +277,53 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   };
 
   // S^T = K . Q^T for the two 32-key blocks of the tile in LDS buffer `buf`.
+  // S^T = K . Q^T for the two 32-key blocks of the tile in LDS buffer `buf`.
+  // The K fragments are read kAhead MFMAs ahead of their use (a ring of
+  // registers), so the LDS latency hides behind the MFMAs before them.
   auto qk_mfma = [&](int buf) __attribute__((always_inline)) {
     const unsigned char *ks = kbuf(buf);
+    constexpr int kSteps = 2 * C::kNs;  // (key block, k-step) pairs
+    constexpr int kAhead = 4;
+    auto rd = [&](int u) __attribute__((always_inline)) {
+      const int kb = u / C::kNs, s = u % C::kNs;
+      return *reinterpret_cast<const bf16x8 *>(ks + (kb * 32 + col) * C::kKRow + (16 * s + 8 * g) * 2);
+    };
+    bf16x8 ka[kAhead];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int u = 0; u < kAhead; ++u) ka[u] = rd(u);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-      for (int s = 0; s < C::kNs; ++s) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(ks + (kb * 32 + col) * C::kKRow + (16 * s + 8 * g) * 2);
-        sacc[kb] = mfma32(ka, bq[s], sacc[kb]);
-      }
+    for (int u = 0; u < kSteps; ++u) {
+      const int kb = u / C::kNs, s = u % C::kNs;
+      const bf16x8 cur = ka[u % kAhead];
+      if (u + kAhead < kSteps) ka[u % kAhead] = rd(u + kAhead);
+      sacc[kb] = mfma32(cur, bq[s], s == 0 ? f32x16{} : sacc[kb]);
       // Keep the product in this (GEMM) half-step: left alone, the compiler
       // sinks it to its first use after the barrier.
-      __asm__ volatile("" : "+v"(sacc[kb]));
-      __builtin_amdgcn_sched_barrier(0);  // bound the K fragments held in registers
+      if (s == C::kNs - 1) __asm__ volatile("" : "+v"(sacc[kb]));
+      __builtin_amdgcn_sched_barrier(0);  // keep each read kAhead MFMAs ahead
     }
   };
-  // O^T += V^T . P^T over four 16-key steps, V from LDS buffer `buf`.
+  // O^T += V^T . P^T over four 16-key steps, V from LDS buffer `buf`.  The
+  // V^T fragments of step t + 1 are read before the MFMAs of step t.
+  auto read_v = [&](const unsigned char *vs, int t, bf16x8 *va) __attribute__((always_inline)) {
+    const int r0 = (t >> 1) * 32 + (t & 1) * 16 + g * 4;
+#pragma unroll
+    for (int db = 0; db < C::kNdb; ++db) {
+      const unsigned char *p1 = vs + (r0 + (tp >> 2)) * C::kVRow + (db * 32 + 16 * (gam & 1) + 4 * (tp & 3)) * 2;
+      va[db] = cat(lds_read_tr16(p1), lds_read_tr16(p1 + 8 * C::kVRow));
+    }
+  };
   auto pv_mfma = [&](int buf) __attribute__((always_inline)) {
     const unsigned char *vs = vbuf(buf);
+    bf16x8 va[2][C::kNdb];
+    read_v(vs, 0, va[0]);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int r0 = (t >> 1) * 32 + (t & 1) * 16 + g * 4;
+      if (t + 1 < 4) read_v(vs, t + 1, va[(t + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);  // the next step's reads go out first
 #pragma unroll
-      for (int db = 0; db < C::kNdb; ++db) {
-        const unsigned char *p1 = vs + (r0 + (tp >> 2)) * C::kVRow + (db * 32 + 16 * (gam & 1) + 4 * (tp & 3)) * 2;
-        const bf16x8 va = cat(lds_read_tr16(p1), lds_read_tr16(p1 + 8 * C::kVRow));
-        o[db] = mfma32(va, bp[t], o[db]);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // bound the V fragments held in registers
+      for (int db = 0; db < C::kNdb; ++db) o[db] = mfma32(va[t & 1][db], bp[t], o[db]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // Mask and online softmax of tile (qt, kt) on sacc; P^T -> bp.
