@@ -62,11 +62,19 @@ def _traffic(kernel: str, workload: str):
     return round(t["hbm_bytes_per_launch"])
 
 
-def _time_loop(fn, steps: int, warmup: int) -> float:
-    """Average ms per call of fn() over `steps` back-to-back calls."""
+def _time_loop(fn, steps: int, warmup: int, min_warm_s: float = 0.2) -> float:
+    """Average ms per call of fn() over `steps` back-to-back calls.  The
+    untimed warm-up runs `warmup` calls and then keeps calling until at least
+    `min_warm_s` seconds of work have run, so the clocks have settled before
+    the timed region (a 50-call loop of a 60 us kernel is over in 3 ms)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_warm_s:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(steps):

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   auto qk_mfma = [&](int buf) __attribute__((always_inline)) {
     const unsigned char *ks = kbuf(buf);
     constexpr int kSteps = 2 * C::kNs;  // (key block, k-step) pairs
-    constexpr int kAhead = 4;
+    constexpr int kAhead = 6;
     auto rd = [&](int u) __attribute__((always_inline)) {
       const int kb = u / C::kNs, s = u % C::kNs;
       return *reinterpret_cast<const bf16x8 *>(ks + (kb * 32 + col) * C::kKRow + (16 * s + 8 * g) * 2);
@@ -405,7 +405,11 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     store_v(0, pv);
   }
   __syncthreads();
+  // Wave priorities: the GEMM wave's MFMAs are the critical path of each
+  // half-step, so its instructions win issue slots over the other engine's
+  // softmax on the same SIMD.
   auto gemm_phase = [&](int t) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(2);
     if (t + 1 < n_mine) {
       int qt, kt;
       my_item(t + 1, qt, kt);
@@ -424,6 +428,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     }
   };
   auto softmax_phase = [&](int t) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(0);
     int qt, kt;
     my_item(t, qt, kt);
     if (qt != qt_o) {
