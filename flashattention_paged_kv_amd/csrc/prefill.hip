@@ -12,10 +12,12 @@
 // 技术" section 2.1).
 //
 // Work split.  Query rows are cut into 128-row tiles; a tile's work is the
-// list of 64-key tiles it can see.  One workgroup of 8 waves takes the pair
-// of query tiles (p, n-1-p) of one (sequence, query head): under a causal
-// mask their key-tile counts add up to the same total for every p, so all
-// workgroups carry equal work.  The workgroup is two engines of 4 waves that
+// list of 64-key tiles it can see.  Under a causal mask without a window, one
+// workgroup of 8 waves takes the pair of query tiles (p, n-1-p) of one
+// (sequence, query head): their key-tile counts add up to the same total for
+// every p, so all workgroups carry equal work.  With a window or without a
+// mask every query tile has about the same work, and a workgroup takes a run
+// of 8 consecutive query tiles instead (fewer, longer workgroups).  The workgroup is two engines of 4 waves that
 // each take half of the pair's key tiles: engine 0 all of the earlier tile
 // and the top of the later one, engine 1 the bottom of the later one, both
 // ascending, so that the two engines read the same key tile at the same
@@ -53,6 +55,7 @@ constexpr int kPfRows = 128;         // query rows per query tile (4 waves x 32)
 constexpr int kPfKeys = 64;          // keys per key tile
 constexpr int kPfEngineThreads = 256;
 constexpr float kPfSlack = 8.f;      // log2 of the largest probability allowed
+constexpr int kPfRun = 8;            // query tiles per workgroup in run mode
 
 template <int D>
 struct PfCfg {
@@ -73,7 +76,7 @@ struct PfCfg {
 // BIG_PAGE: page_size >= 64, so each 64-key tile lies in one page.
 // block_table is a.block_table, passed again as a restrict pointer so that
 // uniform page-id reads are scalar loads.
-template <int D, bool BIG_PAGE>
+template <int D, bool BIG_PAGE, bool RUNS>
 __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, const int32_t *__restrict__ block_table) {
   using C = PfCfg<D>;
   __shared__ __align__(16) unsigned char smem[2 * C::kEngine];
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
   // L2): consecutive ids are remapped so that the pairs of one query head run
   // on one XCD and stream that head's K/V tiles together.
-  int pair = blockIdx.x;
+  int pair = blockIdx.x;  // pair mode: the pair index; run mode: the run index
   int h = blockIdx.y;
   const int b = blockIdx.z;
   if ((gridDim.y & 7) == 0) {
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   const int q0 = __builtin_amdgcn_readfirstlane(a.cu_q[b]);
   const int q_len = __builtin_amdgcn_readfirstlane(a.cu_q[b + 1]) - q0;
   const int n_qt = (q_len + kPfRows - 1) / kPfRows;
-  if (pair >= (n_qt + 1) / 2) return;  // uniform
+  if (RUNS ? pair * kPfRun >= n_qt : pair >= (n_qt + 1) / 2) return;  // uniform
   const int ctx = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
   const int off = ctx - q_len;
   const int hk = h / a.group;
@@ -120,53 +123,115 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     lo = k_lo / kPfKeys;
     hi = (k_hi + kPfKeys - 1) / kPfKeys;
   };
-  const int qa = pair;
-  const int qb = n_qt - 1 - pair;  // == qa for the middle tile of an odd count
-  int lo_a, hi_a, lo_b = 0, hi_b = 0;
-  tile_range(qa, lo_a, hi_a);
-  if (qb != qa) tile_range(qb, lo_b, hi_b);
-  // Split of the pair's key tiles between the engines, half each.  With
-  // na <= nb (always under a causal mask, tile qa being the earlier one):
-  // engine 0 takes all of qa, then the top of qb's tiles; engine 1 takes the
-  // bottom of qb's tiles.  Both ascend, so under a causal mask (both ranges
-  // start at key 0) the engines read the same key tile at the same step.
-  // Otherwise (na > nb, or the middle tile of an odd count, nb = 0): engine 0
-  // takes the bottom of qa; engine 1 takes all of qb, then the top of qa.
-  // Either way the query tile split between the engines (if any) is the last
-  // one each engine works on.
-  const int na = hi_a - lo_a;
-  const int nb = hi_b - lo_b;
-  const int total = na + nb;
-  const int half = (total + 1) / 2;
-  const int n1 = total - half;
-  const int n_mine = eng == 0 ? half : n1;
-  // This engine's items as two runs of consecutive key tiles: item t < s1
-  // is (q1, k1 + t), item t >= s1 is (q2, k2 + t - s1).
-  int s1, q1, k1, q2, k2;
-  if (na <= nb) {
-    if (eng == 0) {
-      s1 = na, q1 = qa, k1 = lo_a, q2 = qb, k2 = lo_b + n1;
+  // The workgroup's items (query tile, key tile) are split between the
+  // engines, half each, as runs of consecutive key tiles of one query tile:
+  // run j of this engine covers its items [st[j], st[j+1]) with query tile
+  // rq[j] and first key tile rk[j].  Whichever query tile the split falls in
+  // (if any) is the last one both engines work on; it is merged at the end.
+  constexpr int kRuns = RUNS ? kPfRun : 2;
+  int st[kRuns], rq[kRuns], rk[kRuns];
+  int total, half, n1;
+  bool shared;
+  if constexpr (!RUNS) {
+    // Pair mode (causal, no window): query tiles (p, n-1-p), whose key-tile
+    // counts add up to the same total for every p.  With na <= nb (always
+    // under a causal mask, tile qa being the earlier one): engine 0 takes all
+    // of qa, then the top of qb's tiles; engine 1 takes the bottom of qb's
+    // tiles.  Both ascend, so (both ranges starting at key 0) the engines
+    // read the same key tile at the same step.  Otherwise (na > nb, or the
+    // middle tile of an odd count, nb = 0): engine 0 takes the bottom of qa;
+    // engine 1 takes all of qb, then the top of qa.
+    const int qa = pair;
+    const int qb = n_qt - 1 - pair;  // == qa for the middle tile of an odd count
+    int lo_a, hi_a, lo_b = 0, hi_b = 0;
+    tile_range(qa, lo_a, hi_a);
+    if (qb != qa) tile_range(qb, lo_b, hi_b);
+    const int na = hi_a - lo_a;
+    const int nb = hi_b - lo_b;
+    total = na + nb;
+    half = (total + 1) / 2;
+    n1 = total - half;
+    shared = half != na;
+    st[0] = 0;
+    if (na <= nb) {
+      if (eng == 0) {
+        rq[0] = qa, rk[0] = lo_a, st[1] = na, rq[1] = qb, rk[1] = lo_b + n1;
+      } else {
+        rq[0] = qb, rk[0] = lo_b, st[1] = n1, rq[1] = qb, rk[1] = lo_b + n1;
+      }
     } else {
-      s1 = 0, q1 = qb, k1 = lo_b, q2 = qb, k2 = lo_b;
+      if (eng == 0) {
+        rq[0] = qa, rk[0] = lo_a, st[1] = half, rq[1] = qa, rk[1] = lo_a + half;
+      } else {
+        rq[0] = qb, rk[0] = lo_b, st[1] = nb, rq[1] = qa, rk[1] = lo_a + half;
+      }
     }
   } else {
+    // Run mode (a window, or no causal mask: about the same work for every
+    // query tile): kPfRun consecutive query tiles.  Engine 0 takes the first
+    // half of their items in order; engine 1 takes the second half with its
+    // query tiles in reverse order, so that the tile holding the split comes
+    // last for both.
+    const int q_begin = pair * kPfRun;
+    int lo[kPfRun], cum[kPfRun + 1];
+    cum[0] = 0;
+#pragma unroll
+    for (int r = 0; r < kPfRun; ++r) {
+      int l = 0, hh = 0;
+      if (q_begin + r < n_qt) tile_range(q_begin + r, l, hh);
+      lo[r] = l;
+      cum[r + 1] = cum[r] + (hh - l);
+    }
+    total = cum[kPfRun];
+    half = (total + 1) / 2;
+    n1 = total - half;
+    shared = false;
+#pragma unroll
+    for (int r = 1; r < kPfRun; ++r) shared |= cum[r] == half;
+    shared = !shared && half > 0 && half < total;
     if (eng == 0) {
-      s1 = 0, q1 = qa, k1 = lo_a, q2 = qa, k2 = lo_a;
+#pragma unroll
+      for (int r = 0; r < kPfRun; ++r) {
+        st[r] = min(cum[r], half);
+        rq[r] = q_begin + r;
+        rk[r] = lo[r];
+      }
     } else {
-      s1 = nb, q1 = qb, k1 = lo_b, q2 = qa, k2 = lo_a + half;
+      int at = 0;
+#pragma unroll
+      for (int j = 0; j < kPfRun; ++j) {
+        const int r = kPfRun - 1 - j;
+        const int first = max(cum[r], half);
+        st[j] = at;
+        rq[j] = q_begin + r;
+        rk[j] = lo[r] + (first - cum[r]);
+        at += max(0, cum[r + 1] - first);
+      }
     }
   }
-  // Written as offsets from the second run so that the choice between runs
-  // is a choice between a value and zero (kept in scalar registers).
-  const int run1 = __builtin_amdgcn_readfirstlane(s1);
-  const int qt2 = __builtin_amdgcn_readfirstlane(q2);
-  const int dq = __builtin_amdgcn_readfirstlane(q1 - q2);
-  const int kt2 = __builtin_amdgcn_readfirstlane(k2 - s1);
-  const int dk = __builtin_amdgcn_readfirstlane(k1 - (k2 - s1));
+  const int n_mine = eng == 0 ? half : n1;
+  // my_item(t): run j applies when t >= st[j] (runs in increasing start
+  // order, empty ones telescoping away).  Written as sums of "value or zero"
+  // offsets between consecutive runs, kept in scalar registers.
+  int dst[kRuns], ddq[kRuns], ddk[kRuns];
+  const int q_base = __builtin_amdgcn_readfirstlane(rq[0]);
+  const int k_base = __builtin_amdgcn_readfirstlane(rk[0] - st[0]);
+#pragma unroll
+  for (int j = 1; j < kRuns; ++j) {
+    dst[j] = __builtin_amdgcn_readfirstlane(st[j]);
+    ddq[j] = __builtin_amdgcn_readfirstlane(rq[j] - rq[j - 1]);
+    ddk[j] = __builtin_amdgcn_readfirstlane((rk[j] - st[j]) - (rk[j - 1] - st[j - 1]));
+  }
   auto my_item = [=](int t, int &qt, int &kt) __attribute__((always_inline)) {
-    const bool first = t < run1;
-    qt = qt2 + (first ? dq : 0);
-    kt = t + kt2 + (first ? dk : 0);
+    int q = q_base, k = t + k_base;
+#pragma unroll
+    for (int j = 1; j < kRuns; ++j) {
+      const bool in = t >= dst[j];
+      q += in ? ddq[j] : 0;
+      k += in ? ddk[j] : 0;
+    }
+    qt = q;
+    kt = k;
   };
 
   unsigned char *ebase = smem + eng * C::kEngine;
@@ -338,14 +403,17 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     const bool edge = (causal && key0 + kPfKeys - 1 > p_first) || (W >= 0 && key0 < p_last - W) ||
                       (key0 + kPfKeys > ctx);
     if (edge) {
-      const int khi = causal ? min(pos, ctx - 1) : ctx - 1;
-      const int klo = W >= 0 ? pos - W : 0;
+      // Bounds relative to this lane's first key, so that each element's
+      // offset in the tile is a constant: visible iff lo <= offset <= hi.
+      const int base = key0 + g * 4;
+      const int hi = (causal ? min(pos, ctx - 1) : ctx - 1) - base;
+      const int lo = (W >= 0 ? pos - W : 0) - base;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = key0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-          sacc[kb][i] = ((key >= klo) & (key <= khi)) ? sacc[kb][i] : -INFINITY;
+          const int c = kb * 32 + (i >> 2) * 8 + (i & 3);
+          sacc[kb][i] = ((c >= lo) & (c <= hi)) ? sacc[kb][i] : -INFINITY;
         }
     }
     float mx0 = -INFINITY, mx1 = -INFINITY;
@@ -474,7 +542,6 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // the second; none if the split falls on the boundary, half == na) has a
   // partial result in each engine: engine 0 hands its (m, l, O) to engine 1
   // through LDS (the K/V buffers are free now) and engine 1 merges.
-  const bool shared = half != na;
   if (!shared) {
     if (qt_cur >= 0) finish(qt_cur, m, lsum, o);
     return;
@@ -512,16 +579,28 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
   if (a.batch == 0 || a.max_q_len == 0) return hipSuccess;
   if (a.c.dtype == 0) return launch_rowwise_f32(a, s);
   const int n_qt = (a.max_q_len + kPfRows - 1) / kPfRows;
-  dim3 grid((n_qt + 1) / 2, a.num_q_heads, a.batch);
+  // Causal without a window: pairs (p, n-1-p) balance the triangle.  A window
+  // or no mask gives every query tile about the same work: runs of kPfRun.
+  const bool runs = !(a.causal && a.window_left < 0);
+  dim3 grid(runs ? (n_qt + kPfRun - 1) / kPfRun : (n_qt + 1) / 2, a.num_q_heads, a.batch);
   const dim3 block(2 * kPfEngineThreads);
   const bool big = a.c.page_size >= kPfKeys;
+#define PA_PREFILL_LAUNCH(DD, BIG, RUN) \
+  hipLaunchKernelGGL((prefill_bf16_kernel<DD, BIG, RUN>), grid, block, 0, s, a, a.block_table)
   if (a.c.head_dim == 64) {
-    if (big) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, s, a, a.block_table);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, s, a, a.block_table);
+    if (runs) {
+      if (big) PA_PREFILL_LAUNCH(64, true, true); else PA_PREFILL_LAUNCH(64, false, true);
+    } else {
+      if (big) PA_PREFILL_LAUNCH(64, true, false); else PA_PREFILL_LAUNCH(64, false, false);
+    }
   } else {
-    if (big) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, s, a, a.block_table);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, s, a, a.block_table);
+    if (runs) {
+      if (big) PA_PREFILL_LAUNCH(128, true, true); else PA_PREFILL_LAUNCH(128, false, true);
+    } else {
+      if (big) PA_PREFILL_LAUNCH(128, true, false); else PA_PREFILL_LAUNCH(128, false, false);
+    }
   }
+#undef PA_PREFILL_LAUNCH
   return hipGetLastError();
 }
 

@@ -55,6 +55,10 @@ PREFILL_CASES = [
     wl.PrefillWorkload("bf16_d128_g8_win128", (400, 129), 8, 1, 128, 64, "bf16", seed=33, window_left=128),
     wl.PrefillWorkload("bf16_d128_win_big", (300,), 2, 2, 128, 16, "bf16", seed=34, window_left=5000),
     wl.PrefillWorkload("bf16_noncausal", (100, 65), 2, 2, 128, 16, "bf16", seed=35, causal=False),
+    # Several runs of 8 query tiles per sequence (windowed and unmasked
+    # prefill split work that way), with partial last runs.
+    wl.PrefillWorkload("bf16_win200_runs", (1500, 1030), 4, 2, 128, 64, "bf16", seed=39, window_left=200),
+    wl.PrefillWorkload("bf16_noncausal_runs", (1100,), 2, 1, 128, 256, "bf16", seed=40, causal=False),
     wl.PrefillWorkload("f32_d64_p16", (128, 45), 2, 1, 64, 16, "f32", seed=36),
     wl.PrefillWorkload("f32_d128_win3", (70,), 2, 2, 128, 32, "f32", seed=37, window_left=3),
 ]
