@@ -27,7 +27,7 @@ from .attention import (
     decode_paged,
     append_pages,
 )
-from .quant import quantize_int8_pages, dequantize_int8_pages
+from .quant import quantize_int8_pages, dequantize_int8_pages, append_int8_pages
 from .counts import visible_pairs, attention_flops, kv_read_bytes, kv_bytes_per_token
 from .twins import brute_force_attention, online_softmax_attention, split_partials, merge_partials
 

@@ -36,6 +36,15 @@ QUANT_MUTANTS = [
 ]
 
 
+APPEND_MUTANTS = [
+    ("* scales[phys, hk]\n", "\n"),                                      # old codes not dequantised
+    ("amax = np.abs(vals).max()", "amax = np.abs(new).max() if new.size else np.float32(0)"),  # old rows out of absmax
+    ("n_old = max(0, min(s0, p0 + page_size) - p0)", "n_old = 0"),      # old rows ignored
+    ("first_row = r0 + (p0 + n_old - s0)", "first_row = r0 + max(0, p0 - s0 - 1)"),  # wrong input row
+    ("hi = min(end, p0 + page_size) - p0", "hi = min(end + 1, p0 + page_size) - p0"),  # one slot past the end
+]
+
+
 def _load_mutant(filename, old, new):
     src = open(os.path.join(ORACLE_DIR, filename)).read()
     assert src.count(old) >= 1, f"mutation anchor not found: {old}"
@@ -62,9 +71,17 @@ def _quant_battery():
     qpins.test_int8_half_way_rounds_to_even()
 
 
+def _append_battery():
+    qpins.test_int8_append_of_a_whole_page_is_the_page_quantiser()
+    qpins.test_int8_append_with_smaller_rows_keeps_scale_and_old_codes()
+    qpins.test_int8_append_error_bound_on_old_and_new_rows()
+    qpins.test_int8_append_matches_scalar_loop()
+
+
 def test_battery_passes_on_the_real_oracle():
     _attention_battery()
     _quant_battery()
+    _append_battery()
 
 
 @pytest.mark.parametrize("old,new", ATTENTION_MUTANTS)
@@ -82,3 +99,11 @@ def test_quant_mutant_is_caught(monkeypatch, old, new):
     monkeypatch.setattr(oracle, "quantize_int8_pages", mut.quantize_int8_pages)
     with pytest.raises((AssertionError, ValueError, IndexError)):
         _quant_battery()
+
+
+@pytest.mark.parametrize("old,new", APPEND_MUTANTS)
+def test_int8_append_mutant_is_caught(monkeypatch, old, new):
+    mut = _load_mutant("quant.py", old, new)
+    monkeypatch.setattr(oracle, "append_int8_pages", mut.append_int8_pages)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        _append_battery()

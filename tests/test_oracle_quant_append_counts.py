@@ -122,3 +122,96 @@ def test_counts_match_mask_and_workload_figures():
     assert oracle.visible_pairs(32768, 32768, True, 128) == 4_218_816
     assert oracle.kv_read_bytes([10, 300], 8, 128, 2) == 2 * 310 * 8 * 128 * 2
     assert oracle.kv_read_bytes([10, 300], 8, 128, 1, 4, 256) == 2 * 310 * 8 * 128 + 2 * 3 * 8 * 4
+
+
+def _rows_bf16(n, hkv, d, seed, mag=1.0):
+    return _bf16_values((n, hkv, d), seed) * np.float32(mag)
+
+
+def test_int8_append_of_a_whole_page_is_the_page_quantiser():
+    """P rows appended at a page boundary into a page holding garbage codes:
+    the page's codes and scales are those of the whole-page quantiser."""
+    P, hkv, d = 16, 2, 8
+    r = np.random.default_rng(5)
+    codes = r.integers(-128, 128, (3, P, hkv, d)).astype(np.int8)
+    scales = r.random((3, hkv)).astype(np.float32) + np.float32(0.5)
+    rows = _rows_bf16(P, hkv, d, 6, mag=3.0)
+    table = np.array([[2, 0]])
+    c2, s2 = oracle.append_int8_pages(codes, scales, rows, table, [0], [0, P], P)
+    qc, qs = oracle.quantize_int8_pages(rows[None])
+    assert np.array_equal(c2[2], qc[0]) and np.array_equal(s2[2], qs[0])
+    assert np.array_equal(c2[:2], codes[:2]) and np.array_equal(s2[:2], scales[:2])   # other pages untouched
+
+
+def test_int8_append_with_smaller_rows_keeps_scale_and_old_codes():
+    P, hkv, d = 16, 2, 8
+    codes = np.zeros((1, P, hkv, d), np.int8)
+    scales = np.ones((1, hkv), np.float32)
+    first = _rows_bf16(5, hkv, d, 7, mag=4.0)
+    c1, s1 = oracle.append_int8_pages(codes, scales, first, np.array([[0]]), [0], [0, 5], P)
+    small = _rows_bf16(6, hkv, d, 8, mag=0.01)
+    c2, s2 = oracle.append_int8_pages(c1, s1, small, np.array([[0]]), [5], [0, 6], P)
+    assert np.array_equal(s2, s1)
+    assert np.array_equal(c2[0, :5], c1[0, :5])
+    assert np.array_equal(c2[0, 11:], codes[0, 11:])      # slots past the end untouched
+
+
+def test_int8_append_error_bound_on_old_and_new_rows():
+    """After one append: new rows within half a step of the new scale, old
+    rows (requantised from their codes) within one step."""
+    P, hkv, d = 32, 3, 16
+    codes = np.zeros((2, P, hkv, d), np.int8)
+    scales = np.ones((2, hkv), np.float32)
+    x_old = _rows_bf16(40, hkv, d, 9, mag=1.0)
+    c1, s1 = oracle.append_int8_pages(codes, scales, x_old, np.array([[1, 0]]), [0], [0, 40], P)
+    x_new = _rows_bf16(17, hkv, d, 10, mag=2.5)          # larger: the second page's scale grows
+    c2, s2 = oracle.append_int8_pages(c1, s1, x_new, np.array([[1, 0]]), [40], [0, 17], P)
+    allx = np.concatenate([x_old, x_new]).astype(np.float64)
+    deq = oracle.dequantize_int8_pages(c2, s2)
+    for pos in range(57):
+        phys, slot = [1, 0][pos // P], pos % P
+        err = np.abs(deq[phys, slot] - allx[pos])
+        step = s2[phys].astype(np.float64)
+        bound = (0.5 if pos >= 40 else 1.0) * step * (1 + 1e-5)
+        assert (err <= bound[:, None]).all(), (pos, err.max(), step)
+    # the scale of a group is its largest valid magnitude over 127
+    assert abs(float(s2[0, 0]) * 127 - np.abs(np.concatenate([c1[0, :8, 0] * s1[0, 0], x_new[:, 0]])).max()) \
+        <= 1e-5 * float(s2[0, 0]) * 127
+
+
+def test_int8_append_matches_scalar_loop():
+    """Element by element in float32 scalars, on a tiny ragged case with two
+    sequences, a page crossing and a partly filled first page."""
+    P, hkv, d = 4, 2, 3
+    r = np.random.default_rng(11)
+    codes = r.integers(-127, 128, (5, P, hkv, d)).astype(np.int8)
+    scales = (r.random((5, hkv)) + 0.1).astype(np.float32)
+    table = np.array([[3, 1, 4], [0, 2, -1]])
+    start, cu = [2, 1], [0, 5, 7]
+    rows = _rows_bf16(7, hkv, d, 12, mag=2.0)
+    c2, s2 = oracle.append_int8_pages(codes, scales, rows, table, start, cu, P)
+    ec, es = codes.copy(), scales.copy()
+    for b in range(2):
+        n = cu[b + 1] - cu[b]
+        pages = sorted({(start[b] + i) // P for i in range(n)})
+        for lp in pages:
+            phys = table[b, lp]
+            for h in range(hkv):
+                vals = {}
+                for slot in range(P):
+                    pos = lp * P + slot
+                    if pos < start[b]:
+                        vals[slot] = [np.float32(np.float32(ec[phys, slot, h, k]) * es[phys, h]) for k in range(d)]
+                    elif pos < start[b] + n:
+                        vals[slot] = [np.float32(rows[cu[b] + pos - start[b], h, k]) for k in range(d)]
+                am = np.float32(0)
+                for v in vals.values():
+                    for e in v:
+                        am = max(am, np.float32(abs(e)))
+                sc = np.float32(am / np.float32(127)) if am != 0 else np.float32(1)
+                for slot, v in vals.items():
+                    for k, e in enumerate(v):
+                        y = min(max(np.float32(e / sc), np.float32(-128)), np.float32(127))
+                        ec[phys, slot, h, k] = int(round(float(y)))
+                es[phys, h] = sc
+    assert np.array_equal(c2, ec) and np.array_equal(s2, es)
