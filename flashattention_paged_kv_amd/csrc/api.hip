@@ -104,15 +104,33 @@ const char *pa_last_error_detail(void) { return g_detail; }
 pa_status kv_cache_append(const pa_kv_cache *cache, const void *k_new, const void *v_new,
                           const int32_t *block_table, int32_t max_pages_per_seq, const int32_t *start_pos,
                           const int32_t *cu_new, int32_t batch, int32_t max_new, void *stream) {
-  pa_status st = check_cache(cache, false);
+  pa_status st = check_cache(cache, true);
   if (st != PA_OK) return st;
-  if (cache->dtype == PA_I8)
-    return fail(PA_ERR_UNSUPPORTED, "append into an int8 cache is not supported; quantise whole pages instead");
   if (batch < 0 || max_new < 0) return fail(PA_ERR_INVALID_ARG, "batch and max_new must be >= 0");
   if (batch == 0 || max_new == 0) return ok();
   if (k_new == nullptr || v_new == nullptr || block_table == nullptr || start_pos == nullptr || cu_new == nullptr)
     return fail(PA_ERR_INVALID_ARG, "NULL pointer argument");
   if (max_pages_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq must be > 0");
+  if (cache->dtype == PA_I8) {
+    pa::AppendI8Args a;
+    a.k_codes = (int8_t *)cache->k_pages;
+    a.v_codes = (int8_t *)cache->v_pages;
+    a.k_scales = cache->k_scales;
+    a.v_scales = cache->v_scales;
+    a.k_new = (const uint16_t *)k_new;
+    a.v_new = (const uint16_t *)v_new;
+    a.block_table = block_table;
+    a.max_pages = max_pages_per_seq;
+    a.start_pos = start_pos;
+    a.cu_new = cu_new;
+    a.batch = batch;
+    a.max_new = max_new;
+    a.page_size = cache->page_size;
+    a.log2_page = log2_exact(cache->page_size);
+    a.num_kv_heads = cache->num_kv_heads;
+    a.head_dim = cache->head_dim;
+    return hip_status(pa::launch_append_i8(a, (hipStream_t)stream), "kv_cache_append launch");
+  }
   pa::AppendArgs a;
   a.k_pages = cache->k_pages;
   a.v_pages = cache->v_pages;

@@ -10,6 +10,11 @@
 //
 // The quantiser follows section 3.2 of "LLM推理系统优化：KV缓存管理与动态批处理
 // 技术" (group quantisation) with 8 bits and one group per (page, KV head).
+//
+// Appending into an int8 cache keeps that grouping for pages that are only
+// partly filled: every (page, KV head) group that receives rows is
+// requantised over its valid slots (those of positions before the
+// sequence's new end), the old slots entering as code * old scale.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -96,6 +101,75 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     }
     *reinterpret_cast<uint2 *>(a.codes + off) = make_uint2(packed[0], packed[1]);
   }
+}
+
+// One workgroup per (touched logical page j of sequence b, KV head hk), K
+// then V.  Pass 1: the largest magnitude over the group's valid slots (old
+// slots as code * old scale in float32, new slots from the bf16 rows).
+// Pass 2: scale = largest / 127 (1 if 0; IEEE division) and every valid
+// slot's code = round-half-even(clamp(value / scale)).  Slots past the
+// sequence's new end are not touched.
+__global__ __launch_bounds__(256) void append_i8_kernel(AppendI8Args a) {
+  const int j = blockIdx.x;
+  const int hk = blockIdx.y;
+  const int b = blockIdx.z;
+  const int r0 = a.cu_new[b];
+  const int n = a.cu_new[b + 1] - r0;
+  if (n <= 0) return;
+  const int P = a.page_size;
+  const int s0 = a.start_pos[b];
+  const int end = s0 + n;
+  const int lp = (s0 >> a.log2_page) + j;
+  const int p0 = lp * P;
+  if (p0 >= end) return;  // uniform
+  const int phys = a.block_table[(size_t)b * a.max_pages + lp];
+  const int n_old = max(0, min(s0, p0 + P) - p0);  // old valid slots [0, n_old)
+  const int hi = min(end, p0 + P) - p0;            // valid slots after the append: [0, hi)
+  const int first_row = r0 + (p0 + n_old - s0);    // input row of slot n_old
+  const int D = a.head_dim;
+  const int hkv = a.num_kv_heads;
+  const size_t slot_stride = (size_t)hkv * D;
+  const size_t gbase = ((size_t)phys * P * hkv + hk) * D;
+  const size_t sidx = (size_t)phys * hkv + hk;
+  __shared__ float red[256];
+
+  for (int which = 0; which < 2; ++which) {
+    int8_t *codes = which ? a.v_codes : a.k_codes;
+    float *scales = which ? a.v_scales : a.k_scales;
+    const uint16_t *src = which ? a.v_new : a.k_new;
+    const float s_old = scales[sidx];
+    auto value = [&](int e) {
+      const int slot = e / D, d = e - slot * D;
+      if (slot < n_old) return (float)codes[gbase + slot * slot_stride + d] * s_old;
+      return bf16_bits_to_f32(src[((size_t)(first_row + slot - n_old) * hkv + hk) * D + d]);
+    };
+    float amax = 0.f;
+    for (int e = threadIdx.x; e < hi * D; e += blockDim.x) amax = fmaxf(amax, fabsf(value(e)));
+    red[threadIdx.x] = amax;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+      if ((int)threadIdx.x < off) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + off]);
+      __syncthreads();
+    }
+    amax = red[0];
+    const float scale = (amax == 0.f) ? 1.f : amax / 127.f;  // IEEE division
+    for (int e = threadIdx.x; e < hi * D; e += blockDim.x) {
+      float y = value(e) / scale;                            // IEEE division
+      y = fminf(fmaxf(y, -128.f), 127.f);
+      const int slot = e / D, d = e - slot * D;
+      codes[gbase + slot * slot_stride + d] = (int8_t)(int)rintf(y);  // round half to even
+    }
+    __syncthreads();  // every read of the old scale and of red[] is done
+    if (threadIdx.x == 0) scales[sidx] = scale;
+  }
+}
+
+hipError_t launch_append_i8(const AppendI8Args &a, hipStream_t s) {
+  if (a.batch == 0 || a.max_new == 0) return hipSuccess;
+  // A sequence's new rows span at most max_new / P + 1 logical pages.
+  const dim3 grid((a.max_new + a.page_size - 1) / a.page_size + 1, a.num_kv_heads, a.batch);
+  hipLaunchKernelGGL(append_i8_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {

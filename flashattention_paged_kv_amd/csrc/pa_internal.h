@@ -38,6 +38,27 @@ struct AppendArgs {
   int row_bytes;  // num_kv_heads * head_dim * element size
 };
 
+// Append into an int8 cache: bf16 rows in, codes and scales requantised
+// per touched (page, KV head) group.
+struct AppendI8Args {
+  int8_t *k_codes;
+  int8_t *v_codes;
+  float *k_scales;
+  float *v_scales;
+  const uint16_t *k_new;  // bf16 bits [total_new, num_kv_heads, head_dim]
+  const uint16_t *v_new;
+  const int32_t *block_table;
+  int max_pages;
+  const int32_t *start_pos;
+  const int32_t *cu_new;
+  int batch;
+  int max_new;
+  int page_size;
+  int log2_page;
+  int num_kv_heads;
+  int head_dim;
+};
+
 struct QuantArgs {
   const uint16_t *src;
   int8_t *codes;
@@ -102,5 +123,6 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_append_i8(const AppendI8Args &a, hipStream_t s);
 
 }  // namespace pa

@@ -151,11 +151,13 @@ class KVCache:
 
 def kv_cache_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, block_table: torch.Tensor,
                     start_pos: torch.Tensor, cu_new: torch.Tensor, max_new: Optional[int] = None) -> None:
-    """Write rows of k_new / v_new [total_new, Hkv, D] into their page slots."""
+    """Write rows of k_new / v_new [total_new, Hkv, D] into their page slots
+    (bfloat16 rows for an int8 cache, which requantises the touched pages)."""
     lib = load_library()
     cs = cache._struct()
-    _dev(k_new, "k_new", cache.dtype)
-    _dev(v_new, "v_new", cache.dtype)
+    row_dtype = torch.bfloat16 if cache.dtype == torch.int8 else cache.dtype
+    _dev(k_new, "k_new", row_dtype)
+    _dev(v_new, "v_new", row_dtype)
     _dev(block_table, "block_table", torch.int32)
     _dev(start_pos, "start_pos", torch.int32)
     _dev(cu_new, "cu_new", torch.int32)

@@ -100,13 +100,23 @@ typedef struct pa_kv_cache {
  * the cache grows by appending the new tokens' K/V) through the page table
  * (section 3.2 of the Flash Attention + Paged KV Cache page).
  *   k_new, v_new : [cu_new[batch], num_kv_heads, head_dim], cache dtype
- *                  (PA_F32 or PA_BF16; PA_I8 caches return PA_ERR_UNSUPPORTED)
+ *                  (bfloat16 rows for a PA_I8 cache)
  *   block_table  : int32 [batch, max_pages_per_seq]; pages must already be
  *                  assigned for every written position
  *   start_pos    : int32 [batch], length of sequence b before this append
  *   cu_new       : int32 [batch + 1], prefix sums of new-token counts
  *   max_new      : host int, an upper bound on cu_new[b+1] - cu_new[b]
- * Row r of sequence b lands at position start_pos[b] + r.  A bit copy. */
+ * Row r of sequence b lands at position start_pos[b] + r.  A bit copy for
+ * PA_F32 / PA_BF16 caches.  For a PA_I8 cache (k_scales, v_scales needed)
+ * each (page, KV head) group that receives rows is requantised with the
+ * group quantiser of section 3.2 of the KV-cache management page over its
+ * valid slots (positions before the sequence's new end; old slots entering
+ * as code * old scale): scale = largest magnitude / 127 (1 if 0), code =
+ * round-half-even(clamp(value / scale, -128, 127)), in float32.  A whole
+ * page appended at once into an empty page gets exactly the codes of
+ * kv_pages_quantize_int8.  Pages shared with another sequence must not be
+ * appended to (the caller copies them first).  Errors: PA_ERR_INVALID_ARG
+ * for NULL pointers, negative sizes or an int8 cache without scales. */
 pa_status kv_cache_append(const pa_kv_cache *cache, const void *k_new, const void *v_new,
                           const int32_t *block_table, int32_t max_pages_per_seq,
                           const int32_t *start_pos, const int32_t *cu_new, int32_t batch,

@@ -128,8 +128,8 @@ def test_workspace_size_query():
 
 def test_append_rejects_bad_args():
     lib = ops.load_library()
-    c = _cache(dtype=ops.PA_I8)
-    assert lib.kv_cache_append(ctypes.byref(c), FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 1, None) == 2
+    c = _cache(dtype=ops.PA_I8)                       # int8 cache without scales
+    assert lib.kv_cache_append(ctypes.byref(c), FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 1, None) == 1
     c = _cache()
     assert lib.kv_cache_append(ctypes.byref(c), None, FAKE, FAKE, 4, FAKE, FAKE, 1, 1, None) == 1
     assert lib.kv_cache_append(ctypes.byref(c), FAKE, FAKE, FAKE, 4, FAKE, FAKE, -1, 1, None) == 1

@@ -233,3 +233,98 @@ def test_decode_other_grid_sizes_match_oracle(monkeypatch, wgs):
     (ref, _), _ = run.oracle()
     check_close(other, ref, "bf16", f"{wgs} workgroups")
     assert (other.double() - base.double()).abs().max().item() <= 2e-2
+
+
+def test_shared_prefix_pages_match_oracle():
+    """Two sequences whose block tables share the physical pages of a common
+    prefix (the refcounted prefix sharing of "Flash Attention与Paged KV Cache
+    优化大模型计算效率" section 3.2's page table, one page set read by two
+    logical sequences): the prefix is appended once, each sequence appends its
+    own suffix into private pages, and chunked prefill of the suffixes plus a
+    decode step of each sequence must match the oracle on the same tables."""
+    P, hq, hkv, d, seed = 16, 8, 2, 128, 60
+    n_pre, n_a, n_b = 160, 70, 45                      # prefix = 10 whole pages
+    pre_pages, a_pages, b_pages = n_pre // P, -(-n_a // P), -(-n_b // P)
+    n_pages = pre_pages + a_pages + b_pages + 2        # two spare pages
+    perm = wl.rng(seed, wl.STREAM_PERM).permutation(n_pages).astype(np.int32)
+    shared, own_a = perm[:pre_pages], perm[pre_pages:pre_pages + a_pages]
+    own_b = perm[pre_pages + a_pages:pre_pages + a_pages + b_pages]
+    width = pre_pages + max(a_pages, b_pages)
+    bt = np.full((2, width), -1, dtype=np.int32)
+    bt[0, :pre_pages + a_pages] = np.concatenate([shared, own_a])
+    bt[1, :pre_pages + b_pages] = np.concatenate([shared, own_b])
+    k_all = wl.normal((n_pre + n_a + n_b, hkv, d), "bf16", seed, wl.STREAM_K)
+    v_all = wl.normal((n_pre + n_a + n_b, hkv, d), "bf16", seed, wl.STREAM_V)
+    q = wl.normal((n_a + n_b, hq, d), "bf16", seed, wl.STREAM_Q)
+    q_dec = wl.normal((2, hq, d), "bf16", seed + 1, wl.STREAM_Q)
+    i32 = lambda x: torch.tensor(np.asarray(x, dtype=np.int32)).cuda()
+    say("shared prefix pages")
+    kp = nan_pool(n_pages, P, hkv, d, torch.bfloat16)
+    vp = nan_pool(n_pages, P, hkv, d, torch.bfloat16)
+    cache = ops.KVCache(kp, vp)
+    # prefix once (through sequence 0's table), then both suffixes
+    ops.kv_cache_append(cache, k_all[:n_pre].cuda(), v_all[:n_pre].cuda(), i32(bt[:1]), i32([0]), i32([0, n_pre]),
+                        max_new=n_pre)
+    shared_before = bits(kp[torch.from_numpy(shared).long().cuda()])
+    ops.kv_cache_append(cache, k_all[n_pre:].cuda(), v_all[n_pre:].cuda(), i32(bt), i32([n_pre, n_pre]),
+                        i32([0, n_a, n_a + n_b]), max_new=max(n_a, n_b))
+    assert np.array_equal(shared_before, bits(kp[torch.from_numpy(shared).long().cuda()]))
+    ctx = [n_pre + n_a, n_pre + n_b]
+    out = ops.attn_prefill_paged(q.cuda(), i32([0, n_a, n_a + n_b]), cache, i32(bt), i32(ctx), max_q_len=n_a)
+    dec = ops.attn_decode_paged(q_dec.cuda(), cache, i32(bt), i32(ctx))
+    torch.cuda.synchronize()
+    # the oracle replays the same appends on NaN pools
+    shape = (n_pages, P, hkv, d)
+    okp, ovp = oracle.append_pages(np.full(shape, np.nan), np.full(shape, np.nan), f64(k_all[:n_pre]),
+                                   f64(v_all[:n_pre]), bt[:1], [0], [0, n_pre], P)
+    okp, ovp = oracle.append_pages(okp, ovp, f64(k_all[n_pre:]), f64(v_all[n_pre:]), bt, [n_pre, n_pre],
+                                   [0, n_a, n_a + n_b], P)
+    ref, _ = oracle.attention_paged(f64(q), [0, n_a, n_a + n_b], okp, ovp, bt, ctx, P)
+    check_close(out, ref, "bf16", "prefill of both suffixes")
+    ref_dec, _ = oracle.decode_paged(f64(q_dec), okp, ovp, bt, ctx, P)
+    check_close(dec, ref_dec, "bf16", "decode of both sequences")
+
+
+def test_int8_append_is_bit_exact_then_decodes():
+    """Appends into an int8 cache requantise each touched (page, KV head)
+    group over its valid slots; codes and scales must equal the oracle's bit
+    for bit after several ragged rounds (starting mid-page, crossing pages),
+    and decode over the result must match the oracle's dequantised cache."""
+    P, hq, hkv, d, seed = 16, 8, 2, 128, 61
+    start0 = [0, 37, 16, 5]                       # lengths before the first append
+    rounds = [[5, 20, 1, 11], [1, 1, 1, 0], [40, 3, 0, 12]]
+    final = [s + sum(r[b] for r in rounds) for b, s in enumerate(start0)]
+    pages = [-(-n // P) for n in final]
+    n_pages = sum(pages) + 2
+    perm = wl.rng(seed, wl.STREAM_PERM).permutation(n_pages).astype(np.int32)
+    bt = np.full((4, max(pages)), -1, dtype=np.int32)
+    at = 0
+    for b, n in enumerate(pages):
+        bt[b, :n] = perm[at:at + n]
+        at += n
+    say("int8 append")
+    pool_k = wl.normal((n_pages, P, hkv, d), "bf16", seed, wl.STREAM_K)
+    pool_v = wl.normal((n_pages, P, hkv, d), "bf16", seed, wl.STREAM_V)
+    kc, ks = ops.kv_pages_quantize_int8(pool_k.cuda())
+    vc, vs = ops.kv_pages_quantize_int8(pool_v.cuda())
+    cache = ops.KVCache(kc, vc, ks, vs)
+    ok, oks = oracle.quantize_int8_pages(f64(pool_k))
+    ov, ovs = oracle.quantize_int8_pages(f64(pool_v))
+    i32 = lambda x: torch.tensor(np.asarray(x, dtype=np.int32)).cuda()
+    starts = list(start0)
+    for i, n_new in enumerate(rounds):
+        cu = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
+        k_new = wl.normal((int(cu[-1]), hkv, d), "bf16", seed + 10 + i, wl.STREAM_KNEW)
+        v_new = wl.normal((int(cu[-1]), hkv, d), "bf16", seed + 10 + i, wl.STREAM_VNEW)
+        ops.kv_cache_append(cache, k_new.cuda(), v_new.cuda(), i32(bt), i32(starts), i32(cu), max_new=max(n_new))
+        ok, oks = oracle.append_int8_pages(ok, oks, f64(k_new), bt, starts, cu, P)
+        ov, ovs = oracle.append_int8_pages(ov, ovs, f64(v_new), bt, starts, cu, P)
+        starts = [s + n for s, n in zip(starts, n_new)]
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), ok) and np.array_equal(vc.cpu().numpy(), ov)
+    assert np.array_equal(ks.cpu().numpy(), oks) and np.array_equal(vs.cpu().numpy(), ovs)
+    q = wl.normal((4, hq, d), "bf16", seed, wl.STREAM_Q)
+    out = ops.attn_decode_paged(q.cuda(), cache, i32(bt), i32(final))
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode_paged(f64(q), ok, ov, bt, final, P, k_scales=oks, v_scales=ovs)
+    check_close(out, ref, "bf16", "decode after int8 appends")
