@@ -17,14 +17,17 @@
 // (sequence, query head): their key-tile counts add up to the same total for
 // every p, so all workgroups carry equal work.  With a window or without a
 // mask every query tile has about the same work, and a workgroup takes a run
-// of 8 consecutive query tiles instead (fewer, longer workgroups).  The workgroup is two engines of 4 waves that
-// each take half of the pair's key tiles: engine 0 all of the earlier tile
-// and the top of the later one, engine 1 the bottom of the later one, both
-// ascending, so that the two engines read the same key tile at the same
-// step while both are in the shared prefix.  The query tile split between
-// them is merged in LDS at the end with the same rescaling algebra as the
-// online softmax.  Each engine has its own double-buffered K/V tiles in LDS
-// and loads the next key tile into registers a whole step ahead.  Workgroup
+// of 8 consecutive query tiles instead (fewer, longer workgroups).  The
+// workgroup is two engines of 4 waves that each take half of the pair's key
+// tiles: engine 0 all of the earlier tile and the top of the later one,
+// engine 1 the bottom of the later one, both ascending, so that the two
+// engines read the same key tile at the same step while both are in the
+// shared prefix.  The query tile split between them is merged in LDS at the
+// end with the same rescaling algebra as the online softmax, each engine
+// merging and storing half of the head dimensions.  Each engine has its own
+// double-buffered K/V tiles in LDS and loads the next key tile into
+// registers a whole step ahead; its first query tile's Q arrives with its
+// first K/V tile, staged in the free LDS buffer.  Workgroup
 // ids are remapped so that the pairs of one query head run on the same XCD
 // (shared L2) and stream its K/V tiles together.
 //
@@ -43,6 +46,8 @@
 // maximum by at most that much: probabilities stay <= 256, and O and l share
 // the reference, so the result is the same attention).
 #include <math.h>
+
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -68,9 +73,6 @@ struct PfCfg {
   static constexpr int kVBuf = kPfKeys * kVRow;
   static constexpr int kEngine = 2 * (kKBuf + kVBuf);                   // two K/V buffers
   static constexpr int kLoads = kPfKeys * kCpr / kPfEngineThreads;      // per thread per tile, K and V each
-  // Final merge: a lane's O^T values, then its (m, l).
-  static constexpr int kMergeLane = 16 * kNdb + 4;
-  static_assert(4 * 64 * kMergeLane * 4 <= kEngine, "merge area must fit one engine's buffers");
 };
 
 // BIG_PAGE: page_size >= 64, so each 64-key tile lies in one page.
@@ -322,26 +324,43 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
   };
   // Normalise and store this wave's rows of query tile qt.
-  auto finish = [&](int qt, float m_row, float l_half, const f32x16 *acc) __attribute__((always_inline)) {
+  // Normalise and store 32-dim blocks [db0, db1) of this wave's rows of
+  // query tile qt.  Lanes l and l + 32 hold the two 4-dim halves of each
+  // 8-dim group; a permlane32 swap gives each lane one whole group, so every
+  // store writes 16 contiguous bytes.
+  auto finish_part = [&](int qt, float m_row, float l_half, const f32x16 *acc, auto DB0, auto DB1, bool with_lse)
+      __attribute__((always_inline)) {
+    constexpr int db0 = decltype(DB0)::value, db1 = decltype(DB1)::value;
     const int qrow = qt * kPfRows + w * 32 + col;
     const float ltot = l_half + __shfl_xor(l_half, 32, 64);
-    if (qrow < q_len) {
-      const float inv = 1.f / ltot;
-      uint16_t *orow = (uint16_t *)a.out + ((size_t)(q0 + qrow) * a.num_q_heads + h) * D;
+    const float inv = 1.f / ltot;
+    uint16_t *orow = (uint16_t *)a.out + ((size_t)(q0 + min(qrow, q_len - 1)) * a.num_q_heads + h) * D;
 #pragma unroll
-      for (int db = 0; db < C::kNdb; ++db)
+    for (int db = 0; db < C::kNdb; ++db) {
+      if (db < db0 || db >= db1) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t lo = pack_bf16x2(acc[db][4 * j] * inv, acc[db][4 * j + 1] * inv);
-          const uint32_t hi = pack_bf16x2(acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv);
-          *reinterpret_cast<uint2 *>(orow + db * 32 + j * 8 + g * 4) = make_uint2(lo, hi);
+      for (int jp = 0; jp < 4; jp += 2) {
+        uint32_t x[2], y[2];
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf) {
+          const int ia = 4 * jp + 2 * hlf, ib = 4 * (jp + 1) + 2 * hlf;
+          const uint32_t va = pack_bf16x2(acc[db][ia] * inv, acc[db][ia + 1] * inv);
+          const uint32_t vb = pack_bf16x2(acc[db][ib] * inv, acc[db][ib + 1] * inv);
+          const auto r = __builtin_amdgcn_permlane32_swap(va, vb, false, false);
+          x[hlf] = r[0];
+          y[hlf] = r[1];
         }
-      if (a.lse != nullptr && g == 0)
-        a.lse[(size_t)(q0 + qrow) * a.num_q_heads + h] = (m_row + __log2f(ltot)) * kLn2;
+        if (qrow < q_len)
+          *reinterpret_cast<uint4 *>(orow + db * 32 + (jp + g) * 8) = make_uint4(x[0], x[1], y[0], y[1]);
+      }
     }
+    if (with_lse && a.lse != nullptr && g == 0 && qrow < q_len)
+      a.lse[(size_t)(q0 + qrow) * a.num_q_heads + h] = (m_row + __log2f(ltot)) * kLn2;
+  };
+  auto finish = [&](int qt, float m_row, float l_half, const f32x16 *acc) __attribute__((always_inline)) {
+    finish_part(qt, m_row, l_half, acc, std::integral_constant<int, 0>{}, std::integral_constant<int, C::kNdb>{}, true);
   };
 
-  // S^T = K . Q^T for the two 32-key blocks of the tile in LDS buffer `buf`.
   // S^T = K . Q^T for the two 32-key blocks of the tile in LDS buffer `buf`.
   // The K fragments are read kAhead MFMAs ahead of their use (a ring of
   // registers), so the LDS latency hides behind the MFMAs before them.
@@ -464,13 +483,27 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // latency.  By then the buffer's previous tile t-2 has been read (its K by
   // G(t-2), its V by G(t-1)), and the next reads, G(t) for K and G(t+1) for
   // V, come after the next barrier.
+  // The first query tile's Q is loaded with the first K/V tile (both
+  // latencies overlap) and staged in LDS buffer 1, free until S(0) stores
+  // tile 1 there; G(0) reads Q^T from it.
+  constexpr int kQLoads = kPfRows * C::kCpr / kPfEngineThreads;
+  static_assert(kPfRows * C::kKRow <= C::kKBuf + C::kVBuf, "Q tile must fit one K/V buffer");
   if (n_mine > 0) {
     int qt, kt;
     my_item(0, qt, kt);
     load_half(kt, kbase, pk);
     load_half(kt, vbase, pv);
+    u32x4 qs[kQLoads];
+#pragma unroll
+    for (int i = 0; i < kQLoads; ++i) {
+      const int row = min(qt * kPfRows + lrow + i * kRowsPerPass, q_len - 1);
+      qs[i] = *reinterpret_cast<const u32x4 *>((const char *)a.q + ((size_t)(q0 + row) * a.num_q_heads + h) * D * 2 + lch * 16);
+    }
     store_k(0, pk);
     store_v(0, pv);
+#pragma unroll
+    for (int i = 0; i < kQLoads; ++i)
+      *reinterpret_cast<u32x4 *>(kbuf(1) + (lrow + i * kRowsPerPass) * C::kKRow + lch * 16) = qs[i];
   }
   __syncthreads();
   // Wave priorities: the GEMM wave's MFMAs are the critical path of each
@@ -489,7 +522,13 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       int qt, kt;
       my_item(t, qt, kt);
       if (qt != qt_q) {
-        load_q(qt);
+        if (t == 0) {
+#pragma unroll
+          for (int s = 0; s < C::kNs; ++s)
+            bq[s] = *reinterpret_cast<const bf16x8 *>(kbuf(1) + (w * 32 + col) * C::kKRow + (16 * s + 8 * g) * 2);
+        } else {
+          load_q(qt);
+        }
         qt_q = qt;
       }
       qk_mfma(t & 1);
@@ -540,39 +579,59 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
 
   // The query tile split between the engines (qb in the first case, qa in
   // the second; none if the split falls on the boundary, half == na) has a
-  // partial result in each engine: engine 0 hands its (m, l, O) to engine 1
-  // through LDS (the K/V buffers are free now) and engine 1 merges.
+  // partial result in each engine.  Each engine finishes half of its 32-dim
+  // blocks (engine 0 the first half, engine 1 the second): it hands the
+  // other half of its (O, m, l) to the other engine through LDS (the K/V
+  // buffers are free now) and merges the half it receives.
   if (!shared) {
     if (qt_cur >= 0) finish(qt_cur, m, lsum, o);
     return;
   }
-  float *mrg = reinterpret_cast<float *>(smem) + (size_t)(w * 64 + lane) * C::kMergeLane;
-  if (eng == 0) {
+  constexpr int kHalfDb = C::kNdb / 2;
+  constexpr int kMrgLane = 16 * kHalfDb + 4;
+  static_assert(2 * 4 * 64 * kMrgLane * 4 <= 2 * C::kEngine, "merge area must fit the K/V buffers");
+  float *mine_out = reinterpret_cast<float *>(smem) + (size_t)((eng * 4 + w) * 64 + lane) * kMrgLane;
+  const float *other_in = reinterpret_cast<const float *>(smem) + (size_t)(((1 - eng) * 4 + w) * 64 + lane) * kMrgLane;
+  auto merge = [&](auto E) __attribute__((always_inline)) {
+    constexpr int e = decltype(E)::value;
+    constexpr int give0 = e == 0 ? kHalfDb : 0;  // first block handed over
+    constexpr int keep0 = e == 0 ? 0 : kHalfDb;  // first block finished here
 #pragma unroll
-    for (int db = 0; db < C::kNdb; ++db)
+    for (int d = 0; d < kHalfDb; ++d)
 #pragma unroll
       for (int i = 0; i < 16; i += 4)
-        *reinterpret_cast<f32x4 *>(mrg + 16 * db + i) = f32x4{o[db][i], o[db][i + 1], o[db][i + 2], o[db][i + 3]};
-    mrg[16 * C::kNdb] = m;
-    mrg[16 * C::kNdb + 1] = lsum;
-  }
-  __syncthreads();
-  if (eng == 1) {
-    const float m0 = mrg[16 * C::kNdb];
-    const float l0 = mrg[16 * C::kNdb + 1];
-    const float mm = fmaxf(m0, m);
+        *reinterpret_cast<f32x4 *>(mine_out + 16 * d + i) =
+            f32x4{o[give0 + d][i], o[give0 + d][i + 1], o[give0 + d][i + 2], o[give0 + d][i + 3]};
+    mine_out[16 * kHalfDb] = m;
+    mine_out[16 * kHalfDb + 1] = lsum;
+    __syncthreads();
+    const float m_other = other_in[16 * kHalfDb];
+    const float l_other = other_in[16 * kHalfDb + 1];
+    // (m0, l0) of engine 0, (m1, l1) of engine 1.
+    const float m0 = e == 0 ? m : m_other, m1 = e == 0 ? m_other : m;
+    const float l0 = e == 0 ? lsum : l_other, l1 = e == 0 ? l_other : lsum;
+    const float mm = fmaxf(m0, m1);
     const float f0 = m0 == -INFINITY ? 0.f : fast_exp2(m0 - mm);
-    const float f1 = m == -INFINITY ? 0.f : fast_exp2(m - mm);
+    const float f1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
 #pragma unroll
-    for (int db = 0; db < C::kNdb; ++db)
+    for (int d = 0; d < kHalfDb; ++d)
 #pragma unroll
       for (int i = 0; i < 16; i += 4) {
-        const f32x4 v0 = *reinterpret_cast<const f32x4 *>(mrg + 16 * db + i);
+        const f32x4 vo = *reinterpret_cast<const f32x4 *>(other_in + 16 * d + i);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[db][i + e] = o[db][i + e] * f1 + v0[e] * f0;
+        for (int j = 0; j < 4; ++j) {
+          const float v0 = e == 0 ? o[keep0 + d][i + j] : vo[j];
+          const float v1 = e == 0 ? vo[j] : o[keep0 + d][i + j];
+          o[keep0 + d][i + j] = v1 * f1 + v0 * f0;
+        }
       }
-    finish(qt_cur, mm, lsum * f1 + l0 * f0, o);
-  }
+    finish_part(qt_cur, mm, l1 * f1 + l0 * f0, o, std::integral_constant<int, keep0>{},
+                std::integral_constant<int, keep0 + kHalfDb>{}, e == 1);
+  };
+  if (eng == 0)
+    merge(std::integral_constant<int, 0>{});
+  else
+    merge(std::integral_constant<int, 1>{});
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
