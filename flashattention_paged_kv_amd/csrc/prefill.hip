@@ -302,18 +302,13 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   f32x16 sacc[2];       // S^T of a tile between its GEMM and softmax phases
   bf16x8 bp[4];         // P^T of a tile between its softmax phase and the next GEMM phase
 
-  auto load_q = [&](int qt) __attribute__((always_inline)) {
+  // Q^T of query tile qt into bq (waited for where it is first used).
+  auto load_q_async = [&](int qt) __attribute__((always_inline)) {
     const int qrow = qt * kPfRows + w * 32 + col;
     const __bf16 *qp = (const __bf16 *)a.q + ((size_t)(q0 + min(qrow, q_len - 1)) * a.num_q_heads + h) * D;
 #pragma unroll
     for (int s = 0; s < C::kNs; ++s)
       bq[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp + 16 * s + 8 * g));
-    // Complete the Q loads on this (rare) path: otherwise the wait counters
-    // merged where the paths join treat Q as possibly in flight, and the QK
-    // MFMAs of every tile wait for all loads issued before them, including
-    // the prefetch of the next K/V tile.
-#pragma unroll
-    for (int s = 0; s < C::kNs; ++s) __asm__ volatile("" : "+v"(bq[s]));
   };
   auto reset_o = [&]() __attribute__((always_inline)) {
     m = -INFINITY;
@@ -511,9 +506,12 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // softmax on the same SIMD.
   auto gemm_phase = [&](int t) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(2);
-    if (t + 1 < n_mine) {
+    // Inside the loop the next tile's loads are unconditional (the last step
+    // re-reads its own tile, never stored): the same loads are in flight on
+    // every path, so the wait counts stay exact.
+    if (t < n_mine) {
       int qt, kt;
-      my_item(t + 1, qt, kt);
+      my_item(min(t + 1, n_mine - 1), qt, kt);
       load_half(kt, kbase, pk);
       load_half(kt, vbase, pv);
     }
@@ -521,17 +519,24 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     if (t < n_mine) {
       int qt, kt;
       my_item(t, qt, kt);
-      if (qt != qt_q) {
-        if (t == 0) {
+      if (t == 0) {
 #pragma unroll
-          for (int s = 0; s < C::kNs; ++s)
-            bq[s] = *reinterpret_cast<const bf16x8 *>(kbuf(1) + (w * 32 + col) * C::kKRow + (16 * s + 8 * g) * 2);
-        } else {
-          load_q(qt);
-        }
+        for (int s = 0; s < C::kNs; ++s)
+          bq[s] = *reinterpret_cast<const bf16x8 *>(kbuf(1) + (w * 32 + col) * C::kKRow + (16 * s + 8 * g) * 2);
         qt_q = qt;
       }
       qk_mfma(t & 1);
+      // The next item's Q, if it starts a new query tile, is loaded as soon
+      // as this tile's QK product is issued: it arrives during the softmax
+      // phase, whose K/V stores wait for all loads anyway.
+      if (t + 1 < n_mine) {
+        int qn, kn;
+        my_item(t + 1, qn, kn);
+        if (qn != qt_q) {
+          load_q_async(qn);
+          qt_q = qn;
+        }
+      }
     }
   };
   auto softmax_phase = [&](int t) __attribute__((always_inline)) {
