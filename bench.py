@@ -111,12 +111,19 @@ def bench_prefill(w: wl.PrefillWorkload, steps: int, warmup: int) -> dict:
     pairs = sum(causal_pairs(n, w.window_left) for n in w.seq_lens)
     flops = 4 * w.head_dim * w.num_q_heads * pairs
     kv_bytes = 2 * sum(w.seq_lens) * w.num_kv_heads * w.head_dim * 2
+    # Algorithmic HBM bytes: Q and O once per query row, K and V once per key.
+    io_bytes = 2 * sum(w.seq_lens) * w.num_q_heads * w.head_dim * 2 + kv_bytes
     achieved = flops / (ms_kernel * 1e-3) / 1e12
+    if flops / io_bytes >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4))
+    else:  # below the ridge point (a short window): bytes bound it
+        gbs = io_bytes / (ms_kernel * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4))
+    roof["traffic"] = _traffic("prefill_bf16_kernel", w.name)
     return dict(workload=w.name, ms_per_step=ms_step, ms_prefill_kernel=ms_kernel, flops=flops,
                 tflops_step=flops / (ms_step * 1e-3) / 1e12, tflops_kernel=achieved, kv_bytes=kv_bytes,
-                roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                              frac=round(achieved / PEAK_BF16_TFLOPS, 4),
-                              traffic=_traffic("prefill_bf16_kernel", w.name)))
+                io_bytes=io_bytes, roofline=roof)
 
 
 def bench_decode(w: wl.DecodeWorkload, steps: int, warmup: int) -> dict:
