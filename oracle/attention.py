@@ -175,6 +175,58 @@ def decode_paged(q, k_pool, v_pool, block_table, ctx_lens, page_size: int,
                            k_scales=k_scales, v_scales=v_scales)
 
 
+def _cached_values(pool, scales, block_row, n_tokens: int, page_size: int) -> np.ndarray:
+    """float64 [n_tokens, Hkv, D] of one sequence's first n_tokens cached
+    positions; int8 codes are read back as code * scale of their (physical
+    page, KV head) group ([SYS] §3.2)."""
+    x = gather_sequence(pool, block_row, n_tokens, page_size)
+    if scales is None:
+        return _f64(x)
+    phys = np.asarray(block_row)[np.arange(n_tokens) // page_size]
+    return _f64(x) * _f64(np.asarray(scales))[phys][:, :, None]
+
+
+def decode_layered(q, hi: dict, lo: dict, softmax_scale: float | None = None):
+    """Single-token decode over a context held in two caches: the layered
+    cache of [KVFA] §2.2 (the first tokens of a sequence kept at full
+    precision, later ones int8 with group scales, [SYS] §3.2).
+
+    q [B, Hq, D].  ``hi`` and ``lo`` are dicts with the pools ``k``, ``v``
+    [N, P, Hkv, D], ``block_table`` [B, max_pages], ``lens`` [B],
+    ``page_size`` and, for int8 pools, ``k_scales`` / ``v_scales`` [N, Hkv].
+    Sequence b's keys are its lens_hi[b] positions in ``hi`` followed by its
+    lens_lo[b] positions in ``lo``; its one query attends to all of them (no
+    mask: the query is the last position).  Returns (out [B, Hq, D],
+    lse [B, Hq]); a sequence without keys gets out = 0, lse = -inf.
+    """
+    q = _f64(q)
+    nb, hq, d = q.shape
+    hkv = np.asarray(hi["k"]).shape[2]
+    group = hq // hkv
+    scale = (1.0 / np.sqrt(d)) if softmax_scale is None else float(softmax_scale)
+    out = np.zeros((nb, hq, d))
+    lse = np.full((nb, hq), -np.inf)
+    for b in range(nb):
+        n_hi = int(np.asarray(hi["lens"])[b])
+        n_lo = int(np.asarray(lo["lens"])[b])
+        parts_k, parts_v = [], []
+        for part, n in ((hi, n_hi), (lo, n_lo)):
+            row = np.asarray(part["block_table"])[b]
+            parts_k.append(_cached_values(part["k"], part.get("k_scales"), row, n, part["page_size"]))
+            parts_v.append(_cached_values(part["v"], part.get("v_scales"), row, n, part["page_size"]))
+        keys = np.concatenate(parts_k, axis=0)
+        values = np.concatenate(parts_v, axis=0)
+        if keys.shape[0] == 0:
+            continue
+        vis = np.ones((1, keys.shape[0]), dtype=bool)
+        for h in range(hq):
+            g = h // group
+            o, l = _attend_rows(q[b:b + 1, h, :], keys[:, g, :], values[:, g, :], scale, vis)
+            out[b, h] = o[0]
+            lse[b, h] = l[0]
+    return out, lse
+
+
 def append_pages(k_pool, v_pool, k_new, v_new, block_table, start_pos, cu_new, page_size: int):
     """Write new K/V rows into their page slots ([KV3X] "KV Cache 的工作原理":
     the cache grows by appending; [FAPKV] §3.2: the slot is found through the

@@ -8,6 +8,7 @@ import types
 import pytest
 
 import oracle
+import test_oracle_layered as lpins
 import test_oracle_pins as pins
 import test_oracle_quant_append_counts as qpins
 
@@ -45,6 +46,15 @@ APPEND_MUTANTS = [
 ]
 
 
+LAYERED_MUTANTS = [
+    ("for part, n in ((hi, n_hi), (lo, n_lo)):", "for part, n in ((hi, n_hi), (lo, max(0, n_lo - 1))):"),  # last int8 key dropped
+    ('part.get("v_scales"), row', 'part.get("k_scales"), row'),          # V read back with K's scales
+    ("keys = np.concatenate(parts_k, axis=0)", "keys = np.concatenate(parts_k[::-1], axis=0)"),  # K/V paired across parts
+    ('row = np.asarray(part["block_table"])[b]', 'row = np.asarray(hi["block_table"])[b]'),  # second part through the first's table
+    ("phys = np.asarray(block_row)[np.arange(n_tokens) // page_size]", "phys = np.arange(n_tokens) // page_size"),  # scale of the logical page
+]
+
+
 def _load_mutant(filename, old, new):
     src = open(os.path.join(ORACLE_DIR, filename)).read()
     assert src.count(old) >= 1, f"mutation anchor not found: {old}"
@@ -78,10 +88,18 @@ def _append_battery():
     qpins.test_int8_append_matches_scalar_loop()
 
 
+def _layered_battery():
+    lpins.test_layered_split_equals_whole_cache()
+    lpins.test_layered_with_an_empty_part_is_the_plain_decode()
+    lpins.test_layered_int8_part_matches_brute_force()
+    lpins.test_layered_sequence_without_keys()
+
+
 def test_battery_passes_on_the_real_oracle():
     _attention_battery()
     _quant_battery()
     _append_battery()
+    _layered_battery()
 
 
 @pytest.mark.parametrize("old,new", ATTENTION_MUTANTS)
@@ -107,3 +125,11 @@ def test_int8_append_mutant_is_caught(monkeypatch, old, new):
     monkeypatch.setattr(oracle, "append_int8_pages", mut.append_int8_pages)
     with pytest.raises((AssertionError, ValueError, IndexError)):
         _append_battery()
+
+
+@pytest.mark.parametrize("old,new", LAYERED_MUTANTS)
+def test_layered_mutant_is_caught(monkeypatch, old, new):
+    mut = _load_mutant("attention.py", old, new)
+    monkeypatch.setattr(oracle, "decode_layered", mut.decode_layered)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        _layered_battery()
