@@ -173,6 +173,41 @@ def bench_decode(w: wl.DecodeWorkload, steps: int, warmup: int) -> dict:
                               traffic=_traffic("decode_split_kernel", w.name)))
 
 
+def bench_layered(w: wl.DecodeWorkload, steps: int, warmup: int) -> dict:
+    """Decode over a layered cache: the first w.full_tokens positions of each
+    sequence in a bf16 cache, the rest in an int8 cache (quantised pages)."""
+    dev = torch.device("cuda")
+    inp = wl.decode_inputs(w)
+    full = wl.layered_full_inputs(w)
+    q = inp["q"].to(dev)
+    kc, ks = ops.kv_pages_quantize_int8(inp["k_pool"].to(dev))
+    vc, vs = ops.kv_pages_quantize_int8(inp["v_pool"].to(dev))
+    lo = ops.KVCache(kc, vc, ks, vs)
+    hi = ops.KVCache(full["k_pool"].to(dev), full["v_pool"].to(dev))
+    ctx_np = inp["ctx_lens"].numpy().astype(np.int64)
+    len_hi = full["lens"].numpy().astype(np.int64)
+    len_lo = ctx_np - len_hi
+    bt_hi, bt_lo = full["block_table"].to(dev), inp["block_table"].to(dev)
+    lh, ll = full["lens"].to(dev), torch.from_numpy(len_lo.astype(np.int32)).to(dev)
+    ws = torch.empty(ops.decode_layered_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+
+    def decode():
+        ops.attn_decode_paged_layered(q, hi, bt_hi, lh, lo, bt_lo, ll, softmax_scale=w.softmax_scale, out=out,
+                                      workspace=ws)
+
+    ms = _time_loop(decode, steps, warmup)
+    row = w.num_kv_heads * w.head_dim
+    kv_bytes = int(2 * len_hi.sum() * row * 2 + 2 * len_lo.sum() * row
+                   + 2 * sum(-(-int(c) // w.page_size) for c in len_lo) * w.num_kv_heads * 4)
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    return dict(workload=w.name, ms_decode_kernels=ms, kv_bytes=kv_bytes, gbs_kernel=gbs,
+                sum_ctx=int(ctx_np.sum()), full_tokens=w.full_tokens,
+                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                              frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+
+
 def cpu_baseline(w: wl.PrefillWorkload, budget_s: float = 15.0) -> dict:
     """The CPU oracle (float64 numpy) on a bounded sample of the prefill
     workload: the whole prompt's append, then as many heads of the causal
@@ -238,8 +273,12 @@ def main() -> int:
 
     if args.workload:
         w = wl.WORKLOADS[args.workload]
-        r = bench_prefill(w, args.steps, args.warmup) if isinstance(w, wl.PrefillWorkload) \
-            else bench_decode(w, args.steps, args.warmup)
+        if isinstance(w, wl.PrefillWorkload):
+            r = bench_prefill(w, args.steps, args.warmup)
+        elif w.full_tokens:
+            r = bench_layered(w, args.steps, args.warmup)
+        else:
+            r = bench_decode(w, args.steps, args.warmup)
         print(json.dumps(r), flush=True)
         return 0
 

@@ -82,6 +82,37 @@ size_t decode_ws_bytes(int batch, int hq, int hkv, int d, int nwg) {
   return heads * g * ((size_t)d + 2) * sizeof(float) + ((size_t)batch + 1) * sizeof(int32_t);
 }
 
+size_t round_up_256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Split/merge arguments of one decode over `cache`, with its workspace at
+// `workspace` (decode_ws_bytes(...) bytes).
+pa::DecodeArgs decode_args(const void *q, const pa_kv_cache *cache, const int32_t *block_table, int32_t max_pages,
+                           const int32_t *ctx_lens, int32_t batch, int32_t num_q_heads, float softmax_scale,
+                           int32_t window_left, void *out, float *lse, void *workspace, int nwg) {
+  pa::DecodeArgs a;
+  const int group = num_q_heads / cache->num_kv_heads;
+  a.q = q;
+  a.c = view_of(cache);
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.ctx_lens = ctx_lens;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.group = group;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.window_left = window_left < 0 ? -1 : window_left;
+  a.out = out;
+  a.lse = lse;
+  const int hpw = pa::decode_heads_per_wg(cache->num_kv_heads);
+  const size_t slots_g = ((size_t)batch * cache->num_kv_heads + (size_t)nwg * hpw) * group;
+  a.ws_o = (float *)workspace;
+  a.ws_ml = a.ws_o + slots_g * cache->head_dim;
+  a.ws_prefix = (int32_t *)(a.ws_ml + slots_g * 2);
+  a.nwg = nwg;
+  a.hpw = hpw;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,27 +288,55 @@ pa_status attn_decode_paged(const void *q, const pa_kv_cache *cache, const int32
   const size_t need = decode_ws_bytes(batch, num_q_heads, cache->num_kv_heads, cache->head_dim, nwg);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(PA_ERR_WORKSPACE, "decode needs %zu workspace bytes (got %zu)", need, workspace_bytes);
-  pa::DecodeArgs a;
-  a.q = q;
-  a.c = view_of(cache);
-  a.block_table = block_table;
-  a.max_pages = max_pages_per_seq;
-  a.ctx_lens = ctx_lens;
-  a.batch = batch;
-  a.num_q_heads = num_q_heads;
-  a.group = group;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  a.window_left = window_left < 0 ? -1 : window_left;
-  a.out = out;
-  a.lse = lse;
-  const int hpw = pa::decode_heads_per_wg(cache->num_kv_heads);
-  const size_t slots_g = ((size_t)batch * cache->num_kv_heads + (size_t)nwg * hpw) * group;
-  a.ws_o = (float *)workspace;
-  a.ws_ml = a.ws_o + slots_g * cache->head_dim;
-  a.ws_prefix = (int32_t *)(a.ws_ml + slots_g * 2);
-  a.nwg = nwg;
-  a.hpw = hpw;
+  const pa::DecodeArgs a = decode_args(q, cache, block_table, max_pages_per_seq, ctx_lens, batch, num_q_heads,
+                                       softmax_scale, window_left, out, lse, workspace, nwg);
   return hip_status(pa::launch_decode(a, (hipStream_t)stream), "attn_decode_paged launch");
+}
+
+size_t attn_decode_layered_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_q_heads % num_kv_heads != 0)
+    return 0;
+  const int nwg = pa::decode_grid_size();
+  if (nwg <= 0) return 0;
+  return 2 * round_up_256(decode_ws_bytes(batch, num_q_heads, num_kv_heads, head_dim, nwg));
+}
+
+pa_status attn_decode_paged_layered(const void *q, const pa_kv_cache *cache_hi, const int32_t *block_table_hi,
+                                    int32_t max_pages_hi, const int32_t *len_hi, const pa_kv_cache *cache_lo,
+                                    const int32_t *block_table_lo, int32_t max_pages_lo, const int32_t *len_lo,
+                                    int32_t batch, int32_t num_q_heads, float softmax_scale, void *out, float *lse,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+  pa_status st = check_cache(cache_hi, true);
+  if (st != PA_OK) return st;
+  if ((st = check_cache(cache_lo, true)) != PA_OK) return st;
+  if (cache_hi->dtype == PA_F32 || cache_lo->dtype == PA_F32)
+    return fail(PA_ERR_UNSUPPORTED, "layered decode takes bf16 or int8 caches");
+  if (cache_hi->num_kv_heads != cache_lo->num_kv_heads || cache_hi->head_dim != cache_lo->head_dim)
+    return fail(PA_ERR_INVALID_ARG, "the two caches must have the same num_kv_heads and head_dim");
+  if (batch < 0) return fail(PA_ERR_INVALID_ARG, "batch must be >= 0");
+  if (num_q_heads <= 0 || num_q_heads % cache_hi->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, cache_hi->num_kv_heads);
+  if (num_q_heads / cache_hi->num_kv_heads > 16)
+    return fail(PA_ERR_UNSUPPORTED, "decode supports at most 16 query heads per KV head (got %d)",
+                num_q_heads / cache_hi->num_kv_heads);
+  if ((st = check_scale(softmax_scale)) != PA_OK) return st;
+  if (batch == 0) return ok();
+  if (q == nullptr || block_table_hi == nullptr || len_hi == nullptr || block_table_lo == nullptr ||
+      len_lo == nullptr || out == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (max_pages_hi <= 0 || max_pages_lo <= 0) return fail(PA_ERR_INVALID_ARG, "max_pages_* must be > 0");
+  const int nwg = pa::decode_grid_size();
+  if (nwg <= 0) return fail(PA_ERR_HIP, "cannot query the current device");
+  const size_t part = round_up_256(decode_ws_bytes(batch, num_q_heads, cache_hi->num_kv_heads, cache_hi->head_dim, nwg));
+  if (workspace == nullptr || workspace_bytes < 2 * part)
+    return fail(PA_ERR_WORKSPACE, "layered decode needs %zu workspace bytes (got %zu)", 2 * part, workspace_bytes);
+  const pa::DecodeArgs hi = decode_args(q, cache_hi, block_table_hi, max_pages_hi, len_hi, batch, num_q_heads,
+                                        softmax_scale, -1, out, lse, workspace, nwg);
+  const pa::DecodeArgs lo = decode_args(q, cache_lo, block_table_lo, max_pages_lo, len_lo, batch, num_q_heads,
+                                        softmax_scale, -1, out, lse, (char *)workspace + part, nwg);
+  return hip_status(pa::launch_decode_layered(hi, lo, (hipStream_t)stream), "attn_decode_paged_layered launch");
 }
 
 }  // extern "C"

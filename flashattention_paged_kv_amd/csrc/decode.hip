@@ -75,15 +75,20 @@ int decode_grid_size() {
 }
 
 // Tiles of 32 keys that a decode query at position ctx - 1 reads: from the
-// tile holding the first visible key to the tile holding the last.
+// tile holding the first visible key to the tile holding the last (none for
+// an empty context).
 __device__ __forceinline__ int seg_tiles(int ctx, int window_left) {
+  ctx = max(ctx, 0);
   const int lo = window_left >= 0 ? max(0, ctx - 1 - window_left) : 0;
   return (ctx + kDecTile - 1) / kDecTile - lo / kDecTile;
 }
 
-// Workgroups that actually take tiles: at least kMinTilesPerWg tiles each,
-// so small problems are not spread thinner than the waves of one group.
-constexpr int kMinTilesPerWg = 8;
+// Workgroups that actually take tiles: at least kMinTilesPerWg tiles each.
+// One: a small problem (a few short contexts) is spread over as many
+// workgroups as it has tiles, so its time is about one tile's latency rather
+// than a chain of them (each tile waits for its block-table entry, then its
+// rows).
+constexpr int kMinTilesPerWg = 1;
 __device__ __forceinline__ int active_wgs(long long total, int launched) {
   const long long want = (total + kMinTilesPerWg - 1) / kMinTilesPerWg;
   return (int)max(1LL, min((long long)launched, want));
@@ -181,7 +186,7 @@ __global__ __launch_bounds__(kDecWaves * 64, kDecWaves / 4 * WPC) void decode_sp
     }
     if (threadIdx.x == 0) a.ws_prefix[a.batch] = per_group_total;
   }
-  if (j >= nwg) return;  // uniform across the workgroup
+  if (j >= nwg || total == 0) return;  // uniform across the workgroup
   const long long start = (long long)j * total / nwg;
   const long long end = (long long)(j + 1) * total / nwg;
   // The thread whose sequences hold list position `start` finds it.
@@ -442,16 +447,16 @@ __global__ __launch_bounds__(kDecWaves * 64, kDecWaves / 4 * WPC) void decode_sp
   }
 }
 
-// Merge the partials of one (sequence, KV head) for its G query heads:
-// M = max m_s, L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M) / L,
-// accumulated in one pass with the same running rescale as the online
-// softmax.  The workgroups that touched the head's segment (sequence, head
-// group) are those whose list ranges contain its first and last tiles and
-// every one in between.  A thread owns 4 consecutive dims of one query head.
+// Running merge of the partials that the split kernel wrote with arguments
+// `a` for (sequence b, KV head hk), query head c, dims d..d+3:
+// M = max m_s, L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M), accumulated
+// in one pass with the same running rescale as the online softmax.  The
+// workgroups that touched the head's segment (sequence, head group) are
+// those whose list ranges contain its first and last tiles and every one in
+// between.  A segment without tiles (empty context) adds nothing.
 template <int D>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
-  const int hk = blockIdx.x;
-  const int b = blockIdx.y;
+__device__ __forceinline__ void merge_partials(const DecodeArgs &a, int b, int hk, int c, int d, float &m, float &l,
+                                               f32x4 &acc) {
   const int hkv = a.c.num_kv_heads;
   const int hpw = a.hpw;
   const int ngr = hkv / hpw;
@@ -459,38 +464,53 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   const int hh = hk - hg * hpw;
   const int G = a.group;
   const long long total = (long long)ngr * a.ws_prefix[a.batch];
-  const int nwg = active_wgs(total, a.nwg);
   const int nb = seg_tiles(a.ctx_lens[b], a.window_left);
+  if (total == 0 || nb == 0) return;
+  const int nwg = active_wgs(total, a.nwg);
   const long long f0 = (long long)ngr * a.ws_prefix[b] + (long long)hg * nb;
   const long long f1 = f0 + nb - 1;
   // Workgroup holding list position f: the largest j with j*total/nwg <= f.
   const int j_lo = (int)(((f0 + 1) * nwg - 1) / total);
   const int j_hi = (int)(((f1 + 1) * nwg - 1) / total);
   const size_t seg = (size_t)b * ngr + hg;
+#pragma unroll 4
+  for (int jj = j_lo; jj <= j_hi; ++jj) {
+    const size_t idx = ((seg + jj) * hpw + hh) * G + c;
+    const float2 ml = *reinterpret_cast<const float2 *>(a.ws_ml + idx * 2);
+    const f32x4 ov = *reinterpret_cast<const f32x4 *>(a.ws_o + idx * D + d);
+    const float m_new = fmaxf(m, ml.x);
+    const float f_old = fast_exp2(m - m_new);  // 0 on the first piece
+    const float f_new = fast_exp2(ml.x - m_new);
+    l = l * f_old + ml.y * f_new;
+    acc = acc * f_old + ov * f_new;
+    m = m_new;
+  }
+}
+
+// Merge kernel: one workgroup per (KV head, sequence) merges the partials of
+// the split kernel (NP = 1), or of two split kernels over disjoint key sets
+// of the same sequences (NP = 2, `a2`), and writes O = acc / L and
+// lse = M + log2 L (natural log).  A sequence without keys gets O = 0 and
+// lse = -inf.  A thread owns 4 consecutive dims of one query head.
+template <int D, int NP>
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a, DecodeArgs a2) {
+  const int hk = blockIdx.x;
+  const int b = blockIdx.y;
+  const int G = a.group;
   for (int e = 4 * threadIdx.x; e < G * D; e += 4 * blockDim.x) {
     const int c = e / D;
     const int d = e - c * D;
     float m = -INFINITY, l = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int jj = j_lo; jj <= j_hi; ++jj) {
-      const size_t idx = ((seg + jj) * hpw + hh) * G + c;
-      const float2 ml = *reinterpret_cast<const float2 *>(a.ws_ml + idx * 2);
-      const f32x4 ov = *reinterpret_cast<const f32x4 *>(a.ws_o + idx * D + d);
-      const float m_new = fmaxf(m, ml.x);
-      const float f_old = fast_exp2(m - m_new);  // 0 on the first piece
-      const float f_new = fast_exp2(ml.x - m_new);
-      l = l * f_old + ml.y * f_new;
-      acc = acc * f_old + ov * f_new;
-      m = m_new;
-    }
-    const float inv = 1.f / l;
+    merge_partials<D>(a, b, hk, c, d, m, l, acc);
+    if constexpr (NP == 2) merge_partials<D>(a2, b, hk, c, d, m, l, acc);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
     const uint32_t lo = pack_bf16x2(acc[0] * inv, acc[1] * inv);
     const uint32_t hi = pack_bf16x2(acc[2] * inv, acc[3] * inv);
     const size_t orow = ((size_t)b * a.num_q_heads + hk * G + c) * D;
     *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + orow + d) = make_uint2(lo, hi);
     if (a.lse != nullptr && d == 0)
-      a.lse[(size_t)b * a.num_q_heads + hk * G + c] = (m + __log2f(l)) * kLn2;
+      a.lse[(size_t)b * a.num_q_heads + hk * G + c] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -559,11 +579,13 @@ __global__ __launch_bounds__(64) void rowwise_f32_kernel(const float *q, const i
       for (int e = 0; e < kPer; ++e) o[e] = fmaf(pj, vr[lane + 64 * e], o[e]);
     }
   }
-  const float inv = 1.f / l;
+  // A row without visible keys (empty context) gets O = 0 and lse = -inf.
+  const float inv = l > 0.f ? 1.f / l : 0.f;
   float *orow = out + ((size_t)(q0 + row) * num_q_heads + h) * D;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) orow[lane + 64 * e] = o[e] * inv;
-  if (lse != nullptr && lane == 0) lse[(size_t)(q0 + row) * num_q_heads + h] = (m + __log2f(l)) * kLn2;
+  if (lse != nullptr && lane == 0)
+    lse[(size_t)(q0 + row) * num_q_heads + h] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
 }
 
 hipError_t launch_rowwise_f32(const PrefillArgs &a, hipStream_t s) {
@@ -580,22 +602,44 @@ hipError_t launch_rowwise_f32(const PrefillArgs &a, hipStream_t s) {
 }
 
 template <int D, bool I8, int NB, int WPC>
-static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
+static hipError_t launch_split_t(const DecodeArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((decode_split_kernel<D, I8, NB, WPC>), dim3(a.nwg), dim3(kDecWaves * 64), 0, s, a, a.block_table,
                      a.c.k_scales, a.c.v_scales);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(a.c.num_kv_heads, a.batch), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Tiles in flight per wave: 1 for bf16 (16 KB), 2 for int8 (8 KB each).
+static hipError_t launch_split(const DecodeArgs &a, hipStream_t s) {
+  const bool i8 = a.c.dtype == 2;
+  if (a.c.head_dim == 64)
+    return i8 ? launch_split_t<64, true, 2, kDecWgsPerCu>(a, s) : launch_split_t<64, false, 1, kDecWgsPerCu>(a, s);
+  return i8 ? launch_split_t<128, true, 2, kDecWgsPerCu>(a, s) : launch_split_t<128, false, 1, kDecWgsPerCu>(a, s);
+}
+
+template <int NP>
+static hipError_t launch_reduce(const DecodeArgs &a, const DecodeArgs &a2, hipStream_t s) {
+  const dim3 grid(a.c.num_kv_heads, a.batch);
+  if (a.c.head_dim == 64)
+    hipLaunchKernelGGL((decode_reduce_kernel<64, NP>), grid, dim3(256), 0, s, a, a2);
+  else
+    hipLaunchKernelGGL((decode_reduce_kernel<128, NP>), grid, dim3(256), 0, s, a, a2);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
-  const bool i8 = a.c.dtype == 2;
-  // Tiles in flight per wave: 1 for bf16 (16 KB), 2 for int8 (8 KB each).
-  if (a.c.head_dim == 64)
-    return i8 ? launch_decode_t<64, true, 2, kDecWgsPerCu>(a, s) : launch_decode_t<64, false, 1, kDecWgsPerCu>(a, s);
-  return i8 ? launch_decode_t<128, true, 2, kDecWgsPerCu>(a, s) : launch_decode_t<128, false, 1, kDecWgsPerCu>(a, s);
+  hipError_t e = launch_split(a, s);
+  if (e != hipSuccess) return e;
+  return launch_reduce<1>(a, a, s);
+}
+
+hipError_t launch_decode_layered(const DecodeArgs &a, const DecodeArgs &a2, hipStream_t s) {
+  if (a.batch == 0) return hipSuccess;
+  hipError_t e = launch_split(a, s);
+  if (e != hipSuccess) return e;
+  e = launch_split(a2, s);
+  if (e != hipSuccess) return e;
+  return launch_reduce<2>(a, a2, s);
 }
 
 }  // namespace pa

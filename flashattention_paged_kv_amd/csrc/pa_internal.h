@@ -123,6 +123,9 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+// Two split launches over disjoint key sets of the same sequences (the
+// caches may differ in dtype and page size), then one merge of both.
+hipError_t launch_decode_layered(const DecodeArgs &a, const DecodeArgs &a2, hipStream_t s);
 hipError_t launch_append_i8(const AppendI8Args &a, hipStream_t s);
 
 }  // namespace pa

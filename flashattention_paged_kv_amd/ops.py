@@ -48,7 +48,8 @@ class _Cache(ctypes.Structure):
 _lib = None
 
 EXPORTED = ("kv_cache_append", "kv_pages_quantize_int8", "attn_prefill_paged", "attn_decode_workspace_bytes",
-            "attn_decode_paged", "pa_status_string", "pa_last_error_detail", "pa_abi_version")
+            "attn_decode_paged", "attn_decode_layered_workspace_bytes", "attn_decode_paged_layered",
+            "pa_status_string", "pa_last_error_detail", "pa_abi_version")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -67,7 +68,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.attn_decode_workspace_bytes.restype = SZ
     lib.attn_decode_paged.argtypes = [P, CP, P, I32, P, I32, I32, F32, I32, P, P, P, SZ, P]
-    for name in ("kv_cache_append", "kv_pages_quantize_int8", "attn_prefill_paged", "attn_decode_paged"):
+    lib.attn_decode_layered_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    lib.attn_decode_layered_workspace_bytes.restype = SZ
+    lib.attn_decode_paged_layered.argtypes = [P, CP, P, I32, P, CP, P, I32, P, I32, I32, F32, P, P, P, SZ, P]
+    for name in ("kv_cache_append", "kv_pages_quantize_int8", "attn_prefill_paged", "attn_decode_paged",
+                 "attn_decode_paged_layered"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -233,4 +238,38 @@ def attn_decode_paged(q: torch.Tensor, cache: KVCache, block_table: torch.Tensor
     _check(lib.attn_decode_paged(_ptr(q), ctypes.byref(cs), _ptr(block_table), block_table.shape[1],
                                  _ptr(ctx_lens), batch, hq, scale, int(window_left), _ptr(out), _ptr(lse),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return (out, lse) if return_lse else out
+
+
+def decode_layered_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:
+    return int(load_library().attn_decode_layered_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim))
+
+
+def attn_decode_paged_layered(q: torch.Tensor, cache_hi: KVCache, block_table_hi: torch.Tensor,
+                              len_hi: torch.Tensor, cache_lo: KVCache, block_table_lo: torch.Tensor,
+                              len_lo: torch.Tensor, softmax_scale: Optional[float] = None,
+                              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                              return_lse: bool = False):
+    """One query per sequence, q [B, Hq, D], against len_hi[b] keys of cache_hi
+    followed by len_lo[b] keys of cache_lo (e.g. the first tokens in bf16, the
+    rest int8).  ``workspace`` is allocated if not given."""
+    lib = load_library()
+    cs_hi, cs_lo = cache_hi._struct(), cache_lo._struct()
+    _dev(q, "q")
+    for t, name in ((block_table_hi, "block_table_hi"), (len_hi, "len_hi"), (block_table_lo, "block_table_lo"),
+                    (len_lo, "len_lo")):
+        _dev(t, name, torch.int32)
+    batch, hq, d = q.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if workspace is None:
+        nbytes = decode_layered_workspace_bytes(batch, hq, cache_hi.num_kv_heads, d)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib.attn_decode_paged_layered(_ptr(q), ctypes.byref(cs_hi), _ptr(block_table_hi), block_table_hi.shape[1],
+                                         _ptr(len_hi), ctypes.byref(cs_lo), _ptr(block_table_lo),
+                                         block_table_lo.shape[1], _ptr(len_lo), batch, hq, scale, _ptr(out),
+                                         _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _stream()))
     return (out, lse) if return_lse else out

@@ -113,6 +113,11 @@ class DecodeWorkload:
     window_left: int = -1
     spare_pages: int = 0
     ctx_lens: tuple = field(default=())   # explicit lengths override the random draw
+    # Layered cache: the first `full_tokens` positions of each sequence sit in
+    # a separate bf16 cache (pages of `full_page_size`), the rest in the
+    # kv_dtype cache.  0: one cache.
+    full_tokens: int = 0
+    full_page_size: int = 16
 
     @property
     def q_dtype(self) -> str:
@@ -166,6 +171,20 @@ def decode_inputs(w: DecodeWorkload) -> dict:
                 cu_new=torch.arange(w.batch + 1, dtype=torch.int32))
 
 
+def layered_full_inputs(w: DecodeWorkload) -> dict:
+    """The full-precision part of a layered workload: bf16 pools holding
+    min(full_tokens, ctx_b) positions of each sequence, its page assignment
+    and those lengths."""
+    ctx = decode_ctx_lens(w)
+    lens = np.minimum(ctx, w.full_tokens)
+    pages = [max(1, int(-(-int(n) // w.full_page_size))) for n in lens]
+    table, num_pages, _ = page_assignment(pages, max(pages), w.seed + 1000, 0)
+    shape = (num_pages, w.full_page_size, w.num_kv_heads, w.head_dim)
+    return dict(k_pool=normal(shape, "bf16", w.seed, STREAM_K, chunk=1),
+                v_pool=normal(shape, "bf16", w.seed, STREAM_V, chunk=1), block_table=table,
+                lens=torch.from_numpy(lens.astype(np.int32)))
+
+
 def tail_slots(block_table: torch.Tensor, ctx_lens, page_size: int):
     """(physical page, first unused slot) of each sequence's last page, as the
     page assignment above laid them out; used to poison slots no valid token
@@ -195,5 +214,10 @@ LONG_PREFILL_WINDOW = PrefillWorkload("long_window128_prefill_L32768_h32_d128_p2
 DECODE_128K_INT8 = DecodeWorkload("int8_decode_B16_hq64_hkv8_d128_ctx64k-128k_p256",
                                   16, 65536, 131072, 64, 8, 128, 256, "i8", seed=5)
 
+# The 128k int8 decode with each sequence's first 128 tokens kept in bf16.
+DECODE_128K_LAYERED = DecodeWorkload("layered_decode_B16_hq64_hkv8_d128_ctx64k-128k_first128_bf16_rest_int8",
+                                     16, 65536, 131072, 64, 8, 128, 256, "i8", seed=5, full_tokens=128,
+                                     full_page_size=16)
+
 WORKLOADS = {w.name: w for w in (TINY_FP32, LLAMA7B_PREFILL, LLAMA70B_DECODE, LONG_PREFILL,
-                                 LONG_PREFILL_WINDOW, DECODE_128K_INT8)}
+                                 LONG_PREFILL_WINDOW, DECODE_128K_INT8, DECODE_128K_LAYERED)}

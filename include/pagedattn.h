@@ -172,7 +172,8 @@ size_t attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t n
  * Sources: as attn_prefill_paged, with q_len = 1; the split merge uses the
  * same running-max / running-sum rescaling as the online softmax.
  *   q        : [batch, num_q_heads, head_dim]; fp32 for PA_F32, else bf16
- *   ctx_lens : int32 [batch] keys per sequence INCLUDING the new token (>= 1)
+ *   ctx_lens : int32 [batch] keys per sequence INCLUDING the new token (>= 1;
+ *              a sequence with 0 keys gets O = 0 and lse = -inf)
  *   window_left: as for prefill (the query sits at position ctx_lens[b] - 1)
  *   out      : [batch, num_q_heads, head_dim], dtype of q
  *   lse      : fp32 [batch, num_q_heads] or NULL
@@ -184,6 +185,35 @@ pa_status attn_decode_paged(const void *q, const pa_kv_cache *cache, const int32
                             int32_t max_pages_per_seq, const int32_t *ctx_lens, int32_t batch,
                             int32_t num_q_heads, float softmax_scale, int32_t window_left, void *out,
                             float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/* attn_decode_layered_workspace_bytes - HOST function: workspace bytes that
+ * attn_decode_paged_layered needs for these sizes (0 on bad input). */
+size_t attn_decode_layered_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim);
+
+/* attn_decode_paged_layered - single-token decode over a context held in two
+ * caches: the first len_hi[b] positions of sequence b in cache_hi (through
+ * block_table_hi) and the next len_lo[b] positions in cache_lo (through
+ * block_table_lo).  This is the layered cache of "大模型推理优化：KV Cache与
+ * FlashAttention实战" section 2.2: the first tokens of a sequence (128
+ * there) kept at full precision, later ones int8 with group scales
+ * ("LLM推理系统优化：KV缓存管理与动态批处理技术" section 3.2).  The result is exactly the attention of the query over all
+ * len_hi[b] + len_lo[b] keys (no mask: the query is the last position).
+ *   q, out, lse : as attn_decode_paged
+ *   cache_hi, cache_lo : bf16 or int8 caches (with scales), same
+ *              num_kv_heads and head_dim; page sizes may differ
+ *   len_hi, len_lo : int32 [batch] device arrays, >= 0 each (a sequence
+ *              with no keys at all gets O = 0, lse = -inf)
+ *   workspace: at least attn_decode_layered_workspace_bytes(...) bytes;
+ *              contents undefined after the call
+ * Errors: PA_ERR_UNSUPPORTED for an fp32 cache or more than 16 query heads
+ * per KV head, PA_ERR_INVALID_ARG for mismatched caches, NULL pointers or
+ * bad sizes, PA_ERR_WORKSPACE when the workspace is missing or too small. */
+pa_status attn_decode_paged_layered(const void *q, const pa_kv_cache *cache_hi, const int32_t *block_table_hi,
+                                    int32_t max_pages_hi, const int32_t *len_hi, const pa_kv_cache *cache_lo,
+                                    const int32_t *block_table_lo, int32_t max_pages_lo, const int32_t *len_lo,
+                                    int32_t batch, int32_t num_q_heads, float softmax_scale, void *out,
+                                    float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static description of a status code. */
 const char *pa_status_string(pa_status status);

@@ -143,3 +143,48 @@ def test_quantize_rejects_bad_args():
     assert lib.kv_pages_quantize_int8(FAKE, FAKE, FAKE, 1, 16, 1, 80, None) == 2
     assert lib.kv_pages_quantize_int8(FAKE, FAKE, FAKE, 1, 48, 1, 128, None) == 2
     assert lib.kv_pages_quantize_int8(FAKE, FAKE, FAKE, 0, 16, 1, 128, None) == 0
+
+
+def _layered(hi, lo, **kw):
+    lib = ops.load_library()
+    a = dict(q=FAKE, bt_hi=FAKE, mp_hi=4, len_hi=FAKE, bt_lo=FAKE, mp_lo=4, len_lo=FAKE, batch=2, hq=4, scale=0.1,
+             out=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.attn_decode_paged_layered(a["q"], ctypes.byref(hi), a["bt_hi"], a["mp_hi"], a["len_hi"],
+                                         ctypes.byref(lo), a["bt_lo"], a["mp_lo"], a["len_lo"], a["batch"],
+                                         a["hq"], a["scale"], a["out"], None, a["ws"], a["ws_bytes"], None)
+
+
+def _i8_cache(**kw):
+    c = dict(dtype=ops.PA_I8, k_scales=0x3000, v_scales=0x4000, page_size=256)
+    c.update(kw)
+    return _cache(**c)
+
+
+@pytest.mark.parametrize("hi_kw,lo_kw,kw,status", [
+    (dict(), dict(), dict(hq=3), 1),                         # heads not a multiple of Hkv
+    (dict(), dict(num_kv_heads=4), dict(), 1),               # caches disagree on heads
+    (dict(), dict(head_dim=64), dict(), 1),                  # caches disagree on head_dim
+    (dict(dtype=ops.PA_F32), dict(), dict(), 2),             # fp32 is not a layered dtype
+    (dict(), dict(k_scales=None), dict(), 1),                # int8 without scales
+    (dict(), dict(), dict(len_lo=None), 1),
+    (dict(), dict(), dict(mp_lo=0), 1),
+    (dict(), dict(), dict(ws=None), 4),
+    (dict(), dict(), dict(ws_bytes=1024), 4),
+    (dict(), dict(), dict(hq=2 * 17), 2),
+    (dict(), dict(), dict(batch=-1), 1),
+])
+def test_layered_decode_rejects_bad_args(hi_kw, lo_kw, kw, status):
+    assert _layered(_cache(**hi_kw), _i8_cache(**lo_kw), **kw) == status
+    assert _detail() != ""
+
+
+def test_layered_decode_workspace_and_empty_batch():
+    lib = ops.load_library()
+    n = lib.attn_decode_layered_workspace_bytes(16, 64, 8, 128)
+    assert n >= 2 * lib.attn_decode_workspace_bytes(16, 64, 8, 128, 4, 16) and n % 256 == 0
+    assert lib.attn_decode_layered_workspace_bytes(0, 64, 8, 128) == 0
+    assert _layered(_cache(), _i8_cache(), batch=0, q=None, out=None) == 0
+    # one byte short of the query for these sizes is rejected (no work enqueued)
+    need = lib.attn_decode_layered_workspace_bytes(2, 4, 2, 128)
+    assert _layered(_cache(), _i8_cache(), batch=2, hq=4, ws_bytes=need - 1) == 4

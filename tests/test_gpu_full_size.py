@@ -76,3 +76,34 @@ def test_int8_decode_128k_sampled_sequences():
     seqs = [int(np.argmin(ctx)), int(np.argmax(ctx)), 7]
     (ref, _), _ = run.oracle(seqs)
     check_close(out[seqs], ref, "bf16", f"sequences {seqs} (ctx {ctx[seqs].tolist()})")
+
+
+def test_layered_decode_128k_sampled_sequences():
+    """The layered bench workload at full size (first 128 tokens bf16, the
+    rest int8), in the launch configuration the bench times; the oracle
+    checks three sampled sequences, quantising their int8 pages itself."""
+    w = wl.DECODE_128K_LAYERED
+    say(f"full size: {w.name}")
+    inp, full = wl.decode_inputs(w), wl.layered_full_inputs(w)
+    kc, ks = ops.kv_pages_quantize_int8(inp["k_pool"].cuda())
+    vc, vs = ops.kv_pages_quantize_int8(inp["v_pool"].cuda())
+    ctx = inp["ctx_lens"].numpy().astype(np.int64)
+    len_hi = full["lens"].numpy().astype(np.int64)
+    len_lo = (ctx - len_hi).astype(np.int32)
+    out = ops.attn_decode_paged_layered(inp["q"].cuda(), ops.KVCache(full["k_pool"].cuda(), full["v_pool"].cuda()),
+                                        full["block_table"].cuda(), full["lens"].cuda(), ops.KVCache(kc, vc, ks, vs),
+                                        inp["block_table"].cuda(), torch.from_numpy(len_lo).cuda())
+    torch.cuda.synchronize()
+    del kc, vc
+    seqs = [int(np.argmin(ctx)), int(np.argmax(ctx)), 7]
+    bt = inp["block_table"].numpy()
+    used = sorted({int(p) for b in seqs for p in bt[b][: -(-int(len_lo[b]) // w.page_size)]})
+    remap = {p: i for i, p in enumerate(used)}
+    k8, k8s = oracle.quantize_int8_pages(f64(inp["k_pool"][used]))
+    v8, v8s = oracle.quantize_int8_pages(f64(inp["v_pool"][used]))
+    lo = dict(k=k8, v=v8, k_scales=k8s, v_scales=v8s, page_size=w.page_size, lens=len_lo[seqs],
+              block_table=np.array([[remap.get(int(p), 0) for p in bt[b]] for b in seqs]))
+    hi = dict(k=f64(full["k_pool"]), v=f64(full["v_pool"]), page_size=w.full_page_size, lens=len_hi[seqs],
+              block_table=full["block_table"].numpy()[seqs])
+    ref, _ = oracle.decode_layered(f64(inp["q"][seqs]), hi, lo)
+    check_close(out[seqs], ref, "bf16", f"sequences {seqs} (ctx {ctx[seqs].tolist()})")

@@ -328,3 +328,74 @@ def test_int8_append_is_bit_exact_then_decodes():
     torch.cuda.synchronize()
     ref, _ = oracle.decode_paged(f64(q), ok, ov, bt, final, P, k_scales=oks, v_scales=ovs)
     check_close(out, ref, "bf16", "decode after int8 appends")
+
+
+def _layered_part(lens, page_size, hkv, d, seed, stream0, int8):
+    """Pools and a permuted block table holding `lens` positions per sequence
+    (int8 parts quantised by the oracle on the CPU)."""
+    pages = [max(1, -(-n // page_size)) for n in lens]
+    n_pages = sum(pages) + 1
+    perm = wl.rng(seed, wl.STREAM_PERM, stream0).permutation(n_pages).astype(np.int32)
+    bt = np.zeros((len(lens), max(pages)), dtype=np.int32)
+    at = 0
+    for b, n in enumerate(pages):
+        bt[b, :n] = perm[at:at + n]
+        at += n
+    k = wl.normal((n_pages, page_size, hkv, d), "bf16", seed, wl.STREAM_K, stream0)
+    v = wl.normal((n_pages, page_size, hkv, d), "bf16", seed, wl.STREAM_V, stream0)
+    part = dict(block_table=bt, lens=np.asarray(lens, dtype=np.int32), page_size=page_size)
+    if int8:
+        kc, ks = oracle.quantize_int8_pages(f64(k))
+        vc, vs = oracle.quantize_int8_pages(f64(v))
+        part.update(k=kc, v=vc, k_scales=ks, v_scales=vs)
+        cache = ops.KVCache(torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda(),
+                            torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda())
+    else:
+        part.update(k=f64(k), v=f64(v))
+        cache = ops.KVCache(k.cuda(), v.cuda())
+    return part, cache
+
+
+@pytest.mark.parametrize("F,p_hi,p_lo,lo_int8,hq,hkv", [
+    (128, 16, 256, True, 64, 8), (64, 64, 16, False, 8, 2), (32, 16, 64, True, 16, 1),
+])
+def test_layered_decode_matches_oracle(F, p_hi, p_lo, lo_int8, hq, hkv):
+    """First F positions of each sequence in a bf16 cache, the rest in a
+    second cache (int8 or bf16, other page size); lengths around F, a single
+    key and a sequence without keys."""
+    d, seed = 128, 71
+    ctx = [1, F - 1, F, F + 1, 700, 2049, 0]
+    say(f"layered decode F={F} P_hi={p_hi} P_lo={p_lo} int8={lo_int8} hq={hq} hkv={hkv}")
+    hi, c_hi = _layered_part([min(F, n) for n in ctx], p_hi, hkv, d, seed, 0, False)
+    lo, c_lo = _layered_part([max(0, n - F) for n in ctx], p_lo, hkv, d, seed, 1, lo_int8)
+    q = wl.normal((len(ctx), hq, d), "bf16", seed, wl.STREAM_Q)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    out, lse = ops.attn_decode_paged_layered(q.cuda(), c_hi, dev(hi["block_table"]), dev(hi["lens"]), c_lo,
+                                             dev(lo["block_table"]), dev(lo["lens"]), return_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.decode_layered(f64(q), hi, lo)
+    check_close(out[:-1], ref[:-1], "bf16", "layered out")
+    assert torch.count_nonzero(out[-1]).item() == 0 and bool(torch.isneginf(lse[-1]).all())
+    err = np.abs(f64(lse[:-1]) - ref_lse[:-1]).max()
+    say(f"  lse max|d|={err:.3e}")
+    assert err <= 1e-3
+
+
+def test_decode_empty_context_gives_zero_output():
+    """A sequence with ctx_lens = 0 has no keys: O = 0, lse = -inf, and the
+    other sequences of the batch are unaffected."""
+    P, hq, hkv, d, seed = 16, 8, 2, 128, 72
+    ctx = [0, 37, 0, 300]
+    say("decode with empty contexts")
+    part, cache = _layered_part(ctx, P, hkv, d, seed, 0, False)
+    q = wl.normal((len(ctx), hq, d), "bf16", seed, wl.STREAM_Q)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    out, lse = ops.attn_decode_paged(q.cuda(), cache, dev(part["block_table"]), dev(part["lens"]), return_lse=True)
+    torch.cuda.synchronize()
+    # decode_layered with an empty second part is the plain decode (pinned),
+    # and defines the no-key case.
+    empty = dict(part, lens=np.zeros(len(ctx), dtype=np.int32))
+    ref, ref_lse = oracle.decode_layered(f64(q), part, empty)
+    check_close(out, ref, "bf16", "decode out")
+    for b in (0, 2):
+        assert torch.count_nonzero(out[b]).item() == 0 and bool(torch.isneginf(lse[b]).all())
