@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 import test_oracle_layered as lpins
+import test_oracle_pages as ppins
 import test_oracle_pins as pins
 import test_oracle_quant_append_counts as qpins
 
@@ -55,6 +56,16 @@ LAYERED_MUTANTS = [
 ]
 
 
+PAGES_MUTANTS = [
+    ("and self.refcount[row[have - 1]] > 1)", "and False)"),                 # no copy-on-write
+    ("length % self.page_size != 0", "True"),                                # copy also at a page boundary
+    ("        self.rows[seq] = []\n", "        pass\n"),                    # release keeps the table row
+    ("            self.refcount[p] += 1\n", "            pass\n"),            # fork does not count holders
+    ("p = min(self.free_pages())", "p = max(self.free_pages())"),            # highest id first
+    ("k[d], v[d] = k[s], v[s]", "k[d], v[d] = k[s], v[d]"),                  # V page not copied
+]
+
+
 def _load_mutant(filename, old, new):
     src = open(os.path.join(ORACLE_DIR, filename)).read()
     assert src.count(old) >= 1, f"mutation anchor not found: {old}"
@@ -95,11 +106,20 @@ def _layered_battery():
     lpins.test_layered_sequence_without_keys()
 
 
+def _pages_battery():
+    ppins.test_hand_worked_scenario()
+    ppins.test_out_of_pages_changes_nothing()
+    for seed in range(6):
+        ppins.test_random_scripts_keep_invariants_and_contents(seed)
+    ppins.test_copy_pages_is_a_page_copy()
+
+
 def test_battery_passes_on_the_real_oracle():
     _attention_battery()
     _quant_battery()
     _append_battery()
     _layered_battery()
+    _pages_battery()
 
 
 @pytest.mark.parametrize("old,new", ATTENTION_MUTANTS)
@@ -133,3 +153,13 @@ def test_layered_mutant_is_caught(monkeypatch, old, new):
     monkeypatch.setattr(oracle, "decode_layered", mut.decode_layered)
     with pytest.raises((AssertionError, ValueError, IndexError)):
         _layered_battery()
+
+
+@pytest.mark.parametrize("old,new", PAGES_MUTANTS)
+def test_pages_mutant_is_caught(monkeypatch, old, new):
+    from oracle import pages
+    mut = _load_mutant("pages.py", old, new)
+    monkeypatch.setattr(pages, "PagePoolModel", mut.PagePoolModel)
+    monkeypatch.setattr(pages, "copy_pages", mut.copy_pages)
+    with pytest.raises((AssertionError, ValueError, IndexError, TypeError)):
+        _pages_battery()
