@@ -115,6 +115,14 @@ pa::DecodeArgs decode_args(const void *q, const pa_kv_cache *cache, const int32_
 
 }  // namespace
 
+namespace pa {
+// Status reporting for the host-side parts outside this file.
+pa_status report(pa_status st, const char *msg) {
+  if (st == PA_OK) return ok();
+  return fail(st, "%s", msg);
+}
+}  // namespace pa
+
 extern "C" {
 
 int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
@@ -126,6 +134,7 @@ const char *pa_status_string(pa_status status) {
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_HIP: return "HIP runtime error";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_OUT_OF_PAGES: return "not enough free pages in the pool";
   }
   return "unknown status";
 }
@@ -232,6 +241,23 @@ pa_status attn_prefill_paged(const void *q, const int32_t *cu_q, const pa_kv_cac
   a.out = out;
   a.lse = lse;
   return hip_status(pa::launch_prefill(a, (hipStream_t)stream), "attn_prefill_paged launch");
+}
+
+pa_status kv_cache_copy_pages(const pa_kv_cache *cache, const int32_t *src_pages, const int32_t *dst_pages,
+                              int32_t n, void *stream) {
+  pa_status st = check_cache(cache, true);
+  if (st != PA_OK) return st;
+  if (n < 0) return fail(PA_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return ok();
+  if (src_pages == nullptr || dst_pages == nullptr) return fail(PA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (n > 65535) return fail(PA_ERR_INVALID_ARG, "at most 65535 pages per call (got %d)", n);
+  const size_t esz = cache->dtype == PA_F32 ? 4 : cache->dtype == PA_BF16 ? 2 : 1;
+  const size_t page_bytes = (size_t)cache->page_size * cache->num_kv_heads * cache->head_dim * esz;
+  const bool i8 = cache->dtype == PA_I8;
+  return hip_status(pa::launch_copy_pages(cache->k_pages, cache->v_pages, i8 ? cache->k_scales : nullptr,
+                                          i8 ? cache->v_scales : nullptr, cache->num_kv_heads, src_pages, dst_pages,
+                                          n, page_bytes, (hipStream_t)stream),
+                    "kv_cache_copy_pages launch");
 }
 
 size_t attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -127,5 +127,8 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 // caches may differ in dtype and page size), then one merge of both.
 hipError_t launch_decode_layered(const DecodeArgs &a, const DecodeArgs &a2, hipStream_t s);
 hipError_t launch_append_i8(const AppendI8Args &a, hipStream_t s);
+// Copy whole pages src[i] -> dst[i] (K, V and, when given, their scales).
+hipError_t launch_copy_pages(void *k, void *v, float *k_scales, float *v_scales, int num_kv_heads,
+                             const int32_t *src, const int32_t *dst, int n, size_t page_bytes, hipStream_t s);
 
 }  // namespace pa

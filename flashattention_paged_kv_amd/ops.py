@@ -49,6 +49,8 @@ _lib = None
 
 EXPORTED = ("kv_cache_append", "kv_pages_quantize_int8", "attn_prefill_paged", "attn_decode_workspace_bytes",
             "attn_decode_paged", "attn_decode_layered_workspace_bytes", "attn_decode_paged_layered",
+            "kv_cache_copy_pages", "pa_pool_create", "pa_pool_destroy", "pa_pool_extend", "pa_pool_fork",
+            "pa_pool_release", "pa_pool_export", "pa_pool_free_pages", "pa_pool_refcount",
             "pa_status_string", "pa_last_error_detail", "pa_abi_version")
 
 
@@ -71,8 +73,22 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode_layered_workspace_bytes.argtypes = [I32, I32, I32, I32]
     lib.attn_decode_layered_workspace_bytes.restype = SZ
     lib.attn_decode_paged_layered.argtypes = [P, CP, P, I32, P, CP, P, I32, P, I32, I32, F32, P, P, P, SZ, P]
+    lib.kv_cache_copy_pages.argtypes = [CP, P, P, I32, P]
+    PI = ctypes.POINTER(I32)
+    lib.pa_pool_create.argtypes = [I32, I32, I32, I32, ctypes.POINTER(P)]
+    lib.pa_pool_destroy.argtypes = [P]
+    lib.pa_pool_destroy.restype = None
+    lib.pa_pool_extend.argtypes = [P, I32, I32, PI, PI, I32, PI]
+    lib.pa_pool_fork.argtypes = [P, I32, I32, I32]
+    lib.pa_pool_release.argtypes = [P, I32]
+    lib.pa_pool_export.argtypes = [P, PI, PI]
+    lib.pa_pool_free_pages.argtypes = [P]
+    lib.pa_pool_refcount.argtypes = [P, I32]
+    for name in ("pa_pool_free_pages", "pa_pool_refcount"):
+        getattr(lib, name).restype = I32
     for name in ("kv_cache_append", "kv_pages_quantize_int8", "attn_prefill_paged", "attn_decode_paged",
-                 "attn_decode_paged_layered"):
+                 "attn_decode_paged_layered", "kv_cache_copy_pages", "pa_pool_create", "pa_pool_extend",
+                 "pa_pool_fork", "pa_pool_release", "pa_pool_export"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -273,3 +289,65 @@ def attn_decode_paged_layered(q: torch.Tensor, cache_hi: KVCache, block_table_hi
                                          _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                          _stream()))
     return (out, lse) if return_lse else out
+
+
+def kv_cache_copy_pages(cache: KVCache, src_pages: torch.Tensor, dst_pages: torch.Tensor) -> None:
+    """Copy whole pages src_pages[i] -> dst_pages[i] of the cache (K, V and
+    int8 scales) on the current stream."""
+    lib = load_library()
+    cs = cache._struct()
+    _dev(src_pages, "src_pages", torch.int32)
+    _dev(dst_pages, "dst_pages", torch.int32)
+    if src_pages.numel() != dst_pages.numel():
+        raise ValueError("src_pages and dst_pages must have the same length")
+    _check(lib.kv_cache_copy_pages(ctypes.byref(cs), _ptr(src_pages), _ptr(dst_pages), src_pages.numel(),
+                                   _stream()))
+
+
+class PagePool:
+    """Host page pool of the library (native): block-table rows, shared
+    pages with reference counts, copy-on-write of a shared partly filled
+    page.  Host-only; ``block_table()`` gives the table to upload."""
+
+    def __init__(self, num_pages: int, page_size: int, max_seqs: int, max_pages_per_seq: int):
+        self._lib = load_library()
+        self._h = ctypes.c_void_p()
+        _check(self._lib.pa_pool_create(num_pages, page_size, max_seqs, max_pages_per_seq, ctypes.byref(self._h)))
+        self.num_pages, self.page_size = num_pages, page_size
+        self.max_seqs, self.max_pages_per_seq = max_seqs, max_pages_per_seq
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.pa_pool_destroy(h)
+            self._h = None
+
+    def extend(self, seq: int, new_len: int):
+        """Grow `seq` to `new_len` tokens; returns the (src, dst) page pairs to
+        copy before appending (empty unless a shared page was replaced)."""
+        src, dst, n = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(self._lib.pa_pool_extend(self._h, seq, new_len, ctypes.byref(src), ctypes.byref(dst), 1,
+                                        ctypes.byref(n)))
+        return [(src.value, dst.value)] if n.value else []
+
+    def fork(self, parent: int, child: int, n_tokens: int) -> None:
+        _check(self._lib.pa_pool_fork(self._h, parent, child, n_tokens))
+
+    def release(self, seq: int) -> None:
+        _check(self._lib.pa_pool_release(self._h, seq))
+
+    def block_table(self) -> torch.Tensor:
+        t = torch.empty((self.max_seqs, self.max_pages_per_seq), dtype=torch.int32)
+        _check(self._lib.pa_pool_export(self._h, ctypes.cast(t.data_ptr(), ctypes.POINTER(ctypes.c_int32)), None))
+        return t
+
+    def lens(self) -> torch.Tensor:
+        t = torch.empty(self.max_seqs, dtype=torch.int32)
+        _check(self._lib.pa_pool_export(self._h, None, ctypes.cast(t.data_ptr(), ctypes.POINTER(ctypes.c_int32))))
+        return t
+
+    def free_pages(self) -> int:
+        return int(self._lib.pa_pool_free_pages(self._h))
+
+    def refcount(self, page: int) -> int:
+        return int(self._lib.pa_pool_refcount(self._h, page))

@@ -66,7 +66,8 @@ typedef enum pa_status {
   PA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad scale, ...      */
   PA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, page_size, dtype  */
   PA_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed        */
-  PA_ERR_WORKSPACE = 4    /* decode workspace missing or too small             */
+  PA_ERR_WORKSPACE = 4,   /* decode workspace missing or too small             */
+  PA_ERR_OUT_OF_PAGES = 5 /* a page pool has too few free pages (no change)    */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -214,6 +215,59 @@ pa_status attn_decode_paged_layered(const void *q, const pa_kv_cache *cache_hi, 
                                     const int32_t *block_table_lo, int32_t max_pages_lo, const int32_t *len_lo,
                                     int32_t batch, int32_t num_q_heads, float softmax_scale, void *out,
                                     float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/* kv_cache_copy_pages - copy whole pages src_pages[i] -> dst_pages[i]
+ * (K, V and, for PA_I8, the pages' scales): the device half of a page pool's
+ * copy-on-write (below).
+ *   src_pages, dst_pages : int32 [n] device arrays of physical page ids
+ *                          (not validated; dst pages must not be src pages)
+ *   n                    : host int, 0 <= n <= 65535 */
+pa_status kv_cache_copy_pages(const pa_kv_cache *cache, const int32_t *src_pages, const int32_t *dst_pages,
+                              int32_t n, void *stream);
+
+/* Page pool - HOST bookkeeping of a cache's physical pages: which pages each
+ * sequence holds (its block-table row) and how many sequences hold each
+ * page.  Sources: the page table of "Flash Attention与Paged KV Cache优化大模型
+ * 计算效率" section 3.2 (allocate a page per logical page; releasing a
+ * sequence also clears its table entries, that page's section 5), and the
+ * shared prompt pages with reference counts of "大模型推理优化：KV Cache与
+ * FlashAttention实战" section 4.1 and "LLM推理系统优化：KV缓存管理与动态批处理
+ * 技术" section 3.1.  Free pages are taken lowest id first.  Every function
+ * below runs on the host only, touches no device memory and serialises
+ * calls on one pool with a lock; the caller uploads the exported table. */
+typedef struct pa_page_pool pa_page_pool;
+
+/* Pool of num_pages pages of page_size tokens for sequences 0..max_seqs-1 of
+ * at most max_pages_per_seq pages each; *pool receives the handle. */
+pa_status pa_pool_create(int32_t num_pages, int32_t page_size, int32_t max_seqs, int32_t max_pages_per_seq,
+                         pa_page_pool **pool);
+void pa_pool_destroy(pa_page_pool *pool);
+
+/* Grow sequence seq to new_len tokens (before its rows [len, new_len) are
+ * appended), taking fresh pages as needed.  If the page that receives
+ * position len is partly filled and held by other sequences too, seq gets a
+ * fresh page in its place and the pair (shared page, fresh page) is written
+ * to copy_src[0] / copy_dst[0] with *n_copies = 1: copy it on the device
+ * (kv_cache_copy_pages) before appending.  PA_ERR_OUT_OF_PAGES leaves the
+ * pool unchanged. */
+pa_status pa_pool_extend(pa_page_pool *pool, int32_t seq, int32_t new_len, int32_t *copy_src, int32_t *copy_dst,
+                         int32_t copy_cap, int32_t *n_copies);
+
+/* Let the empty sequence child share the pages that hold the first n_tokens
+ * (1 <= n_tokens <= parent length) of parent: a shared prompt. */
+pa_status pa_pool_fork(pa_page_pool *pool, int32_t parent, int32_t child, int32_t n_tokens);
+
+/* Drop seq's hold on its pages (a page is free once no sequence holds it)
+ * and clear its table row (entries -1, length 0). */
+pa_status pa_pool_release(pa_page_pool *pool, int32_t seq);
+
+/* Copy the block table, int32 [max_seqs, max_pages_per_seq] (-1 unused),
+ * and/or the lengths, int32 [max_seqs], into HOST buffers (NULL skips). */
+pa_status pa_pool_export(pa_page_pool *pool, int32_t *block_table, int32_t *lens);
+
+/* Free pages, and the number of sequences holding a page (-1 on bad input). */
+int32_t pa_pool_free_pages(pa_page_pool *pool);
+int32_t pa_pool_refcount(pa_page_pool *pool, int32_t page);
 
 /* Static description of a status code. */
 const char *pa_status_string(pa_status status);

@@ -20,7 +20,7 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails it
 
 def _declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:pa_status|size_t|const char \*|int32_t)\s*\*?\s*(\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:pa_status|size_t|const char \*|int32_t|void)\s*\*?\s*(\w+)\s*\(",
                                  text, flags=re.M)))
 
 
@@ -40,7 +40,7 @@ def test_header_declarations_are_exported():
 def test_status_strings():
     lib = ops.load_library()
     assert lib.pa_status_string(0) == b"ok"
-    for s in range(1, 5):
+    for s in range(1, 6):
         assert lib.pa_status_string(s) not in (b"ok", b"unknown status")
     assert lib.pa_status_string(99) == b"unknown status"
 

@@ -399,3 +399,82 @@ def test_decode_empty_context_gives_zero_output():
     check_close(out, ref, "bf16", "decode out")
     for b in (0, 2):
         assert torch.count_nonzero(out[b]).item() == 0 and bool(torch.isneginf(lse[b]).all())
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_page_pool_prefix_sharing_with_copy_on_write(int8):
+    """A 150-token prompt in sequence 0, forked whole into sequence 1 and at
+    100 tokens into sequence 2; each then appends its own rows, so the pool
+    hands out private copies of the shared partly filled pages
+    (kv_cache_copy_pages) before the appends.  The device pools must equal
+    the oracle's replay of the same steps (its model's tables, page copies
+    and appends) bit for bit, and each sequence's decode must match the
+    oracle over its own tokens."""
+    from oracle import pages
+    n_pages, P, hq, hkv, d, seed = 48, 16, 8, 2, 128, 81
+    say(f"page pool with copy-on-write, int8={int8}")
+    pool = ops.PagePool(n_pages, P, 3, 16)
+    model = pages.PagePoolModel(n_pages, P, 3, 16)
+    shape = (n_pages, P, hkv, d)
+    if int8:
+        kc, vc = torch.zeros(shape, dtype=torch.int8), torch.zeros(shape, dtype=torch.int8)
+        ks, vs = torch.ones((n_pages, hkv)), torch.ones((n_pages, hkv))
+        cache = ops.KVCache(kc.cuda(), vc.cuda(), ks.cuda(), vs.cuda())
+        ref = [kc.numpy(), vc.numpy(), ks.numpy(), vs.numpy()]
+    else:
+        cache = ops.KVCache(torch.zeros(shape, dtype=torch.bfloat16).cuda(), torch.zeros(shape, dtype=torch.bfloat16).cuda())
+        ref = [np.zeros(shape, dtype=np.int16), np.zeros(shape, dtype=np.int16), None, None]
+    i32 = lambda x: torch.tensor(np.asarray(x, dtype=np.int32)).cuda()
+
+    def step(seq, rows_k, rows_v, fork=None):
+        if fork is not None:
+            pool.fork(*fork)
+            model.fork(*fork)
+            return
+        start = model.lens[seq]
+        new_len = start + rows_k.shape[0]
+        copies = pool.extend(seq, new_len)
+        want = model.extend(seq, new_len)
+        assert copies == want
+        table = model.block_table()
+        assert np.array_equal(pool.block_table().numpy(), table)
+        if copies:
+            src, dst = [c[0] for c in copies], [c[1] for c in copies]
+            ops.kv_cache_copy_pages(cache, i32(src), i32(dst))
+            ref[0], ref[1], ref[2], ref[3] = pages.copy_pages(ref[0], ref[1], src, dst, ref[2], ref[3])
+        row = table[seq:seq + 1]
+        ops.kv_cache_append(cache, rows_k.cuda(), rows_v.cuda(), i32(row), i32([start]),
+                            i32([0, rows_k.shape[0]]), max_new=rows_k.shape[0])
+        if int8:
+            ref[0], ref[2] = oracle.append_int8_pages(ref[0], ref[2], f64(rows_k), row, [start], [0, rows_k.shape[0]], P)
+            ref[1], ref[3] = oracle.append_int8_pages(ref[1], ref[3], f64(rows_v), row, [start], [0, rows_k.shape[0]], P)
+        else:
+            ref[0], ref[1] = oracle.append_pages(ref[0], ref[1], bits(rows_k), bits(rows_v), row, [start],
+                                                 [0, rows_k.shape[0]], P)
+
+    rows = lambda n, c: (wl.normal((n, hkv, d), "bf16", seed, wl.STREAM_KNEW, c),
+                         wl.normal((n, hkv, d), "bf16", seed, wl.STREAM_VNEW, c))
+    step(0, *rows(150, 0))
+    step(None, None, None, fork=(0, 1, 150))
+    step(None, None, None, fork=(0, 2, 100))
+    step(1, *rows(40, 1))
+    step(2, *rows(37, 2))
+    step(0, *rows(5, 3))
+    torch.cuda.synchronize()
+    if int8:
+        assert np.array_equal(cache.k_pages.cpu().numpy(), ref[0]) and np.array_equal(cache.v_pages.cpu().numpy(), ref[1])
+        assert np.array_equal(cache.k_scales.cpu().numpy(), ref[2]) and np.array_equal(cache.v_scales.cpu().numpy(), ref[3])
+    else:
+        assert np.array_equal(bits(cache.k_pages), ref[0]) and np.array_equal(bits(cache.v_pages), ref[1])
+    lens = model.lens
+    assert lens == [155, 190, 137] and pool.lens().tolist() == lens
+    q = wl.normal((3, hq, d), "bf16", seed, wl.STREAM_Q)
+    out = ops.attn_decode_paged(q.cuda(), cache, i32(model.block_table()), i32(lens))
+    torch.cuda.synchronize()
+    if int8:
+        want, _ = oracle.decode_paged(f64(q), ref[0], ref[1], model.block_table(), lens, P, k_scales=ref[2], v_scales=ref[3])
+    else:
+        kf = torch.from_numpy(ref[0]).view(torch.bfloat16).float().numpy()
+        vf = torch.from_numpy(ref[1]).view(torch.bfloat16).float().numpy()
+        want, _ = oracle.decode_paged(f64(q), kf, vf, model.block_table(), lens, P)
+    check_close(out, want, "bf16", "decode over shared and copied pages")
