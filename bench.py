@@ -208,6 +208,27 @@ def bench_layered(w: wl.DecodeWorkload, steps: int, warmup: int) -> dict:
                               frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
 
 
+PAGE_COPY = "page_copy_512_pages_p256_hkv8_d128_bf16"
+
+
+def bench_page_copy(steps: int, warmup: int) -> dict:
+    """kv_cache_copy_pages (the device half of copy-on-write) over 512 page
+    pairs of 256 tokens x 8 KV heads x 128 dims, bf16: each copy reads and
+    writes one K and one V page (2 x 512 KiB)."""
+    dev = torch.device("cuda")
+    n, P, hkv, d = 512, 256, 8, 128
+    shape = (2 * n, P, hkv, d)
+    cache = ops.KVCache(torch.randn(shape, device=dev).to(torch.bfloat16), torch.randn(shape, device=dev).to(torch.bfloat16))
+    perm = torch.randperm(2 * n, generator=torch.Generator().manual_seed(9)).to(torch.int32)
+    src, dst = perm[:n].to(dev), perm[n:].to(dev)
+    ms = _time_loop(lambda: ops.kv_cache_copy_pages(cache, src, dst), steps, warmup)
+    nbytes = 2 * 2 * n * P * hkv * d * 2     # K and V, read and written
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(workload=PAGE_COPY, ms_copy_kernel=ms, bytes=nbytes,
+                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                              frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+
+
 def cpu_baseline(w: wl.PrefillWorkload, budget_s: float = 15.0) -> dict:
     """The CPU oracle (float64 numpy) on a bounded sample of the prefill
     workload: the whole prompt's append, then as many heads of the causal
@@ -271,6 +292,9 @@ def main() -> int:
         return 0
     ops.load_library()
 
+    if args.workload == PAGE_COPY:
+        print(json.dumps(bench_page_copy(args.steps, args.warmup)), flush=True)
+        return 0
     if args.workload:
         w = wl.WORKLOADS[args.workload]
         if isinstance(w, wl.PrefillWorkload):
