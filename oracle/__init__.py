@@ -28,6 +28,7 @@ from .attention import (
     decode_layered,
     append_pages,
 )
+from .backward import attention_backward_paged
 from .quant import quantize_int8_pages, dequantize_int8_pages, append_int8_pages
 from .counts import visible_pairs, attention_flops, kv_read_bytes, kv_bytes_per_token
 from .twins import brute_force_attention, online_softmax_attention, split_partials, merge_partials
@@ -36,5 +37,5 @@ __all__ = [
     "gather_sequence", "dequantize_pool", "visible_mask", "attention_paged", "decode_paged", "decode_layered",
     "append_pages", "quantize_int8_pages", "dequantize_int8_pages", "visible_pairs",
     "attention_flops", "kv_read_bytes", "kv_bytes_per_token", "brute_force_attention",
-    "online_softmax_attention", "split_partials", "merge_partials",
+    "online_softmax_attention", "split_partials", "merge_partials", "attention_backward_paged",
 ]

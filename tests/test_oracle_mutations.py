@@ -8,6 +8,7 @@ import types
 import pytest
 
 import oracle
+import test_oracle_backward as bpins
 import test_oracle_layered as lpins
 import test_oracle_pages as ppins
 import test_oracle_pins as pins
@@ -66,6 +67,16 @@ PAGES_MUTANTS = [
 ]
 
 
+BACKWARD_MUTANTS = [
+    ("ds = p * (dp - (doh * o).sum(axis=1)[:, None])", "ds = p * dp"),           # softmax Jacobian term dropped
+    ("dq[q0:q1, h, :] = scale * (ds @ kh)", "dq[q0:q1, h, :] = ds @ kh"),         # scale dropped in dQ
+    ("dk[:, g, :] += scale * (ds.T @ qh)", "dk[:, g, :] = scale * (ds.T @ qh)"),  # GQA heads not summed
+    ("dv[:, g, :] += p.T @ doh", "dv[:, g, :] += p.T @ doh[::-1]"),              # rows of dO misaligned
+    ("dp = doh @ vh.T", "dp = doh @ kh.T"),                                     # dP from K instead of V
+    ("g = h // group", "g = h % hkv"),                                          # wrong GQA head map
+]
+
+
 def _load_mutant(filename, old, new):
     src = open(os.path.join(ORACLE_DIR, filename)).read()
     assert src.count(old) >= 1, f"mutation anchor not found: {old}"
@@ -114,12 +125,20 @@ def _pages_battery():
     ppins.test_copy_pages_is_a_page_copy()
 
 
+def _backward_battery():
+    for case in bpins.CASES:
+        bpins.test_backward_matches_torch_autograd(case)
+    bpins.test_gqa_gradient_is_the_sum_over_repeated_heads()
+    bpins.test_keys_no_query_sees_get_zero_gradient()
+
+
 def test_battery_passes_on_the_real_oracle():
     _attention_battery()
     _quant_battery()
     _append_battery()
     _layered_battery()
     _pages_battery()
+    _backward_battery()
 
 
 @pytest.mark.parametrize("old,new", ATTENTION_MUTANTS)
@@ -163,3 +182,16 @@ def test_pages_mutant_is_caught(monkeypatch, old, new):
     monkeypatch.setattr(pages, "copy_pages", mut.copy_pages)
     with pytest.raises((AssertionError, ValueError, IndexError, TypeError)):
         _pages_battery()
+
+
+@pytest.mark.parametrize("old,new", BACKWARD_MUTANTS)
+def test_backward_mutant_is_caught(monkeypatch, old, new):
+    from oracle import backward
+    src = open(os.path.join(ORACLE_DIR, "backward.py")).read()
+    assert src.count(old) == 1, old
+    src = src.replace(old, new).replace("from .attention import", "from oracle.attention import")
+    mod = types.ModuleType("oracle_mutant_backward")
+    exec(compile(src, "backward.py (mutant)", "exec"), mod.__dict__)
+    monkeypatch.setattr(backward, "attention_backward_paged", mod.attention_backward_paged)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        _backward_battery()
