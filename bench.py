@@ -209,6 +209,40 @@ def bench_layered(w: wl.DecodeWorkload, steps: int, warmup: int) -> dict:
 
 
 PAGE_COPY = "page_copy_512_pages_p256_hkv8_d128_bf16"
+BACKWARD = "backward_causal_L2048_h32_d128_p256_bf16"
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector: 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (dual issue) x 2.4 GHz
+
+
+def bench_backward(steps: int, warmup: int) -> dict:
+    """attn_backward_paged on the L=2048 causal prefill shape (32 heads, D=128,
+    bf16, pages of 256): forward once for out / lse, then time the backward.
+    Algorithmic FLOPs: the five products of the gradient chain (recompute
+    q.K^T, dO.V^T, P^T.dO, dS^T.q, dS.K), 2.5x the forward's 4*D per pair."""
+    w = wl.LLAMA7B_PREFILL
+    dev = torch.device("cuda")
+    inp = wl.prefill_inputs(w)
+    shape = (inp["num_pages"], w.page_size, w.num_kv_heads, w.head_dim)
+    cache = ops.KVCache(torch.zeros(shape, dtype=torch.bfloat16, device=dev),
+                        torch.zeros(shape, dtype=torch.bfloat16, device=dev))
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    bt, cu, ctx, start = (inp[n].to(dev) for n in ("block_table", "cu_q", "ctx_lens", "start_pos"))
+    L = max(w.seq_lens)
+    ops.kv_cache_append(cache, k, v, bt, start, cu, max_new=L)
+    out, lse = ops.attn_prefill_paged(q, cu, cache, bt, ctx, max_q_len=L, return_lse=True)
+    d_out = wl.normal(tuple(q.shape), "bf16", w.seed, wl.STREAM_KNEW).to(dev)
+    dk = torch.zeros(shape, dtype=torch.float32, device=dev)
+    dv = torch.zeros(shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(ops.load_library().attn_backward_workspace_bytes(q.shape[0], w.num_q_heads), dtype=torch.uint8,
+                     device=dev)
+    fn = lambda: ops.attn_backward_paged(q, cu, cache, bt, ctx, out, lse, d_out, max_q_len=L, max_ctx=L, dk=dk, dv=dv,
+                                         workspace=ws)
+    ms = _time_loop(fn, steps, warmup)
+    pairs = sum(causal_pairs(n, w.window_left) for n in w.seq_lens)
+    flops = 10 * w.head_dim * w.num_q_heads * pairs
+    tf = flops / (ms * 1e-3) / 1e12
+    return dict(workload=BACKWARD, ms_backward_kernels=ms, flops=flops, tflops=tf,
+                roofline=dict(bound="alu", achieved=round(tf, 2), peak=PEAK_FP32_VALU_TFLOPS, unit="TFLOP/s",
+                              frac=round(tf / PEAK_FP32_VALU_TFLOPS, 4), traffic=None))
 
 
 def bench_page_copy(steps: int, warmup: int) -> dict:
@@ -292,6 +326,9 @@ def main() -> int:
         return 0
     ops.load_library()
 
+    if args.workload == BACKWARD:
+        print(json.dumps(bench_backward(args.steps, args.warmup)), flush=True)
+        return 0
     if args.workload == PAGE_COPY:
         print(json.dumps(bench_page_copy(args.steps, args.warmup)), flush=True)
         return 0

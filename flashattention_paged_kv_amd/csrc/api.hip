@@ -260,6 +260,63 @@ pa_status kv_cache_copy_pages(const pa_kv_cache *cache, const int32_t *src_pages
                     "kv_cache_copy_pages launch");
 }
 
+size_t attn_backward_workspace_bytes(int32_t total_q, int32_t num_q_heads) {
+  if (total_q < 0 || num_q_heads <= 0) return 0;
+  return (size_t)total_q * num_q_heads * sizeof(float);
+}
+
+pa_status attn_backward_paged(const void *q, const int32_t *cu_q, const pa_kv_cache *cache, const int32_t *block_table,
+                              int32_t max_pages_per_seq, const int32_t *ctx_lens, int32_t batch, int32_t total_q,
+                              int32_t max_q_len, int32_t max_ctx, int32_t num_q_heads, float softmax_scale,
+                              int32_t causal, int32_t window_left, const void *out, const float *lse,
+                              const void *d_out, float *dq, float *dk_pages, float *dv_pages, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  pa_status st = check_cache(cache, false);
+  if (st != PA_OK) return st;
+  if (cache->dtype == PA_I8) return fail(PA_ERR_UNSUPPORTED, "the backward pass takes bf16 or fp32 caches");
+  if (batch < 0 || total_q < 0 || max_q_len < 0 || max_ctx < 0)
+    return fail(PA_ERR_INVALID_ARG, "batch, total_q, max_q_len and max_ctx must be >= 0");
+  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, cache->num_kv_heads);
+  if ((st = check_scale(softmax_scale)) != PA_OK) return st;
+  if (causal != 0 && causal != 1) return fail(PA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (batch == 0 || total_q == 0 || max_q_len == 0) return ok();
+  if (q == nullptr || cu_q == nullptr || block_table == nullptr || ctx_lens == nullptr || out == nullptr ||
+      lse == nullptr || d_out == nullptr || dq == nullptr || dk_pages == nullptr || dv_pages == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (max_pages_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq must be > 0");
+  if (max_q_len > 65535 * 64 || batch > 65535) return fail(PA_ERR_INVALID_ARG, "batch or max_q_len too large");
+  const size_t need = attn_backward_workspace_bytes(total_q, num_q_heads);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "backward needs %zu workspace bytes (got %zu)", need, workspace_bytes);
+  pa::BackwardArgs a;
+  a.q = q;
+  a.cu_q = cu_q;
+  a.c = view_of(cache);
+  a.block_table = block_table;
+  a.max_pages = max_pages_per_seq;
+  a.ctx_lens = ctx_lens;
+  a.batch = batch;
+  a.max_q_len = max_q_len;
+  a.max_ctx = max_ctx;
+  a.total_q = total_q;
+  a.num_q_heads = num_q_heads;
+  a.group = num_q_heads / cache->num_kv_heads;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.causal = causal;
+  a.window_left = window_left < 0 ? -1 : window_left;
+  a.out = out;
+  a.lse = lse;
+  a.d_out = d_out;
+  a.dq = dq;
+  a.dk = dk_pages;
+  a.dv = dv_pages;
+  a.delta = (float *)workspace;
+  return hip_status(pa::launch_backward(a, (hipStream_t)stream), "attn_backward_paged launch");
+}
+
 size_t attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t max_pages_per_seq, int32_t page_size) {
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_pages_per_seq <= 0 ||

@@ -107,6 +107,34 @@ struct DecodeArgs {
   int hpw;             // KV heads per split workgroup; slots = batch * Hkv / hpw + nwg, hpw heads each
 };
 
+// Backward pass: gradients of the attention of ragged query rows against a
+// paged cache (bf16 or fp32), fp32 outputs.
+struct BackwardArgs {
+  const void *q;             // [total_q, num_q_heads, head_dim], cache element type
+  const int32_t *cu_q;
+  CacheView c;
+  const int32_t *block_table;
+  int max_pages;
+  const int32_t *ctx_lens;
+  int batch;
+  int max_q_len;
+  int max_ctx;
+  int total_q;
+  int num_q_heads;
+  int group;
+  float scale;
+  float scale_log2;
+  int causal;
+  int window_left;
+  const void *out;           // forward output O, like q
+  const float *lse;          // forward log-sum-exp (natural log) [total_q, num_q_heads]
+  const void *d_out;         // upstream gradient dO, like q
+  float *dq;                 // [total_q, num_q_heads, head_dim]
+  float *dk;                 // [num_pages, page_size, num_kv_heads, head_dim]
+  float *dv;
+  float *delta;              // workspace [total_q, num_q_heads]: dO . O
+};
+
 // Decode grid size (workgroups) on the current device, used by both the
 // workspace query and the call.
 int decode_grid_size();
@@ -127,6 +155,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 // caches may differ in dtype and page size), then one merge of both.
 hipError_t launch_decode_layered(const DecodeArgs &a, const DecodeArgs &a2, hipStream_t s);
 hipError_t launch_append_i8(const AppendI8Args &a, hipStream_t s);
+hipError_t launch_backward(const BackwardArgs &a, hipStream_t s);
 // Copy whole pages src[i] -> dst[i] (K, V and, when given, their scales).
 hipError_t launch_copy_pages(void *k, void *v, float *k_scales, float *v_scales, int num_kv_heads,
                              const int32_t *src, const int32_t *dst, int n, size_t page_bytes, hipStream_t s);

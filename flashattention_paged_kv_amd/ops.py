@@ -49,7 +49,7 @@ _lib = None
 
 EXPORTED = ("kv_cache_append", "kv_pages_quantize_int8", "attn_prefill_paged", "attn_decode_workspace_bytes",
             "attn_decode_paged", "attn_decode_layered_workspace_bytes", "attn_decode_paged_layered",
-            "kv_cache_copy_pages", "pa_pool_create", "pa_pool_destroy", "pa_pool_extend", "pa_pool_fork",
+            "kv_cache_copy_pages", "attn_backward_workspace_bytes", "attn_backward_paged", "pa_pool_create", "pa_pool_destroy", "pa_pool_extend", "pa_pool_fork",
             "pa_pool_release", "pa_pool_export", "pa_pool_free_pages", "pa_pool_refcount",
             "pa_status_string", "pa_last_error_detail", "pa_abi_version")
 
@@ -74,6 +74,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode_layered_workspace_bytes.restype = SZ
     lib.attn_decode_paged_layered.argtypes = [P, CP, P, I32, P, CP, P, I32, P, I32, I32, F32, P, P, P, SZ, P]
     lib.kv_cache_copy_pages.argtypes = [CP, P, P, I32, P]
+    lib.attn_backward_workspace_bytes.argtypes = [I32, I32]
+    lib.attn_backward_workspace_bytes.restype = SZ
+    lib.attn_backward_paged.argtypes = [P, P, CP, P, I32, P, I32, I32, I32, I32, I32, F32, I32, I32, P, P, P, P, P, P,
+                                        P, SZ, P]
     PI = ctypes.POINTER(I32)
     lib.pa_pool_create.argtypes = [I32, I32, I32, I32, ctypes.POINTER(P)]
     lib.pa_pool_destroy.argtypes = [P]
@@ -87,7 +91,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("pa_pool_free_pages", "pa_pool_refcount"):
         getattr(lib, name).restype = I32
     for name in ("kv_cache_append", "kv_pages_quantize_int8", "attn_prefill_paged", "attn_decode_paged",
-                 "attn_decode_paged_layered", "kv_cache_copy_pages", "pa_pool_create", "pa_pool_extend",
+                 "attn_decode_paged_layered", "kv_cache_copy_pages", "attn_backward_paged", "pa_pool_create",
+                 "pa_pool_extend",
                  "pa_pool_fork", "pa_pool_release", "pa_pool_export"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
@@ -351,3 +356,40 @@ class PagePool:
 
     def refcount(self, page: int) -> int:
         return int(self._lib.pa_pool_refcount(self._h, page))
+
+
+def attn_backward_paged(q: torch.Tensor, cu_q: torch.Tensor, cache: KVCache, block_table: torch.Tensor,
+                        ctx_lens: torch.Tensor, out: torch.Tensor, lse: torch.Tensor, d_out: torch.Tensor,
+                        max_q_len: Optional[int] = None, max_ctx: Optional[int] = None,
+                        softmax_scale: Optional[float] = None, causal: bool = True, window_left: int = -1,
+                        dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk_pages, dv_pages), fp32, of attn_prefill_paged's output
+    for upstream gradient d_out; out and lse are the forward's.  dk / dv
+    (fp32, pool-shaped) are allocated zero-filled if not given; only the slots
+    of cached positions are written."""
+    lib = load_library()
+    cs = cache._struct()
+    for t, name in ((q, "q"), (out, "out"), (d_out, "d_out")):
+        _dev(t, name, cache.dtype)
+    _dev(lse, "lse", torch.float32)
+    for t, name in ((cu_q, "cu_q"), (block_table, "block_table"), (ctx_lens, "ctx_lens")):
+        _dev(t, name, torch.int32)
+    total_q, hq, d = q.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    max_q_len = total_q if max_q_len is None else max_q_len
+    max_ctx = int(ctx_lens.max().item()) if max_ctx is None else max_ctx
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    shape = tuple(cache.k_pages.shape)
+    dk = torch.zeros(shape, dtype=torch.float32, device=q.device) if dk is None else _dev(dk, "dk", torch.float32)
+    dv = torch.zeros(shape, dtype=torch.float32, device=q.device) if dv is None else _dev(dv, "dv", torch.float32)
+    if workspace is None:
+        workspace = torch.empty(max(lib.attn_backward_workspace_bytes(total_q, hq), 1), dtype=torch.uint8,
+                                device=q.device)
+    _dev(workspace, "workspace")
+    _check(lib.attn_backward_paged(_ptr(q), _ptr(cu_q), ctypes.byref(cs), _ptr(block_table), block_table.shape[1],
+                                   _ptr(ctx_lens), ctx_lens.shape[0], total_q, max_q_len, max_ctx, hq, scale,
+                                   int(bool(causal)), int(window_left), _ptr(out), _ptr(lse), _ptr(d_out), _ptr(dq),
+                                   _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream()))
+    return dq, dk, dv

@@ -216,6 +216,37 @@ pa_status attn_decode_paged_layered(const void *q, const pa_kv_cache *cache_hi, 
                                     int32_t batch, int32_t num_q_heads, float softmax_scale, void *out,
                                     float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
+/* attn_backward_workspace_bytes - HOST function: workspace bytes of
+ * attn_backward_paged (total_q * num_q_heads floats; 0 on bad input). */
+size_t attn_backward_workspace_bytes(int32_t total_q, int32_t num_q_heads);
+
+/* attn_backward_paged - gradients of attn_prefill_paged's output with
+ * respect to q and to the cached K and V, from the forward's out and lse.
+ * Source: recomputation in the backward pass ("大模型推理优化：KV Cache与
+ * FlashAttention实战" section 3.1; "Flash Attention与Paged KV Cache优化大模型
+ * 计算效率" section 2.1): the probabilities are rebuilt from q, K and lse
+ * instead of being stored, and differentiated through softmax and the two
+ * products.  Same arguments, masks and GQA map as attn_prefill_paged, plus:
+ *   total_q, max_ctx : host ints, cu_q[batch] and max over b of ctx_lens[b]
+ *   out, lse         : the forward output and log-sum-exp (natural log)
+ *   d_out            : [total_q, num_q_heads, head_dim] upstream gradient
+ *   q, out, d_out    : bf16 for a PA_BF16 cache, fp32 for PA_F32
+ *   dq               : fp32 [total_q, num_q_heads, head_dim]
+ *   dk_pages, dv_pages: fp32 [num_pages, page_size, num_kv_heads, head_dim];
+ *                      the slot of every cached position 0..ctx_lens[b]-1 of
+ *                      every sequence is written (gradients of the GQA
+ *                      group's query heads summed), other slots untouched.
+ *                      Sequences must not share physical pages here.
+ *   workspace        : at least attn_backward_workspace_bytes(...) bytes
+ * Arithmetic is fp32 on the vector ALUs.  PA_ERR_UNSUPPORTED for an int8
+ * cache. */
+pa_status attn_backward_paged(const void *q, const int32_t *cu_q, const pa_kv_cache *cache, const int32_t *block_table,
+                              int32_t max_pages_per_seq, const int32_t *ctx_lens, int32_t batch, int32_t total_q,
+                              int32_t max_q_len, int32_t max_ctx, int32_t num_q_heads, float softmax_scale,
+                              int32_t causal, int32_t window_left, const void *out, const float *lse,
+                              const void *d_out, float *dq, float *dk_pages, float *dv_pages, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 /* kv_cache_copy_pages - copy whole pages src_pages[i] -> dst_pages[i]
  * (K, V and, for PA_I8, the pages' scales): the device half of a page pool's
  * copy-on-write (below).

@@ -188,3 +188,34 @@ def test_layered_decode_workspace_and_empty_batch():
     # one byte short of the query for these sizes is rejected (no work enqueued)
     need = lib.attn_decode_layered_workspace_bytes(2, 4, 2, 128)
     assert _layered(_cache(), _i8_cache(), batch=2, hq=4, ws_bytes=need - 1) == 4
+
+
+def _backward(cache, **kw):
+    lib = ops.load_library()
+    a = dict(q=FAKE, cu_q=FAKE, block_table=FAKE, max_pages=4, ctx=FAKE, batch=1, total_q=8, max_q_len=8,
+             max_ctx=8, hq=4, scale=0.1, causal=1, window=-1, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE,
+             dv=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.attn_backward_paged(a["q"], a["cu_q"], ctypes.byref(cache), a["block_table"], a["max_pages"],
+                                   a["ctx"], a["batch"], a["total_q"], a["max_q_len"], a["max_ctx"], a["hq"],
+                                   a["scale"], a["causal"], a["window"], a["out"], a["lse"], a["dout"], a["dq"],
+                                   a["dk"], a["dv"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("cache_kw,kw,status", [
+    (dict(dtype=ops.PA_I8, k_scales=0x3000, v_scales=0x4000), dict(), 2),
+    (dict(), dict(hq=3), 1), (dict(), dict(scale=0.0), 1), (dict(), dict(causal=3), 1),
+    (dict(), dict(dk=None), 1), (dict(), dict(lse=None), 1), (dict(), dict(ws=None), 4),
+    (dict(), dict(ws_bytes=8 * 4 * 4 - 1), 4), (dict(), dict(batch=-1), 1), (dict(), dict(max_pages=0), 1),
+])
+def test_backward_rejects_bad_args(cache_kw, kw, status):
+    assert _backward(_cache(**cache_kw), **kw) == status
+    assert _detail() != ""
+
+
+def test_backward_empty_and_workspace_query():
+    lib = ops.load_library()
+    assert lib.attn_backward_workspace_bytes(8, 4) == 8 * 4 * 4
+    assert lib.attn_backward_workspace_bytes(8, 0) == 0
+    assert _backward(_cache(), batch=0, q=None) == 0
+    assert _backward(_cache(), total_q=0, q=None) == 0

@@ -478,3 +478,63 @@ def test_page_pool_prefix_sharing_with_copy_on_write(int8):
         vf = torch.from_numpy(ref[1]).view(torch.bfloat16).float().numpy()
         want, _ = oracle.decode_paged(f64(q), kf, vf, model.block_table(), lens, P)
     check_close(out, want, "bf16", "decode over shared and copied pages")
+
+
+BACKWARD_CASES = [
+    # name, q_lens, ctx_lens, hq, hkv, d, P, dtype, causal, window
+    ("bf16_chunked_gqa", (300, 77), (300, 200), 8, 2, 128, 16, "bf16", True, -1),
+    ("bf16_window64", (257,), (257,), 4, 4, 128, 64, "bf16", True, 64),
+    ("bf16_unmasked_d64", (130,), (130,), 4, 1, 64, 32, "bf16", False, -1),
+    ("f32_d64", (100, 33), (100, 60), 4, 2, 64, 16, "f32", True, -1),
+]
+
+
+@pytest.mark.parametrize("case", BACKWARD_CASES, ids=lambda c: c[0])
+def test_backward_matches_oracle(case):
+    """Gradients of the paged attention: the GPU forward's out and lse feed
+    the GPU backward; the oracle differentiates the definition in float64
+    from q, K, V and dO alone.  Gradient pages start as NaN, so every cached
+    position must be written and no other slot touched."""
+    name, q_lens, ctx, hq, hkv, d, P, dtype, causal, window = case
+    say(f"backward {name}")
+    seed = 91
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    pages = [-(-c // P) for c in ctx]
+    n_pages = sum(pages) + 2
+    perm = wl.rng(seed, wl.STREAM_PERM).permutation(n_pages).astype(np.int32)
+    bt = np.zeros((len(ctx), max(pages)), dtype=np.int32)
+    at = 0
+    for b, n in enumerate(pages):
+        bt[b, :n] = perm[at:at + n]
+        at += n
+    kpool = wl.normal((n_pages, P, hkv, d), dtype, seed, wl.STREAM_K)
+    vpool = wl.normal((n_pages, P, hkv, d), dtype, seed, wl.STREAM_V)
+    q = wl.normal((int(cu[-1]), hq, d), dtype, seed, wl.STREAM_Q)
+    dout = wl.normal((int(cu[-1]), hq, d), dtype, seed, wl.STREAM_KNEW)
+    i32 = lambda x: torch.tensor(np.asarray(x, dtype=np.int32)).cuda()
+    cache = ops.KVCache(kpool.cuda(), vpool.cuda())
+    out, lse = ops.attn_prefill_paged(q.cuda(), i32(cu), cache, i32(bt), i32(ctx), max_q_len=max(q_lens),
+                                      causal=causal, window_left=window, return_lse=True)
+    dk0 = torch.full((n_pages, P, hkv, d), float("nan"), device="cuda")
+    dv0 = torch.full((n_pages, P, hkv, d), float("nan"), device="cuda")
+    dq, dk, dv = ops.attn_backward_paged(q.cuda(), i32(cu), cache, i32(bt), i32(ctx), out, lse, dout.cuda(),
+                                         max_q_len=max(q_lens), max_ctx=max(ctx), causal=causal,
+                                         window_left=window, dk=dk0, dv=dv0)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle.attention_backward_paged(f64(q), cu, f64(kpool), f64(vpool), bt, ctx, P, f64(dout),
+                                                    causal=causal, window_left=window)
+    used = np.zeros((n_pages, P), dtype=bool)
+    for b, c in enumerate(ctx):
+        for t in range(c):
+            used[bt[b, t // P], t % P] = True
+    gk, gv = dk.cpu().numpy(), dv.cpu().numpy()
+    assert np.isfinite(gk[used]).all() and np.isfinite(gv[used]).all(), "a cached position was not written"
+    assert np.isnan(gk[~used]).all() and np.isnan(gv[~used]).all(), "a slot outside the cache was written"
+    # bf16: O (rounded to bf16 by the forward) enters through D = dO . O, and
+    # q, K, V, dO are bf16; errors scale with the gradient's own size.
+    tol_max, tol_mean = (1e-4, 1e-5) if dtype == "f32" else (2e-2, 2e-3)
+    for what, got, ref in (("dq", dq.cpu().numpy(), rdq), ("dk", gk[used], rdk[used]), ("dv", gv[used], rdv[used])):
+        scale = max(1.0, float(np.abs(ref).max()))
+        err = np.abs(got.astype(np.float64) - ref)
+        say(f"  {what}: max|ref|={np.abs(ref).max():.3e} max|d|={err.max():.3e} mean|d|={err.mean():.3e}")
+        assert err.max() <= tol_max * scale and err.mean() <= tol_mean * scale, what
