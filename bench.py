@@ -240,9 +240,11 @@ def bench_backward(steps: int, warmup: int) -> dict:
     pairs = sum(causal_pairs(n, w.window_left) for n in w.seq_lens)
     flops = 10 * w.head_dim * w.num_q_heads * pairs
     tf = flops / (ms * 1e-3) / 1e12
+    # bf16 caches run the dQ and dK/dV products on MFMA (fp32 caches on the
+    # vector ALUs, whose peak is PEAK_FP32_VALU_TFLOPS).
     return dict(workload=BACKWARD, ms_backward_kernels=ms, flops=flops, tflops=tf,
-                roofline=dict(bound="alu", achieved=round(tf, 2), peak=PEAK_FP32_VALU_TFLOPS, unit="TFLOP/s",
-                              frac=round(tf / PEAK_FP32_VALU_TFLOPS, 4), traffic=None))
+                roofline=dict(bound="mfma", achieved=round(tf, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                              frac=round(tf / PEAK_BF16_TFLOPS, 4), traffic=None))
 
 
 def bench_page_copy(steps: int, warmup: int) -> dict:

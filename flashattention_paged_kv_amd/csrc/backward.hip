@@ -11,15 +11,19 @@
 //   dQ    = s sum_j ds_j k_j,   dK_j += s ds_j q,
 // with the masks, GQA head map and page layout of the forward pass.
 //
-// Three kernels, all fp32 arithmetic on the vector ALUs:
+// Three kernels:
 //   delta_kernel : D = dO . O per (row, head);
-//   dq_kernel    : one wave per (query row, head); keys one per lane for the
-//                  dot products, then the wave accumulates dQ with lanes over
-//                  head dims;
-//   dkv_kernel   : one wave per (key position, KV head); query rows (of all
-//                  G query heads of the group) one per lane, then dK / dV
-//                  accumulated with lanes over head dims and written once, so
-//                  no atomics and no zero fill are needed.
+//   dQ           : bf16 caches: dq_mfma_kernel (128 query rows per workgroup,
+//                  K/V tiles staged in LDS, products on MFMA); fp32 caches:
+//                  dq_kernel, one wave per (query row, head) on the vector
+//                  ALUs;
+//   dK / dV      : bf16: dkv_mfma_kernel (128 keys per workgroup, Q / dO
+//                  tiles staged in LDS); fp32: dkv_kernel, one wave per (key
+//                  position, KV head).  Each key's gradient is accumulated in
+//                  one workgroup over all query rows and heads of its group
+//                  and written once, so no atomics and no zero fill are
+//                  needed.
+// dS (like P in the forward pass) is rounded to bf16 before its MFMA.
 #include <math.h>
 
 #include "pa_device.h"
@@ -207,14 +211,270 @@ __global__ __launch_bounds__(64) void dkv_kernel(BackwardArgs a) {
   }
 }
 
+// dQ on MFMA (bf16 caches).  A workgroup of 4 waves takes 128 query rows
+// of one (sequence, head), 32 per wave; per 64-key tile, staged in LDS:
+//   S^T  = K . Q^T   and  dP^T = V . dO^T  (v_mfma_f32_32x32x16_bf16, keys on
+//                                            M, the wave's rows on N),
+//   P^T  = exp(s S^T - lse),  dS^T = P^T (dP^T - D)  (rounded to bf16),
+//   dQ^T += K^T . dS^T  (K^T read transposed from the staged K rows).
+constexpr int kBwRows = 128;
+constexpr int kBwKeys = 64;
+
+template <int D>
+struct BwCfg {
+  static constexpr int kKRow = 2 * D + 16;   // staged K row bytes
+  static constexpr int kVRow = 2 * D + 16;   // staged V row bytes
+  static constexpr int kCpr = D / 8;         // 16-byte chunks per row
+  static constexpr int kNs = D / 16;         // k-steps over the head dim
+  static constexpr int kNdb = D / 32;        // 32-dim output blocks
+  static constexpr int kLoads = kBwKeys * kCpr / 256;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void dq_mfma_kernel(BackwardArgs a) {
+  using C = BwCfg<D>;
+  __shared__ __align__(16) unsigned char ksm[kBwKeys * C::kKRow];
+  __shared__ __align__(16) unsigned char vsm[kBwKeys * C::kVRow];
+  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int q0 = a.cu_q[b];
+  const int q_len = a.cu_q[b + 1] - q0;
+  if (qt * kBwRows >= q_len) return;  // uniform
+  const int ctx = a.ctx_lens[b];
+  const int off = ctx - q_len;
+  const int hk = h / a.group;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, g = lane >> 5, gam = lane >> 4, tp = lane & 15;
+  const int row = qt * kBwRows + w * 32 + col;
+  const int rowc = min(row, q_len - 1);
+  const int pos = off + row;
+  const size_t qidx = (size_t)(q0 + rowc) * a.num_q_heads + h;
+  const __bf16 *qp = (const __bf16 *)a.q + qidx * D;
+  const __bf16 *dop = (const __bf16 *)a.d_out + qidx * D;
+  bf16x8 bq[C::kNs], bdo[C::kNs];
+#pragma unroll
+  for (int s = 0; s < C::kNs; ++s) {
+    bq[s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s + 8 * g);
+    bdo[s] = *reinterpret_cast<const bf16x8 *>(dop + 16 * s + 8 * g);
+  }
+  const float lse = a.lse[qidx];
+  const float lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;  // no visible key: every p = 0
+  const float dlt = a.delta[qidx];
+  // Visible keys of the tile's rows: [k_lo, k_hi].
+  const int p_first = off + qt * kBwRows;
+  const int p_last = off + min(qt * kBwRows + kBwRows - 1, q_len - 1);
+  const int k_lo = a.window_left >= 0 ? max(0, p_first - a.window_left) : 0;
+  const int k_hi = a.causal ? min(p_last, ctx - 1) : ctx - 1;
+  // This lane's row sees keys [lo_r, hi_r].
+  const int hi_r = a.causal ? min(pos, ctx - 1) : ctx - 1;
+  const int lo_r = a.window_left >= 0 ? pos - a.window_left : 0;
+  f32x16 acc[C::kNdb];
+#pragma unroll
+  for (int db = 0; db < C::kNdb; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  const size_t row_elems = (size_t)a.c.num_kv_heads * D;
+  const __bf16 *kpool = (const __bf16 *)a.c.k + (size_t)hk * D;
+  const __bf16 *vpool = (const __bf16 *)a.c.v + (size_t)hk * D;
+  const int lrow = tid / C::kCpr, lch = tid % C::kCpr;
+  constexpr int kRowsPerPass = 256 / C::kCpr;
+  for (int kt = k_lo / kBwKeys; kt * kBwKeys <= k_hi; ++kt) {
+    const int key0 = kt * kBwKeys;
+    // Stage the tile (rows past the context read the last valid row).
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+      const int r = lrow + i * kRowsPerPass;
+      const int key = min(key0 + r, ctx - 1);
+      const int page = a.block_table[(size_t)b * a.max_pages + (key >> a.c.log2_page)];
+      const size_t ro = ((size_t)page * a.c.page_size + (key & (a.c.page_size - 1))) * row_elems + lch * 8;
+      *reinterpret_cast<uint4 *>(ksm + r * C::kKRow + lch * 16) = *reinterpret_cast<const uint4 *>(kpool + ro);
+      *reinterpret_cast<uint4 *>(vsm + r * C::kVRow + lch * 16) = *reinterpret_cast<const uint4 *>(vpool + ro);
+    }
+    __syncthreads();
+    f32x16 sacc[2], dpacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = dpacc[kb][i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < C::kNs; ++s) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ksm + (kb * 32 + col) * C::kKRow + (16 * s + 8 * g) * 2);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vsm + (kb * 32 + col) * C::kVRow + (16 * s + 8 * g) * 2);
+        sacc[kb] = mfma32(kf, bq[s], sacc[kb]);
+        dpacc[kb] = mfma32(vf, bdo[s], dpacc[kb]);
+      }
+    }
+    // dS^T = P^T (dP^T - D), masked; element i of block kb is key
+    // key0 + kb*32 + (i/4)*8 + g*4 + i%4 of this lane's row.
+    bf16x8 bds[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = key0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+        const bool vis = key >= lo_r && key <= hi_r;
+        const float p = vis ? fast_exp2(sacc[kb][i] * a.scale_log2 - lse2) : 0.f;
+        bds[2 * kb + (i >> 3)][i & 7] = (__bf16)(p * (dpacc[kb][i] - dlt));
+      }
+    // dQ^T += K^T . dS^T over four 16-key steps.
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r0 = (t >> 1) * 32 + (t & 1) * 16 + g * 4;
+#pragma unroll
+      for (int db = 0; db < C::kNdb; ++db) {
+        const unsigned char *p1 = ksm + (r0 + (tp >> 2)) * C::kKRow + (db * 32 + 16 * (gam & 1) + 4 * (tp & 3)) * 2;
+        const bf16x8 kt_frag = cat(lds_read_tr16(p1), lds_read_tr16(p1 + 8 * C::kKRow));
+        acc[db] = mfma32(kt_frag, bds[t], acc[db]);
+      }
+    }
+    __syncthreads();  // the tile is restaged next
+  }
+  if (row < q_len) {
+    float *dq = a.dq + ((size_t)(q0 + row) * a.num_q_heads + h) * D;
+#pragma unroll
+    for (int db = 0; db < C::kNdb; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dq[db * 32 + (i >> 2) * 8 + g * 4 + (i & 3)] = acc[db][i] * a.scale;
+  }
+}
+
+// dK / dV on MFMA (bf16 caches).  A workgroup of 4 waves takes 128 keys of
+// one (sequence, KV head), 32 per wave, their K and V rows held as MFMA B
+// operands; for each query head of the GQA group and each 32-row query tile
+// that sees the keys (staged in LDS: Q, dO, lse, D):
+//   S  = Q . K^T  and  dP = dO . V^T   (rows on M, the wave's keys on N),
+//   P  = exp(s S - lse),  dS = P (dP - D)  (rounded to bf16),
+//   dV^T += dO^T . P,   dK^T += Q^T . dS   (Q^T, dO^T read transposed).
+constexpr int kBwKeyTile = 128;
+constexpr int kBwRowTile = 32;
+
+template <int D>
+__global__ __launch_bounds__(256) void dkv_mfma_kernel(BackwardArgs a) {
+  using C = BwCfg<D>;
+  constexpr int kPitch = C::kKRow;
+  __shared__ __align__(16) unsigned char qsm[kBwRowTile * kPitch];
+  __shared__ __align__(16) unsigned char dosm[kBwRowTile * kPitch];
+  __shared__ float lse_s[kBwRowTile], dl_s[kBwRowTile];
+  const int kt = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int ctx = a.ctx_lens[b];
+  if (kt * kBwKeyTile >= ctx) return;  // uniform
+  const int q0 = a.cu_q[b];
+  const int q_len = a.cu_q[b + 1] - q0;
+  const int off = ctx - q_len;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, g = lane >> 5, gam = lane >> 4, tp = lane & 15;
+  const int key = kt * kBwKeyTile + w * 32 + col;  // this lane's key (B-operand column)
+  const int keyc = min(key, ctx - 1);
+  const size_t row_elems = (size_t)a.c.num_kv_heads * D;
+  const int kpage = a.block_table[(size_t)b * a.max_pages + (keyc >> a.c.log2_page)];
+  const size_t krow = ((size_t)kpage * a.c.page_size + (keyc & (a.c.page_size - 1))) * row_elems + (size_t)hk * D;
+  bf16x8 bk[C::kNs], bv[C::kNs];
+#pragma unroll
+  for (int s = 0; s < C::kNs; ++s) {
+    bk[s] = *reinterpret_cast<const bf16x8 *>((const __bf16 *)a.c.k + krow + 16 * s + 8 * g);
+    bv[s] = *reinterpret_cast<const bf16x8 *>((const __bf16 *)a.c.v + krow + 16 * s + 8 * g);
+  }
+  f32x16 dk[C::kNdb], dv[C::kNdb];
+#pragma unroll
+  for (int db = 0; db < C::kNdb; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
+  // Query rows that can see some key of the tile: positions in
+  // [first key, last key + W] (causal), rows = positions - off.
+  const int key_first = kt * kBwKeyTile, key_last = min(kt * kBwKeyTile + kBwKeyTile - 1, ctx - 1);
+  const int r_lo = a.causal ? max(0, key_first - off) : 0;
+  const int r_hi = a.window_left >= 0 ? min(q_len - 1, key_last + a.window_left - off) : q_len - 1;
+  const int lrow = tid / C::kCpr, lch = tid % C::kCpr;
+  constexpr int kRowsPerPass = 256 / C::kCpr;
+  constexpr int kLoads = kBwRowTile * C::kCpr / 256;
+  for (int gi = 0; gi < a.group; ++gi) {
+    const int h = hk * a.group + gi;
+    for (int rt = r_lo - (r_lo % kBwRowTile); rt <= r_hi; rt += kBwRowTile) {
+      // Stage Q, dO (rows past the sequence read its last row), lse and D.
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int r = lrow + i * kRowsPerPass;
+        const size_t idx = (size_t)(q0 + min(rt + r, q_len - 1)) * a.num_q_heads + h;
+        *reinterpret_cast<uint4 *>(qsm + r * kPitch + lch * 16) =
+            *reinterpret_cast<const uint4 *>((const __bf16 *)a.q + idx * D + lch * 8);
+        *reinterpret_cast<uint4 *>(dosm + r * kPitch + lch * 16) =
+            *reinterpret_cast<const uint4 *>((const __bf16 *)a.d_out + idx * D + lch * 8);
+      }
+      if (tid < kBwRowTile) {
+        const int r = rt + tid;
+        const size_t idx = (size_t)(q0 + min(r, q_len - 1)) * a.num_q_heads + h;
+        const float l = a.lse[idx];
+        lse_s[tid] = (r < q_len && l != -INFINITY) ? l * kLog2e : INFINITY;  // INFINITY: p = 0
+        dl_s[tid] = a.delta[idx];
+      }
+      __syncthreads();
+      f32x16 sacc, dpacc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < C::kNs; ++s) {
+        const bf16x8 qf = *reinterpret_cast<const bf16x8 *>(qsm + col * kPitch + (16 * s + 8 * g) * 2);
+        const bf16x8 df = *reinterpret_cast<const bf16x8 *>(dosm + col * kPitch + (16 * s + 8 * g) * 2);
+        sacc = mfma32(qf, bk[s], sacc);
+        dpacc = mfma32(df, bv[s], dpacc);
+      }
+      // Element i is row rt + (i/4)*8 + g*4 + i%4 against this lane's key.
+      bf16x8 bp[2], bds[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rr = (i >> 2) * 8 + g * 4 + (i & 3);
+        const int pos = off + rt + rr;
+        bool vis = key < ctx && rt + rr < q_len;
+        if (a.causal) vis = vis && key <= pos;
+        if (a.window_left >= 0) vis = vis && pos - key <= a.window_left;
+        const float p = vis ? fast_exp2(sacc[i] * a.scale_log2 - lse_s[rr]) : 0.f;
+        bp[i >> 3][i & 7] = (__bf16)p;
+        bds[i >> 3][i & 7] = (__bf16)(p * (dpacc[i] - dl_s[rr]));
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int r0 = t * 16 + g * 4;
+#pragma unroll
+        for (int db = 0; db < C::kNdb; ++db) {
+          const int c = (db * 32 + 16 * (gam & 1) + 4 * (tp & 3)) * 2;
+          const unsigned char *pd = dosm + (r0 + (tp >> 2)) * kPitch + c;
+          const unsigned char *pq = qsm + (r0 + (tp >> 2)) * kPitch + c;
+          dv[db] = mfma32(cat(lds_read_tr16(pd), lds_read_tr16(pd + 8 * kPitch)), bp[t], dv[db]);
+          dk[db] = mfma32(cat(lds_read_tr16(pq), lds_read_tr16(pq + 8 * kPitch)), bds[t], dk[db]);
+        }
+      }
+      __syncthreads();  // the tiles are restaged next
+    }
+  }
+  if (key < ctx) {
+    float *dkr = a.dk + krow;
+    float *dvr = a.dv + krow;
+#pragma unroll
+    for (int db = 0; db < C::kNdb; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int d = db * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+        dkr[d] = dk[db][i] * a.scale;
+        dvr[d] = dv[db][i];
+      }
+  }
+}
+
 template <int D, typename T>
 hipError_t launch_t(const BackwardArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((delta_kernel<D, T>), dim3(a.total_q), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dq_kernel<D, T>), dim3(a.max_q_len, a.num_q_heads, a.batch), dim3(64), 0, s, a);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((dq_mfma_kernel<D>), dim3((a.max_q_len + kBwRows - 1) / kBwRows, a.num_q_heads, a.batch),
+                       dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((dq_kernel<D, T>), dim3(a.max_q_len, a.num_q_heads, a.batch), dim3(64), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((dkv_kernel<D, T>), dim3(a.max_ctx, a.c.num_kv_heads, a.batch), dim3(64), 0, s, a);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((dkv_mfma_kernel<D>), dim3((a.max_ctx + kBwKeyTile - 1) / kBwKeyTile, a.c.num_kv_heads, a.batch),
+                       dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((dkv_kernel<D, T>), dim3(a.max_ctx, a.c.num_kv_heads, a.batch), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
