@@ -222,8 +222,11 @@ constexpr int kBwKeys = 64;
 
 template <int D>
 struct BwCfg {
-  static constexpr int kKRow = 2 * D + 16;   // staged K row bytes
-  static constexpr int kVRow = 2 * D + 16;   // staged V row bytes
+  // Staged rows are read both as 16-byte rows and transposed
+  // (ds_read_b64_tr_b16); a pitch of 2D + 32 bytes keeps both patterns free
+  // of bank conflicts.
+  static constexpr int kKRow = 2 * D + 32;   // staged K (and Q) row bytes
+  static constexpr int kVRow = 2 * D + 32;   // staged V (and dO) row bytes
   static constexpr int kCpr = D / 8;         // 16-byte chunks per row
   static constexpr int kNs = D / 16;         // k-steps over the head dim
   static constexpr int kNdb = D / 32;        // 32-dim output blocks
@@ -231,11 +234,9 @@ struct BwCfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void dq_mfma_kernel(BackwardArgs a) {
+__device__ __forceinline__ void dq_tile(const BackwardArgs &a, int qt, int h, int b, unsigned char *ksm,
+                                        unsigned char *vsm) {
   using C = BwCfg<D>;
-  __shared__ __align__(16) unsigned char ksm[kBwKeys * C::kKRow];
-  __shared__ __align__(16) unsigned char vsm[kBwKeys * C::kVRow];
-  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int q0 = a.cu_q[b];
   const int q_len = a.cu_q[b + 1] - q0;
   if (qt * kBwRows >= q_len) return;  // uniform
@@ -277,19 +278,31 @@ __global__ __launch_bounds__(256) void dq_mfma_kernel(BackwardArgs a) {
   const __bf16 *vpool = (const __bf16 *)a.c.v + (size_t)hk * D;
   const int lrow = tid / C::kCpr, lch = tid % C::kCpr;
   constexpr int kRowsPerPass = 256 / C::kCpr;
-  for (int kt = k_lo / kBwKeys; kt * kBwKeys <= k_hi; ++kt) {
+  // K/V of a tile in registers (rows past the context read the last valid
+  // row), one tile ahead of the one being computed.
+  u32x4 kreg[C::kLoads], vreg[C::kLoads];
+  auto load_tile = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+      const int key = min(kt * kBwKeys + lrow + i * kRowsPerPass, ctx - 1);
+      const int page = a.block_table[(size_t)b * a.max_pages + (key >> a.c.log2_page)];
+      const size_t ro = ((size_t)page * a.c.page_size + (key & (a.c.page_size - 1))) * row_elems + lch * 8;
+      kreg[i] = *reinterpret_cast<const u32x4 *>(kpool + ro);
+      vreg[i] = *reinterpret_cast<const u32x4 *>(vpool + ro);
+    }
+  };
+  const int kt_end = k_hi / kBwKeys;
+  load_tile(k_lo / kBwKeys);
+  for (int kt = k_lo / kBwKeys; kt <= kt_end; ++kt) {
     const int key0 = kt * kBwKeys;
-    // Stage the tile (rows past the context read the last valid row).
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
       const int r = lrow + i * kRowsPerPass;
-      const int key = min(key0 + r, ctx - 1);
-      const int page = a.block_table[(size_t)b * a.max_pages + (key >> a.c.log2_page)];
-      const size_t ro = ((size_t)page * a.c.page_size + (key & (a.c.page_size - 1))) * row_elems + lch * 8;
-      *reinterpret_cast<uint4 *>(ksm + r * C::kKRow + lch * 16) = *reinterpret_cast<const uint4 *>(kpool + ro);
-      *reinterpret_cast<uint4 *>(vsm + r * C::kVRow + lch * 16) = *reinterpret_cast<const uint4 *>(vpool + ro);
+      *reinterpret_cast<u32x4 *>(ksm + r * C::kKRow + lch * 16) = kreg[i];
+      *reinterpret_cast<u32x4 *>(vsm + r * C::kVRow + lch * 16) = vreg[i];
     }
     __syncthreads();
+    load_tile(min(kt + 1, kt_end));  // unconditional: exact wait counts
     f32x16 sacc[2], dpacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -348,13 +361,10 @@ constexpr int kBwKeyTile = 128;
 constexpr int kBwRowTile = 32;
 
 template <int D>
-__global__ __launch_bounds__(256) void dkv_mfma_kernel(BackwardArgs a) {
+__device__ __forceinline__ void dkv_tile(const BackwardArgs &a, int kt, int hk, int b, unsigned char *qsm,
+                                         unsigned char *dosm, float *lse_s, float *dl_s) {
   using C = BwCfg<D>;
   constexpr int kPitch = C::kKRow;
-  __shared__ __align__(16) unsigned char qsm[kBwRowTile * kPitch];
-  __shared__ __align__(16) unsigned char dosm[kBwRowTile * kPitch];
-  __shared__ float lse_s[kBwRowTile], dl_s[kBwRowTile];
-  const int kt = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int ctx = a.ctx_lens[b];
   if (kt * kBwKeyTile >= ctx) return;  // uniform
   const int q0 = a.cu_q[b];
@@ -386,27 +396,44 @@ __global__ __launch_bounds__(256) void dkv_mfma_kernel(BackwardArgs a) {
   const int lrow = tid / C::kCpr, lch = tid % C::kCpr;
   constexpr int kRowsPerPass = 256 / C::kCpr;
   constexpr int kLoads = kBwRowTile * C::kCpr / 256;
-  for (int gi = 0; gi < a.group; ++gi) {
-    const int h = hk * a.group + gi;
-    for (int rt = r_lo - (r_lo % kBwRowTile); rt <= r_hi; rt += kBwRowTile) {
-      // Stage Q, dO (rows past the sequence read its last row), lse and D.
+  // Steps j = (head gi, row tile) pairs; Q, dO, lse, D of a step in
+  // registers (rows past the sequence read its last row), one step ahead.
+  const int rt0 = r_lo - (r_lo % kBwRowTile);
+  const int n_rt = r_hi >= rt0 ? (r_hi - rt0) / kBwRowTile + 1 : 0;
+  const int n_steps = a.group * n_rt;
+  u32x4 qreg[kLoads], dreg[kLoads];
+  float lreg = 0.f, dlreg = 0.f;
+  auto load_step = [&](int j) __attribute__((always_inline)) {
+    const int h = hk * a.group + j / n_rt;
+    const int rt = rt0 + (j % n_rt) * kBwRowTile;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const size_t idx = (size_t)(q0 + min(rt + lrow + i * kRowsPerPass, q_len - 1)) * a.num_q_heads + h;
+      qreg[i] = *reinterpret_cast<const u32x4 *>((const __bf16 *)a.q + idx * D + lch * 8);
+      dreg[i] = *reinterpret_cast<const u32x4 *>((const __bf16 *)a.d_out + idx * D + lch * 8);
+    }
+    const int r = rt + (tid & (kBwRowTile - 1));
+    const size_t idx = (size_t)(q0 + min(r, q_len - 1)) * a.num_q_heads + h;
+    const float l = a.lse[idx];
+    lreg = (r < q_len && l != -INFINITY) ? l * kLog2e : INFINITY;  // INFINITY: p = 0
+    dlreg = a.delta[idx];
+  };
+  if (n_steps > 0) load_step(0);
+  for (int j = 0; j < n_steps; ++j) {
+    const int rt = rt0 + (j % n_rt) * kBwRowTile;
+    {
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         const int r = lrow + i * kRowsPerPass;
-        const size_t idx = (size_t)(q0 + min(rt + r, q_len - 1)) * a.num_q_heads + h;
-        *reinterpret_cast<uint4 *>(qsm + r * kPitch + lch * 16) =
-            *reinterpret_cast<const uint4 *>((const __bf16 *)a.q + idx * D + lch * 8);
-        *reinterpret_cast<uint4 *>(dosm + r * kPitch + lch * 16) =
-            *reinterpret_cast<const uint4 *>((const __bf16 *)a.d_out + idx * D + lch * 8);
+        *reinterpret_cast<u32x4 *>(qsm + r * kPitch + lch * 16) = qreg[i];
+        *reinterpret_cast<u32x4 *>(dosm + r * kPitch + lch * 16) = dreg[i];
       }
       if (tid < kBwRowTile) {
-        const int r = rt + tid;
-        const size_t idx = (size_t)(q0 + min(r, q_len - 1)) * a.num_q_heads + h;
-        const float l = a.lse[idx];
-        lse_s[tid] = (r < q_len && l != -INFINITY) ? l * kLog2e : INFINITY;  // INFINITY: p = 0
-        dl_s[tid] = a.delta[idx];
+        lse_s[tid] = lreg;
+        dl_s[tid] = dlreg;
       }
       __syncthreads();
+      load_step(min(j + 1, n_steps - 1));  // unconditional: exact wait counts
       f32x16 sacc, dpacc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.f;
@@ -459,19 +486,53 @@ __global__ __launch_bounds__(256) void dkv_mfma_kernel(BackwardArgs a) {
   }
 }
 
+// Under a causal mask the work of tile i grows (dQ) or shrinks (dK/dV) with
+// i; a workgroup takes the pair of tiles (p, n-1-p), so all carry the same.
+template <int D>
+__global__ __launch_bounds__(256) void dq_mfma_kernel(BackwardArgs a) {
+  using C = BwCfg<D>;
+  __shared__ __align__(16) unsigned char ksm[kBwKeys * C::kKRow];
+  __shared__ __align__(16) unsigned char vsm[kBwKeys * C::kVRow];
+  const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int n = (a.cu_q[b + 1] - a.cu_q[b] + kBwRows - 1) / kBwRows;
+  if (p >= (n + 1) / 2) return;  // uniform
+  dq_tile<D>(a, n - 1 - p, h, b, ksm, vsm);
+  if (n - 1 - p != p) {
+    __syncthreads();
+    dq_tile<D>(a, p, h, b, ksm, vsm);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void dkv_mfma_kernel(BackwardArgs a) {
+  using C = BwCfg<D>;
+  __shared__ __align__(16) unsigned char qsm[kBwRowTile * C::kKRow];
+  __shared__ __align__(16) unsigned char dosm[kBwRowTile * C::kKRow];
+  __shared__ float lse_s[kBwRowTile], dl_s[kBwRowTile];
+  const int p = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int n = (a.ctx_lens[b] + kBwKeyTile - 1) / kBwKeyTile;
+  if (p >= (n + 1) / 2) return;  // uniform
+  dkv_tile<D>(a, p, hk, b, qsm, dosm, lse_s, dl_s);
+  if (n - 1 - p != p) {
+    __syncthreads();
+    dkv_tile<D>(a, n - 1 - p, hk, b, qsm, dosm, lse_s, dl_s);
+  }
+}
+
 template <int D, typename T>
 hipError_t launch_t(const BackwardArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((delta_kernel<D, T>), dim3(a.total_q), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((dq_mfma_kernel<D>), dim3((a.max_q_len + kBwRows - 1) / kBwRows, a.num_q_heads, a.batch),
+    hipLaunchKernelGGL((dq_mfma_kernel<D>), dim3(((a.max_q_len + kBwRows - 1) / kBwRows + 1) / 2, a.num_q_heads, a.batch),
                        dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((dq_kernel<D, T>), dim3(a.max_q_len, a.num_q_heads, a.batch), dim3(64), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((dkv_mfma_kernel<D>), dim3((a.max_ctx + kBwKeyTile - 1) / kBwKeyTile, a.c.num_kv_heads, a.batch),
+    hipLaunchKernelGGL((dkv_mfma_kernel<D>), dim3(((a.max_ctx + kBwKeyTile - 1) / kBwKeyTile + 1) / 2, a.c.num_kv_heads,
+                                                  a.batch),
                        dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((dkv_kernel<D, T>), dim3(a.max_ctx, a.c.num_kv_heads, a.batch), dim3(64), 0, s, a);
