@@ -107,3 +107,51 @@ def test_layered_decode_128k_sampled_sequences():
               block_table=full["block_table"].numpy()[seqs])
     ref, _ = oracle.decode_layered(f64(inp["q"][seqs]), hi, lo)
     check_close(out[seqs], ref, "bf16", f"sequences {seqs} (ctx {ctx[seqs].tolist()})")
+
+
+def test_backward_2048_sampled_heads():
+    """The backward bench configuration (L=2048 causal, 32 heads, D=128, bf16,
+    pages of 256) at full size; with Hq = Hkv the heads are independent, so
+    the oracle differentiates three sampled heads."""
+    w = wl.LLAMA7B_PREFILL
+    say(f"full size backward: {w.name}")
+    inp = wl.prefill_inputs(w)
+    shape = (inp["num_pages"], w.page_size, w.num_kv_heads, w.head_dim)
+    cache = ops.KVCache(torch.zeros(shape, dtype=torch.bfloat16).cuda(), torch.zeros(shape, dtype=torch.bfloat16).cuda())
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    bt, cu, ctx, st = (inp[n].cuda() for n in ("block_table", "cu_q", "ctx_lens", "start_pos"))
+    L = max(w.seq_lens)
+    ops.kv_cache_append(cache, k, v, bt, st, cu, max_new=L)
+    out, lse = ops.attn_prefill_paged(q, cu, cache, bt, ctx, max_q_len=L, return_lse=True)
+    d_out = wl.normal(tuple(q.shape), "bf16", w.seed, wl.STREAM_KNEW)
+    dq, dk, dv = ops.attn_backward_paged(q, cu, cache, bt, ctx, out, lse, d_out.cuda(), max_q_len=L, max_ctx=L)
+    torch.cuda.synchronize()
+    btn = inp["block_table"].numpy()
+    t = np.arange(L)
+    phys, slot = btn[0][t // w.page_size], t % w.page_size
+    for h in (0, 13, 31):
+        sl = slice(h, h + 1)
+        rdq, rdk, rdv = oracle.attention_backward_paged(
+            f64(inp["q"][:, sl]), inp["cu_q"].numpy(), _dense_pages(inp["k"][:, sl], w.page_size),
+            _dense_pages(inp["v"][:, sl], w.page_size),
+            _identity_table(L, w.page_size), inp["ctx_lens"].numpy(), w.page_size, f64(d_out[:, sl]))
+        got_q = dq[:, sl].cpu().numpy()
+        got_k = dk.cpu().numpy()[phys, slot][:, sl]
+        got_v = dv.cpu().numpy()[phys, slot][:, sl]
+        ref_k = rdk.reshape(L, 1, w.head_dim)
+        ref_v = rdv.reshape(L, 1, w.head_dim)
+        for what, got, ref in (("dq", got_q, rdq), ("dk", got_k, ref_k), ("dv", got_v, ref_v)):
+            scale = max(1.0, float(np.abs(ref).max()))
+            err = np.abs(got.astype(np.float64) - ref)
+            say(f"  head {h} {what}: max|ref|={np.abs(ref).max():.3e} max|d|={err.max():.3e} mean|d|={err.mean():.3e}")
+            assert err.max() <= 2e-2 * scale and err.mean() <= 2e-3 * scale, (h, what)
+
+
+def _dense_pages(rows, page_size):
+    """Rows [L, 1, D] laid out as consecutive pages [L / P, P, 1, D] (float64)."""
+    x = f64(rows)
+    return x.reshape(-1, page_size, x.shape[1], x.shape[2])
+
+
+def _identity_table(n_tokens, page_size):
+    return np.arange(n_tokens // page_size, dtype=np.int64)[None, :]
