@@ -352,13 +352,13 @@ __device__ __forceinline__ void dq_tile(const BackwardArgs &a, int qt, int h, in
 
 // dK / dV on MFMA (bf16 caches).  A workgroup of 4 waves takes 128 keys of
 // one (sequence, KV head), 32 per wave, their K and V rows held as MFMA B
-// operands; for each query head of the GQA group and each 32-row query tile
+// operands; for each query head of the GQA group and each 64-row query tile
 // that sees the keys (staged in LDS: Q, dO, lse, D):
 //   S  = Q . K^T  and  dP = dO . V^T   (rows on M, the wave's keys on N),
 //   P  = exp(s S - lse),  dS = P (dP - D)  (rounded to bf16),
 //   dV^T += dO^T . P,   dK^T += Q^T . dS   (Q^T, dO^T read transposed).
 constexpr int kBwKeyTile = 128;
-constexpr int kBwRowTile = 32;
+constexpr int kBwRowTile = 64;  // query rows per step (two 32-row MFMA blocks)
 
 template <int D>
 __device__ __forceinline__ void dkv_tile(const BackwardArgs &a, int kt, int hk, int b, unsigned char *qsm,
@@ -434,32 +434,39 @@ __device__ __forceinline__ void dkv_tile(const BackwardArgs &a, int kt, int hk, 
       }
       __syncthreads();
       load_step(min(j + 1, n_steps - 1));  // unconditional: exact wait counts
-      f32x16 sacc, dpacc;
+      constexpr int kMb = kBwRowTile / 32;  // 32-row blocks
+      f32x16 sacc[kMb], dpacc[kMb];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.f;
+      for (int mb = 0; mb < kMb; ++mb) {
 #pragma unroll
-      for (int s = 0; s < C::kNs; ++s) {
-        const bf16x8 qf = *reinterpret_cast<const bf16x8 *>(qsm + col * kPitch + (16 * s + 8 * g) * 2);
-        const bf16x8 df = *reinterpret_cast<const bf16x8 *>(dosm + col * kPitch + (16 * s + 8 * g) * 2);
-        sacc = mfma32(qf, bk[s], sacc);
-        dpacc = mfma32(df, bv[s], dpacc);
+        for (int i = 0; i < 16; ++i) sacc[mb][i] = dpacc[mb][i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < C::kNs; ++s) {
+          const int ro = (mb * 32 + col) * kPitch + (16 * s + 8 * g) * 2;
+          sacc[mb] = mfma32(*reinterpret_cast<const bf16x8 *>(qsm + ro), bk[s], sacc[mb]);
+          dpacc[mb] = mfma32(*reinterpret_cast<const bf16x8 *>(dosm + ro), bv[s], dpacc[mb]);
+        }
       }
-      // Element i is row rt + (i/4)*8 + g*4 + i%4 against this lane's key.
-      bf16x8 bp[2], bds[2];
+      // Element i of block mb is row rt + mb*32 + (i/4)*8 + g*4 + i%4 against
+      // this lane's key; 16-row step t of the products below holds block
+      // t/2, elements 8(t%2) .. 8(t%2)+7.
+      bf16x8 bp[2 * kMb], bds[2 * kMb];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rr = (i >> 2) * 8 + g * 4 + (i & 3);
-        const int pos = off + rt + rr;
-        bool vis = key < ctx && rt + rr < q_len;
-        if (a.causal) vis = vis && key <= pos;
-        if (a.window_left >= 0) vis = vis && pos - key <= a.window_left;
-        const float p = vis ? fast_exp2(sacc[i] * a.scale_log2 - lse_s[rr]) : 0.f;
-        bp[i >> 3][i & 7] = (__bf16)p;
-        bds[i >> 3][i & 7] = (__bf16)(p * (dpacc[i] - dl_s[rr]));
-      }
+      for (int mb = 0; mb < kMb; ++mb)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r0 = t * 16 + g * 4;
+        for (int i = 0; i < 16; ++i) {
+          const int rr = mb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+          const int pos = off + rt + rr;
+          bool vis = key < ctx && rt + rr < q_len;
+          if (a.causal) vis = vis && key <= pos;
+          if (a.window_left >= 0) vis = vis && pos - key <= a.window_left;
+          const float p = vis ? fast_exp2(sacc[mb][i] * a.scale_log2 - lse_s[rr]) : 0.f;
+          bp[2 * mb + (i >> 3)][i & 7] = (__bf16)p;
+          bds[2 * mb + (i >> 3)][i & 7] = (__bf16)(p * (dpacc[mb][i] - dl_s[rr]));
+        }
+#pragma unroll
+      for (int t = 0; t < 2 * kMb; ++t) {
+        const int r0 = (t >> 1) * 32 + (t & 1) * 16 + g * 4;
 #pragma unroll
         for (int db = 0; db < C::kNdb; ++db) {
           const int c = (db * 32 + 16 * (gam & 1) + 4 * (tp & 3)) * 2;
