@@ -12,7 +12,8 @@
 // with the masks, GQA head map and page layout of the forward pass.
 //
 // Three kernels:
-//   delta_kernel : D = dO . O per (row, head);
+//   D = dO . O   : per (row, head); computed by the bf16 dQ kernel, by
+//                  delta_kernel for fp32 caches;
 //   dQ           : bf16 caches: dq_mfma_kernel (128 query rows per workgroup,
 //                  K/V tiles staged in LDS, products on MFMA); fp32 caches:
 //                  dq_kernel, one wave per (query row, head) on the vector
@@ -259,7 +260,19 @@ __device__ __forceinline__ void dq_tile(const BackwardArgs &a, int qt, int h, in
   }
   const float lse = a.lse[qidx];
   const float lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;  // no visible key: every p = 0
-  const float dlt = a.delta[qidx];
+  // D = dO . O of this lane's row: the lane holds half of its dims (those
+  // of bdo), the lane 32 apart the other half.  Written for the dK/dV
+  // kernel, which runs after this one.
+  const __bf16 *op = (const __bf16 *)a.out + qidx * D;
+  float dpart = 0.f;
+#pragma unroll
+  for (int s = 0; s < C::kNs; ++s) {
+    const bf16x8 ov = *reinterpret_cast<const bf16x8 *>(op + 16 * s + 8 * g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dpart = fmaf((float)bdo[s][e], (float)ov[e], dpart);
+  }
+  const float dlt = dpart + __shfl_xor(dpart, 32, 64);
+  if (g == 0 && row < q_len) a.delta[qidx] = dlt;
   // Visible keys of the tile's rows: [k_lo, k_hi].
   const int p_first = off + qt * kBwRows;
   const int p_last = off + min(qt * kBwRows + kBwRows - 1, q_len - 1);
@@ -528,9 +541,11 @@ __global__ __launch_bounds__(256) void dkv_mfma_kernel(BackwardArgs a) {
 
 template <int D, typename T>
 hipError_t launch_t(const BackwardArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((delta_kernel<D, T>), dim3(a.total_q), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if constexpr (sizeof(T) != 2) {  // the bf16 dQ kernel computes D itself
+    hipLaunchKernelGGL((delta_kernel<D, T>), dim3(a.total_q), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((dq_mfma_kernel<D>), dim3(((a.max_q_len + kBwRows - 1) / kBwRows + 1) / 2, a.num_q_heads, a.batch),
                        dim3(256), 0, s, a);
