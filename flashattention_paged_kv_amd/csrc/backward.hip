@@ -291,8 +291,8 @@ __device__ __forceinline__ void dq_tile(const BackwardArgs &a, int qt, int h, in
   const __bf16 *vpool = (const __bf16 *)a.c.v + (size_t)hk * D;
   const int lrow = tid / C::kCpr, lch = tid % C::kCpr;
   constexpr int kRowsPerPass = 256 / C::kCpr;
-  // K/V of a tile in registers (rows past the context read the last valid
-  // row), one tile ahead of the one being computed.
+  // K/V of a tile through registers into LDS (rows past the context read
+  // the last valid row).
   u32x4 kreg[C::kLoads], vreg[C::kLoads];
   auto load_tile = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
@@ -305,9 +305,9 @@ __device__ __forceinline__ void dq_tile(const BackwardArgs &a, int qt, int h, in
     }
   };
   const int kt_end = k_hi / kBwKeys;
-  load_tile(k_lo / kBwKeys);
   for (int kt = k_lo / kBwKeys; kt <= kt_end; ++kt) {
     const int key0 = kt * kBwKeys;
+    load_tile(kt);
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
       const int r = lrow + i * kRowsPerPass;
@@ -315,7 +315,6 @@ __device__ __forceinline__ void dq_tile(const BackwardArgs &a, int qt, int h, in
       *reinterpret_cast<u32x4 *>(vsm + r * C::kVRow + lch * 16) = vreg[i];
     }
     __syncthreads();
-    load_tile(min(kt + 1, kt_end));  // unconditional: exact wait counts
     f32x16 sacc[2], dpacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -506,23 +505,25 @@ __device__ __forceinline__ void dkv_tile(const BackwardArgs &a, int kt, int hk, 
   }
 }
 
-// Under a causal mask the work of tile i grows (dQ) or shrinks (dK/dV) with
-// i; a workgroup takes the pair of tiles (p, n-1-p), so all carry the same.
+// dQ: two workgroups share a CU (at most 256 registers per lane), so one's
+// softmax work overlaps the other's MFMAs.  Tiles are taken heaviest first
+// (under a causal mask the last query tile sees the most keys), and the
+// dispatcher hands the lighter ones to whichever CU frees up.
 template <int D>
-__global__ __launch_bounds__(256) void dq_mfma_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(256, 2) void dq_mfma_kernel(BackwardArgs a) {
   using C = BwCfg<D>;
   __shared__ __align__(16) unsigned char ksm[kBwKeys * C::kKRow];
   __shared__ __align__(16) unsigned char vsm[kBwKeys * C::kVRow];
   const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n = (a.cu_q[b + 1] - a.cu_q[b] + kBwRows - 1) / kBwRows;
-  if (p >= (n + 1) / 2) return;  // uniform
+  if (p >= n) return;  // uniform
   dq_tile<D>(a, n - 1 - p, h, b, ksm, vsm);
-  if (n - 1 - p != p) {
-    __syncthreads();
-    dq_tile<D>(a, p, h, b, ksm, vsm);
-  }
 }
 
+// dK / dV: one workgroup per CU (its accumulators need more than 256
+// registers per lane).  Under a causal mask the work of key tile i shrinks
+// with i; a workgroup takes the pair of tiles (p, n-1-p), so all carry the
+// same.
 template <int D>
 __global__ __launch_bounds__(256) void dkv_mfma_kernel(BackwardArgs a) {
   using C = BwCfg<D>;
@@ -547,7 +548,7 @@ hipError_t launch_t(const BackwardArgs &a, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((dq_mfma_kernel<D>), dim3(((a.max_q_len + kBwRows - 1) / kBwRows + 1) / 2, a.num_q_heads, a.batch),
+    hipLaunchKernelGGL((dq_mfma_kernel<D>), dim3((a.max_q_len + kBwRows - 1) / kBwRows, a.num_q_heads, a.batch),
                        dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((dq_kernel<D, T>), dim3(a.max_q_len, a.num_q_heads, a.batch), dim3(64), 0, s, a);
