@@ -3,9 +3,12 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 One step is one pass of the hot path over one batch of synthetic input:
-  * prefill step (the headline workload): kv_cache_append of a 2048-token
-    Llama-2-7B-shaped prompt (32 heads, D=128, bf16) into 256-token pages with
-    a permuted block table, then causal attn_prefill_paged over it;
+  * prefill step (the headline workload): a 2048-token Llama-2-7B-shaped
+    prompt (32 heads, D=128, bf16) appended into 256-token pages with a
+    permuted block table and attended over causally, by
+    attn_prefill_paged_append (the append fused into the prefill kernel; the
+    two separate calls, kv_cache_append then attn_prefill_paged, are timed
+    beside it);
   * decode step (reported beside it): kv_cache_append of one new token for
     each of 64 Llama-2-70B-shaped GQA sequences (64 q heads, 8 KV heads,
     contexts uniform in [512, 8192]) and attn_decode_paged over their pages.
@@ -102,12 +105,18 @@ def bench_prefill(w: wl.PrefillWorkload, steps: int, warmup: int) -> dict:
         ops.attn_prefill_paged(q, cu, cache, bt, ctx, max_q_len=max_len, softmax_scale=w.softmax_scale,
                                causal=w.causal, window_left=w.window_left, out=out)
 
-    def step():
+    def separate():
         append()
         prefill()
 
+    def step():  # the append fused into the prefill kernel: one launch
+        ops.attn_prefill_paged_append(q, k, v, cu, cache, bt, ctx, max_q_len=max_len, softmax_scale=w.softmax_scale,
+                                      causal=w.causal, window_left=w.window_left, out=out)
+
     ms_step = _time_loop(step, steps, warmup)
-    ms_kernel = _time_loop(prefill, steps, warmup)
+    ms_separate = _time_loop(separate, steps, warmup)
+    ms_attn_only = _time_loop(prefill, steps, warmup)
+    ms_kernel = ms_step  # the step is one kernel
     pairs = sum(causal_pairs(n, w.window_left) for n in w.seq_lens)
     flops = 4 * w.head_dim * w.num_q_heads * pairs
     kv_bytes = 2 * sum(w.seq_lens) * w.num_kv_heads * w.head_dim * 2
@@ -120,10 +129,18 @@ def bench_prefill(w: wl.PrefillWorkload, steps: int, warmup: int) -> dict:
     else:  # below the ridge point (a short window): bytes bound it
         gbs = io_bytes / (ms_kernel * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4))
-    roof["traffic"] = _traffic("prefill_bf16_kernel", w.name)
-    return dict(workload=w.name, ms_per_step=ms_step, ms_prefill_kernel=ms_kernel, flops=flops,
+    roof["traffic"] = _traffic("prefill_bf16_kernel_fused", w.name)
+    # The same for attention alone (attn_prefill_paged, no append), for reference.
+    attn = flops / (ms_attn_only * 1e-3) / 1e12
+    roof_attn = dict(bound=roof["bound"], achieved=round(attn, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                     frac=round(attn / PEAK_BF16_TFLOPS, 4), traffic=_traffic("prefill_bf16_kernel", w.name))
+    if roof["bound"] == "hbm":
+        gbs = io_bytes / (ms_attn_only * 1e-3) / 1e9
+        roof_attn.update(achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4))
+    return dict(workload=w.name, ms_per_step=ms_step, ms_prefill_kernel=ms_kernel, ms_separate_calls=ms_separate,
+                ms_attention_only=ms_attn_only, flops=flops,
                 tflops_step=flops / (ms_step * 1e-3) / 1e12, tflops_kernel=achieved, kv_bytes=kv_bytes,
-                io_bytes=io_bytes, roofline=roof)
+                io_bytes=io_bytes, roofline=roof, attention_only_roofline=roof_attn)
 
 
 def bench_decode(w: wl.DecodeWorkload, steps: int, warmup: int) -> dict:
@@ -362,9 +379,12 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) bf16, permuted page tables)",
         "config": {"workload": pre["workload"], "batch": 1, "seq_len": 2048, "num_q_heads": 32,
                    "num_kv_heads": 32, "head_dim": 128, "page_size": 256, "causal": True,
-                   "step": "kv_cache_append + attn_prefill_paged"},
+                   "step": "attn_prefill_paged_append (append fused into the prefill kernel)"},
         "roofline": pre["roofline"],
         "prefill_kernel_ms": round(pre["ms_prefill_kernel"], 5),
+        "separate_calls_ms": round(pre["ms_separate_calls"], 5),
+        "attention_only_kernel_ms": round(pre["ms_attention_only"], 5),
+        "attention_only_roofline": pre["attention_only_roofline"],
         "decode": {"metric": "decode KV-read GB/s", "value": round(dec["gbs_step"], 1), "unit": "GB/s",
                    "ms_per_step": round(dec["ms_per_step"], 5), "kernel_ms": round(dec["ms_decode_kernels"], 5),
                    "kv_bytes": dec["kv_bytes"], "sum_ctx": dec["sum_ctx"],

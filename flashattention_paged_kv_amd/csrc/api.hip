@@ -123,6 +123,46 @@ pa_status report(pa_status st, const char *msg) {
 }
 }  // namespace pa
 
+// Checks shared by the prefill entry points; fills *a.  *empty: nothing to
+// compute (batch or max_q_len is 0).
+static pa_status prefill_args(const void *q, const int32_t *cu_q, const pa_kv_cache *cache, const int32_t *block_table,
+                       int32_t max_pages_per_seq, const int32_t *ctx_lens, int32_t batch, int32_t max_q_len,
+                       int32_t num_q_heads, float softmax_scale, int32_t causal, int32_t window_left, void *out,
+                       float *lse, pa::PrefillArgs *a, bool *empty) {
+  pa_status st = check_cache(cache, false);
+  if (st != PA_OK) return st;
+  if (cache->dtype == PA_I8) return fail(PA_ERR_UNSUPPORTED, "prefill over an int8 cache is not supported");
+  if (batch < 0 || max_q_len < 0) return fail(PA_ERR_INVALID_ARG, "batch and max_q_len must be >= 0");
+  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, cache->num_kv_heads);
+  if ((st = check_scale(softmax_scale)) != PA_OK) return st;
+  if (causal != 0 && causal != 1) return fail(PA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  *empty = batch == 0 || max_q_len == 0;
+  if (*empty) return ok();
+  if (q == nullptr || cu_q == nullptr || block_table == nullptr || ctx_lens == nullptr || out == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (max_pages_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq must be > 0");
+  a->q = q;
+  a->cu_q = cu_q;
+  a->c = view_of(cache);
+  a->block_table = block_table;
+  a->max_pages = max_pages_per_seq;
+  a->ctx_lens = ctx_lens;
+  a->batch = batch;
+  a->max_q_len = max_q_len;
+  a->num_q_heads = num_q_heads;
+  a->group = num_q_heads / cache->num_kv_heads;
+  a->scale_log2 = softmax_scale * 1.4426950408889634f;
+  a->causal = causal;
+  a->window_left = window_left < 0 ? -1 : window_left;
+  a->out = out;
+  a->lse = lse;
+  a->k_new = nullptr;
+  a->v_new = nullptr;
+  return ok();
+}
+
 extern "C" {
 
 int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
@@ -179,6 +219,7 @@ pa_status kv_cache_append(const pa_kv_cache *cache, const void *k_new, const voi
   a.block_table = block_table;
   a.max_pages = max_pages_per_seq;
   a.start_pos = start_pos;
+  a.ctx_lens = nullptr;
   a.cu_new = cu_new;
   a.batch = batch;
   a.max_new = max_new;
@@ -211,36 +252,51 @@ pa_status attn_prefill_paged(const void *q, const int32_t *cu_q, const pa_kv_cac
                              const int32_t *block_table, int32_t max_pages_per_seq, const int32_t *ctx_lens,
                              int32_t batch, int32_t max_q_len, int32_t num_q_heads, float softmax_scale,
                              int32_t causal, int32_t window_left, void *out, float *lse, void *stream) {
-  pa_status st = check_cache(cache, false);
-  if (st != PA_OK) return st;
-  if (cache->dtype == PA_I8) return fail(PA_ERR_UNSUPPORTED, "prefill over an int8 cache is not supported");
-  if (batch < 0 || max_q_len < 0) return fail(PA_ERR_INVALID_ARG, "batch and max_q_len must be >= 0");
-  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0)
-    return fail(PA_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
-                num_q_heads, cache->num_kv_heads);
-  if ((st = check_scale(softmax_scale)) != PA_OK) return st;
-  if (causal != 0 && causal != 1) return fail(PA_ERR_INVALID_ARG, "causal must be 0 or 1");
-  if (batch == 0 || max_q_len == 0) return ok();
-  if (q == nullptr || cu_q == nullptr || block_table == nullptr || ctx_lens == nullptr || out == nullptr)
-    return fail(PA_ERR_INVALID_ARG, "NULL pointer argument");
-  if (max_pages_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq must be > 0");
   pa::PrefillArgs a;
-  a.q = q;
-  a.cu_q = cu_q;
-  a.c = view_of(cache);
-  a.block_table = block_table;
-  a.max_pages = max_pages_per_seq;
-  a.ctx_lens = ctx_lens;
-  a.batch = batch;
-  a.max_q_len = max_q_len;
-  a.num_q_heads = num_q_heads;
-  a.group = num_q_heads / cache->num_kv_heads;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  a.causal = causal;
-  a.window_left = window_left < 0 ? -1 : window_left;
-  a.out = out;
-  a.lse = lse;
+  bool empty = false;
+  pa_status st = prefill_args(q, cu_q, cache, block_table, max_pages_per_seq, ctx_lens, batch, max_q_len, num_q_heads,
+                              softmax_scale, causal, window_left, out, lse, &a, &empty);
+  if (st != PA_OK || empty) return st;
   return hip_status(pa::launch_prefill(a, (hipStream_t)stream), "attn_prefill_paged launch");
+}
+
+pa_status attn_prefill_paged_append(const void *q, const void *k_new, const void *v_new, const int32_t *cu_q,
+                                    const pa_kv_cache *cache, const int32_t *block_table, int32_t max_pages_per_seq,
+                                    const int32_t *ctx_lens, int32_t batch, int32_t max_q_len, int32_t num_q_heads,
+                                    float softmax_scale, int32_t causal, int32_t window_left, void *out, float *lse,
+                                    void *stream) {
+  pa::PrefillArgs a;
+  bool empty = false;
+  pa_status st = prefill_args(q, cu_q, cache, block_table, max_pages_per_seq, ctx_lens, batch, max_q_len, num_q_heads,
+                              softmax_scale, causal, window_left, out, lse, &a, &empty);
+  if (st != PA_OK) return st;
+  if (!empty && (k_new == nullptr || v_new == nullptr)) return fail(PA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (empty) return ok();
+  const hipStream_t s = (hipStream_t)stream;
+  if (cache->dtype == PA_BF16 && cache->page_size >= 64) {
+    a.k_new = k_new;
+    a.v_new = v_new;
+    return hip_status(pa::launch_prefill(a, s), "attn_prefill_paged_append launch");
+  }
+  // Other caches (fp32, or pages smaller than a key tile): the append kernel
+  // (start = ctx_lens[b] - q_len_b) and then the prefill, on the same stream.
+  pa::AppendArgs ap;
+  ap.k_pages = cache->k_pages;
+  ap.v_pages = cache->v_pages;
+  ap.k_new = k_new;
+  ap.v_new = v_new;
+  ap.block_table = block_table;
+  ap.max_pages = max_pages_per_seq;
+  ap.start_pos = nullptr;
+  ap.ctx_lens = ctx_lens;
+  ap.cu_new = cu_q;
+  ap.batch = batch;
+  ap.max_new = max_q_len;
+  ap.page_size = cache->page_size;
+  ap.log2_page = log2_exact(cache->page_size);
+  ap.row_bytes = cache->num_kv_heads * cache->head_dim * (cache->dtype == PA_F32 ? 4 : 2);
+  if ((st = hip_status(pa::launch_append(ap, s), "attn_prefill_paged_append (append) launch")) != PA_OK) return st;
+  return hip_status(pa::launch_prefill(a, s), "attn_prefill_paged_append launch");
 }
 
 pa_status kv_cache_copy_pages(const pa_kv_cache *cache, const int32_t *src_pages, const int32_t *dst_pages,

@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int n_new = a.cu_new[b + 1] - n0;
   const int r_begin = blockIdx.x * kAppendRowsPerBlock;
   if (r_begin >= n_new) return;
-  const int start = a.start_pos[b];
+  const int start = a.start_pos != nullptr ? a.start_pos[b] : a.ctx_lens[b] - n_new;
   const int chunks = a.row_bytes >> 4;
   const int rows = min(kAppendRowsPerBlock, n_new - r_begin);
   for (int c = threadIdx.x; c < rows * chunks; c += blockDim.x) {

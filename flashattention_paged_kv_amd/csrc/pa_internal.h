@@ -29,7 +29,8 @@ struct AppendArgs {
   const void *v_new;
   const int32_t *block_table;
   int max_pages;
-  const int32_t *start_pos;
+  const int32_t *start_pos;  // NULL: start = ctx_lens[b] - (new rows of b)
+  const int32_t *ctx_lens;   // used only when start_pos is NULL
   const int32_t *cu_new;
   int batch;
   int max_new;
@@ -85,6 +86,12 @@ struct PrefillArgs {
   int window_left;
   void *out;
   float *lse;
+  // Fused append (bf16 caches with page_size >= 64): the K/V rows of the
+  // queries themselves, [cu_q[batch], num_kv_heads, head_dim], positions
+  // ctx_lens[b] - q_len_b + i.  The kernel reads these keys from here and
+  // writes them into their page slots (c.k / c.v).  NULL: no append.
+  const void *k_new;
+  const void *v_new;
 };
 
 struct DecodeArgs {

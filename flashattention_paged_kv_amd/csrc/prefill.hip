@@ -76,10 +76,16 @@ struct PfCfg {
 };
 
 // BIG_PAGE: page_size >= 64, so each 64-key tile lies in one page.
+// FUSED (with BIG_PAGE): the queries' own K/V rows arrive in a.k_new /
+// a.v_new; keys at positions >= ctx - q_len are read from there, and each
+// such row is written into its page slot once, by the item (query tile, key
+// tile) of that position in a workgroup of the first query head of its KV
+// group.  No key the launch reads from a page is written by it.
 // block_table is a.block_table, passed again as a restrict pointer so that
 // uniform page-id reads are scalar loads.
-template <int D, bool BIG_PAGE, bool RUNS>
+template <int D, bool BIG_PAGE, bool RUNS, bool FUSED>
 __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, const int32_t *__restrict__ block_table) {
+  static_assert(!FUSED || BIG_PAGE, "the fused append needs whole key tiles inside one page");
   using C = PfCfg<D>;
   __shared__ __align__(16) unsigned char smem[2 * C::kEngine];
 
@@ -243,6 +249,11 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   const char *kbase = (const char *)a.c.k + (size_t)hk * D * 2;
   const char *vbase = (const char *)a.c.v + (size_t)hk * D * 2;
   const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
+  // Fused append: key position k >= off is row q0 + k - off of k_new / v_new.
+  const char *knew = FUSED ? (const char *)a.k_new + ((size_t)q0 * a.c.num_kv_heads + hk) * D * 2 : nullptr;
+  const char *vnew = FUSED ? (const char *)a.v_new + ((size_t)q0 * a.c.num_kv_heads + hk) * D * 2 : nullptr;
+  // Of the query heads sharing KV head hk, the first writes its new rows.
+  const bool kv_writer = h % a.group == 0;
 
   // Prefetch of one key tile, K and V separately: thread `tid` moves chunks
   // tid + 256 i, i.e. row tid / kCpr + i * kRowsPerPass, chunk tid % kCpr.
@@ -254,13 +265,29 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   const int lrow = tid / C::kCpr;
   const int lch = tid % C::kCpr;
   const uint32_t lane_goff = (uint32_t)lrow * (uint32_t)row_bytes + lch * 16;
-  auto load_half = [&](int kt, const char *base, uint4 *dst) __attribute__((always_inline)) {
+  // Byte offset of key tile kt inside the K (or V) pool (BIG_PAGE: one page).
+  auto tile_page_off = [&](int kt) __attribute__((always_inline)) {
+    const int key0 = kt * kPfKeys;
+    return ((size_t)block_table[(size_t)b * a.max_pages + (key0 >> lp)] * P + (key0 & (P - 1))) * row_bytes;
+  };
+  auto load_half = [&](int kt, size_t tile_off, const char *base, const char *nbase, uint4 *dst)
+      __attribute__((always_inline)) {
     const int key0 = kt * kPfKeys;
     if constexpr (BIG_PAGE) {
-      const size_t tile_off = ((size_t)block_table[(size_t)b * a.max_pages + (key0 >> lp)] * P + (key0 & (P - 1))) *
-                              row_bytes;  // uniform
+      // Fused: a tile of new keys only comes from the new rows; a tile that
+      // also holds cached keys comes from its page, and its new rows are
+      // replaced once the loads have landed (fix_new_rows).
+      const char *tb = base + tile_off;
+      if constexpr (FUSED) {
+        if (key0 >= off) tb = nbase + (size_t)(key0 - off) * row_bytes;
+        // The choice is the same for every lane; say so, or the descriptor
+        // is treated as per-lane (a loop over its distinct values).
+        const uint64_t u = (uint64_t)(uintptr_t)tb;
+        tb = (const char *)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(u >> 32)) << 32) |
+                                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u));
+      }
       const uint32_t span = (uint32_t)(min(kPfKeys, ctx - key0) * row_bytes);
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(base + tile_off, span);
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(tb, span);
 #pragma unroll
       for (int i = 0; i < C::kLoads; ++i)
         dst[i] = buf_load16(r, lane_goff + (uint32_t)(i * kRowsPerPass) * (uint32_t)row_bytes);
@@ -291,7 +318,56 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       *reinterpret_cast<uint4 *>(vbuf(buf) + lane_voff + i * kRowsPerPass * C::kVRow) = src[i];
   };
   uint4 pk[C::kLoads], pv[C::kLoads];  // K / V of a tile in flight
-
+  size_t pk_off = 0;  // BIG_PAGE: tile_page_off of the tile in pk / pv
+  auto load_tile = [&](int kt) __attribute__((always_inline)) {
+    pk_off = BIG_PAGE ? tile_page_off(kt) : 0;
+    load_half(kt, pk_off, kbase, knew, pk);
+    load_half(kt, pk_off, vbase, vnew, pv);
+  };
+  // Fused append, tile kt holding both cached and new keys (only the first
+  // new position's tile): once its page loads have landed in pk / pv, the
+  // rows of new positions are read again from the new rows.  Rare (one tile
+  // per sequence, and only when that position is not a multiple of 64), so
+  // these loads are waited for at once, outside the prefetch pipeline.
+  auto fix_new_rows = [&](int kt) __attribute__((always_inline)) {
+    if constexpr (FUSED) {
+      const int key0 = kt * kPfKeys;
+      if (key0 < off && key0 + kPfKeys > off) {
+#pragma unroll
+        for (int i = 0; i < C::kLoads; ++i) {
+          const int key = key0 + lrow + i * kRowsPerPass;
+          if (key >= off && key < ctx) {
+            const size_t o = (size_t)(key - off) * row_bytes + lch * 16;
+            pk[i] = *reinterpret_cast<const uint4 *>(knew + o);
+            pv[i] = *reinterpret_cast<const uint4 *>(vnew + o);
+          }
+        }
+      }
+    }
+  };
+  // Fused append: the tile of item idx is in pk / pv; write the rows that
+  // are new and belong to the item's query tile into their page slots.
+  auto write_new = [&](int idx) __attribute__((always_inline)) {
+    if constexpr (FUSED) {
+      int qt, kt;
+      my_item(idx, qt, kt);
+      const int key0 = kt * kPfKeys;
+      const int w_lo = max(key0, off + qt * kPfRows);
+      const int w_hi = min(min(key0 + kPfKeys, off + qt * kPfRows + kPfRows), ctx);
+      if (kv_writer && w_lo < w_hi) {
+        char *kd = (char *)a.c.k + (size_t)hk * D * 2 + pk_off + lane_goff;
+        char *vd = (char *)a.c.v + (size_t)hk * D * 2 + pk_off + lane_goff;
+#pragma unroll
+        for (int i = 0; i < C::kLoads; ++i) {
+          const int key = key0 + lrow + i * kRowsPerPass;
+          if (key >= w_lo && key < w_hi) {
+            *reinterpret_cast<uint4 *>(kd + (size_t)(i * kRowsPerPass) * row_bytes) = pk[i];
+            *reinterpret_cast<uint4 *>(vd + (size_t)(i * kRowsPerPass) * row_bytes) = pv[i];
+          }
+        }
+      }
+    }
+  };
   // Per-wave state.  qt_q: the query tile whose Q^T is in bq; qt_o: the
   // query tile that (m, lsum, o) belong to.
   int qt_q = -1, qt_o = -1;
@@ -486,19 +562,20 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   if (n_mine > 0) {
     int qt, kt;
     my_item(0, qt, kt);
-    load_half(kt, kbase, pk);
-    load_half(kt, vbase, pv);
+    load_tile(kt);
     u32x4 qs[kQLoads];
 #pragma unroll
     for (int i = 0; i < kQLoads; ++i) {
       const int row = min(qt * kPfRows + lrow + i * kRowsPerPass, q_len - 1);
       qs[i] = *reinterpret_cast<const u32x4 *>((const char *)a.q + ((size_t)(q0 + row) * a.num_q_heads + h) * D * 2 + lch * 16);
     }
+    fix_new_rows(kt);
     store_k(0, pk);
     store_v(0, pv);
 #pragma unroll
     for (int i = 0; i < kQLoads; ++i)
       *reinterpret_cast<u32x4 *>(kbuf(1) + (lrow + i * kRowsPerPass) * C::kKRow + lch * 16) = qs[i];
+    write_new(0);
   }
   __syncthreads();
   // Wave priorities: the GEMM wave's MFMAs are the critical path of each
@@ -512,8 +589,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     if (t < n_mine) {
       int qt, kt;
       my_item(min(t + 1, n_mine - 1), qt, kt);
-      load_half(kt, kbase, pk);
-      load_half(kt, vbase, pv);
+      load_tile(kt);
     }
     if (t >= 1) pv_mfma((t - 1) & 1);
     if (t < n_mine) {
@@ -541,6 +617,18 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   };
   auto softmax_phase = [&](int t) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(0);
+    if constexpr (FUSED) {
+      // The next tile's new rows go to their pages first, so that the whole
+      // softmax hides the stores' completion: the memory counter drains in
+      // order, and the wait for the next tile's loads at the end of the
+      // phase includes them.
+      if (t + 1 < n_mine) {
+        int qn, kn;
+        my_item(t + 1, qn, kn);
+        fix_new_rows(kn);
+        write_new(t + 1);
+      }
+    }
     int qt, kt;
     my_item(t, qt, kt);
     if (qt != qt_o) {
@@ -650,7 +738,20 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
   const dim3 block(2 * kPfEngineThreads);
   const bool big = a.c.page_size >= kPfKeys;
 #define PA_PREFILL_LAUNCH(DD, BIG, RUN) \
-  hipLaunchKernelGGL((prefill_bf16_kernel<DD, BIG, RUN>), grid, block, 0, s, a, a.block_table)
+  hipLaunchKernelGGL((prefill_bf16_kernel<DD, BIG, RUN, false>), grid, block, 0, s, a, a.block_table)
+#define PA_PREFILL_FUSED(DD, RUN) \
+  hipLaunchKernelGGL((prefill_bf16_kernel<DD, true, RUN, true>), grid, block, 0, s, a, a.block_table)
+  if (a.k_new != nullptr) {
+    // The fused append reads whole key tiles from one page (the caller
+    // routes smaller pages through a separate append).
+    if (!big) return hipErrorInvalidValue;
+    if (a.c.head_dim == 64) {
+      if (runs) PA_PREFILL_FUSED(64, true); else PA_PREFILL_FUSED(64, false);
+    } else {
+      if (runs) PA_PREFILL_FUSED(128, true); else PA_PREFILL_FUSED(128, false);
+    }
+    return hipGetLastError();
+  }
   if (a.c.head_dim == 64) {
     if (runs) {
       if (big) PA_PREFILL_LAUNCH(64, true, true); else PA_PREFILL_LAUNCH(64, false, true);
@@ -665,6 +766,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
     }
   }
 #undef PA_PREFILL_LAUNCH
+#undef PA_PREFILL_FUSED
   return hipGetLastError();
 }
 

@@ -47,7 +47,8 @@ class _Cache(ctypes.Structure):
 
 _lib = None
 
-EXPORTED = ("kv_cache_append", "kv_pages_quantize_int8", "attn_prefill_paged", "attn_decode_workspace_bytes",
+EXPORTED = ("kv_cache_append", "kv_pages_quantize_int8", "attn_prefill_paged", "attn_prefill_paged_append",
+            "attn_decode_workspace_bytes",
             "attn_decode_paged", "attn_decode_layered_workspace_bytes", "attn_decode_paged_layered",
             "kv_cache_copy_pages", "attn_backward_workspace_bytes", "attn_backward_paged", "pa_pool_create", "pa_pool_destroy", "pa_pool_extend", "pa_pool_fork",
             "pa_pool_release", "pa_pool_export", "pa_pool_free_pages", "pa_pool_refcount",
@@ -67,6 +68,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kv_cache_append.argtypes = [CP, P, P, P, I32, P, P, I32, I32, P]
     lib.kv_pages_quantize_int8.argtypes = [P, P, P, I32, I32, I32, I32, P]
     lib.attn_prefill_paged.argtypes = [P, P, CP, P, I32, P, I32, I32, I32, F32, I32, I32, P, P, P]
+    lib.attn_prefill_paged_append.argtypes = [P, P, P, P, CP, P, I32, P, I32, I32, I32, F32, I32, I32, P, P, P]
     lib.attn_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.attn_decode_workspace_bytes.restype = SZ
     lib.attn_decode_paged.argtypes = [P, CP, P, I32, P, I32, I32, F32, I32, P, P, P, SZ, P]
@@ -227,6 +229,37 @@ def attn_prefill_paged(q: torch.Tensor, cu_q: torch.Tensor, cache: KVCache, bloc
     _check(lib.attn_prefill_paged(_ptr(q), _ptr(cu_q), ctypes.byref(cs), _ptr(block_table), block_table.shape[1],
                                   _ptr(ctx_lens), ctx_lens.shape[0], max_q_len, hq, scale, int(bool(causal)),
                                   int(window_left), _ptr(out), _ptr(lse), _stream()))
+    return (out, lse) if return_lse else out
+
+
+def attn_prefill_paged_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cu_q: torch.Tensor,
+                              cache: KVCache, block_table: torch.Tensor, ctx_lens: torch.Tensor,
+                              max_q_len: Optional[int] = None, softmax_scale: Optional[float] = None,
+                              causal: bool = True, window_left: int = -1, out: Optional[torch.Tensor] = None,
+                              return_lse: bool = False):
+    """Append the queries' own K/V rows k_new / v_new [total_q, Hkv, D] at
+    positions ctx_lens[b] - q_len_b + i, then attend q over the whole
+    context: kv_cache_append followed by attn_prefill_paged, in one kernel
+    for bf16 caches with pages of 64 keys or more."""
+    lib = load_library()
+    cs = cache._struct()
+    _dev(q, "q")
+    _dev(k_new, "k_new", cache.dtype)
+    _dev(v_new, "v_new", cache.dtype)
+    _dev(cu_q, "cu_q", torch.int32)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(ctx_lens, "ctx_lens", torch.int32)
+    total_q, hq, d = q.shape
+    if k_new.shape != (total_q, cache.num_kv_heads, d) or v_new.shape != k_new.shape:
+        raise ValueError(f"k_new / v_new must be [{total_q}, {cache.num_kv_heads}, {d}]")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    max_q_len = total_q if max_q_len is None else max_q_len
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib.attn_prefill_paged_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(cu_q), ctypes.byref(cs),
+                                         _ptr(block_table), block_table.shape[1], _ptr(ctx_lens), ctx_lens.shape[0],
+                                         max_q_len, hq, scale, int(bool(causal)), int(window_left), _ptr(out),
+                                         _ptr(lse), _stream()))
     return (out, lse) if return_lse else out
 
 

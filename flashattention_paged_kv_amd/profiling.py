@@ -35,6 +35,8 @@ CSRC = os.path.join(_HERE, "csrc")
 # Kernel name fragment -> source files whose text defines it.
 KERNEL_SOURCES = {
     "prefill_bf16_kernel": ("prefill.hip", "pa_device.h", "pa_internal.h"),
+    # the same kernel with the append fused in (its 4th template argument)
+    "prefill_bf16_kernel_fused": ("prefill.hip", "pa_device.h", "pa_internal.h"),
     "decode_split_kernel": ("decode.hip", "pa_device.h", "pa_internal.h"),
     "decode_reduce_kernel": ("decode.hip", "pa_device.h", "pa_internal.h"),
     "append_kernel": ("append.hip", "pa_device.h", "pa_internal.h"),
@@ -89,9 +91,10 @@ def traffic(args) -> dict:
     cwrite = _pick(counter_per_dispatch(args.copy_write, "WRITE_SIZE"), "copyBuffer")
     f_scale = args.copy_bytes / (cfetch * 1024.0)
     w_scale = args.copy_bytes / (cwrite * 1024.0)
-    rd = _pick(fetch, args.kernel) * 1024.0 * f_scale
-    wr = _pick(write, args.kernel) * 1024.0 * w_scale
-    return dict(kernel=args.kernel, source_hash=source_hash(args.kernel), workload=args.workload,
+    match = args.match or args.kernel
+    rd = _pick(fetch, match) * 1024.0 * f_scale
+    wr = _pick(write, match) * 1024.0 * w_scale
+    return dict(kernel=args.kernel, match=match, source_hash=source_hash(args.kernel), workload=args.workload,
                 read_bytes_per_launch=rd, write_bytes_per_launch=wr, hbm_bytes_per_launch=rd + wr,
                 fetch_scale=f_scale, write_scale=w_scale, copy_bytes=args.copy_bytes)
 
@@ -109,6 +112,9 @@ def main(argv=None) -> int:
         t.add_argument("--" + n, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--kernel", required=True, choices=sorted(KERNEL_SOURCES))
+    t.add_argument("--match", default=None,
+                   help="kernel-name fragment to select dispatches by (default: --kernel), e.g. "
+                        "'prefill_bf16_kernel<128, true, false, true>' for one instantiation")
     t.add_argument("--workload", required=True)
     t.add_argument("--out", required=True)
     args = ap.parse_args(argv)

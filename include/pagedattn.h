@@ -163,6 +163,34 @@ pa_status attn_prefill_paged(const void *q, const int32_t *cu_q, const pa_kv_cac
                              int32_t num_q_heads, float softmax_scale, int32_t causal,
                              int32_t window_left, void *out, float *lse, void *stream);
 
+/* attn_prefill_paged_append - kv_cache_append of the queries' own K/V rows
+ * followed by attn_prefill_paged over the grown context, in one pass: the
+ * prompt step of "大模型推理优化实战：KV Cache + Flash Attention" (KV Cache
+ * section: the new tokens' keys and values join the cache, then the queries
+ * attend over everything cached), with the paging of section 3.2 of the
+ * Flash Attention + Paged KV Cache page.  The result (out, lse and the page
+ * contents) is the same as calling kv_cache_append(cache, k_new, v_new,
+ * block_table, max_pages_per_seq, start_pos, cu_q, batch, max_q_len) with
+ * start_pos[b] = ctx_lens[b] - q_len_b and then attn_prefill_paged with the
+ * remaining arguments.
+ *   k_new, v_new : [cu_q[batch], num_kv_heads, head_dim], cache element type
+ *                (bf16 or fp32); row cu_q[b] + i is the key / value at
+ *                position ctx_lens[b] - q_len_b + i (the position of query
+ *                row i)
+ *   all other arguments: as attn_prefill_paged
+ * bf16 caches with page_size >= 64 run as one kernel that reads the new
+ * keys from k_new / v_new and writes them into their page slots; fp32
+ * caches and smaller pages run the append kernel and then the prefill on
+ * the same stream.  The slots of the new positions must not be read by
+ * another sequence of the same call (they are written during it).  int8
+ * caches: PA_ERR_UNSUPPORTED (as for attn_prefill_paged). */
+pa_status attn_prefill_paged_append(const void *q, const void *k_new, const void *v_new,
+                                    const int32_t *cu_q, const pa_kv_cache *cache,
+                                    const int32_t *block_table, int32_t max_pages_per_seq,
+                                    const int32_t *ctx_lens, int32_t batch, int32_t max_q_len,
+                                    int32_t num_q_heads, float softmax_scale, int32_t causal,
+                                    int32_t window_left, void *out, float *lse, void *stream);
+
 /* attn_decode_workspace_bytes - HOST function: bytes of workspace that
  * attn_decode_paged needs for these sizes (an upper bound; 0 on bad input). */
 size_t attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

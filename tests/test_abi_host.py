@@ -101,6 +101,32 @@ def test_prefill_empty_batch_is_ok_without_work():
     assert _prefill(_cache(), max_q_len=0) == 0
 
 
+def _prefill_append(cache, **kw):
+    lib = ops.load_library()
+    a = dict(q=FAKE, k_new=FAKE, v_new=FAKE, cu_q=FAKE, block_table=FAKE, max_pages=4, ctx=FAKE, batch=1,
+             max_q_len=8, hq=4, scale=0.1, causal=1, window=-1, out=FAKE, lse=None)
+    a.update(kw)
+    return lib.attn_prefill_paged_append(a["q"], a["k_new"], a["v_new"], a["cu_q"], ctypes.byref(cache),
+                                         a["block_table"], a["max_pages"], a["ctx"], a["batch"], a["max_q_len"],
+                                         a["hq"], a["scale"], a["causal"], a["window"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_new=None), 1), (dict(v_new=None), 1), (dict(hq=3), 1), (dict(scale=0.0), 1), (dict(causal=2), 1),
+    (dict(q=None), 1), (dict(out=None), 1), (dict(max_pages=0), 1), (dict(batch=-1), 1),
+])
+def test_prefill_append_rejects_bad_args(kw, status):
+    assert _prefill_append(_cache(), **kw) == status
+    assert _detail() != ""
+
+
+def test_prefill_append_rejects_bad_cache_and_allows_empty():
+    assert _prefill_append(_cache(dtype=ops.PA_I8)) == 2
+    assert _prefill_append(_cache(head_dim=96)) == 2
+    assert _prefill_append(_cache(), batch=0, q=None, out=None, k_new=None, v_new=None) == 0
+    assert _prefill_append(_cache(), max_q_len=0) == 0
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(hq=3), 1), (dict(scale=0.0), 1), (dict(q=None), 1), (dict(ws=None), 4), (dict(ws_bytes=16), 4),
     (dict(hq=2 * 17), 2),

@@ -1,0 +1,107 @@
+"""GPU parity of attn_prefill_paged_append (the new rows' K/V written into
+their pages and attended over in one call) against the CPU oracle's append
+followed by its attention, on seeded inputs: fresh prompts, chunks after a
+cached prefix whose first new position falls on a key-tile boundary, inside a
+tile and inside a query tile, windows, no mask, GQA and MHA, D = 64 / 128,
+and the caches that take the two-launch route (16-key pages, fp32).  Pools
+start as NaN, so a slot written twice, missed or written out of place shows
+up in the bit-exact page comparison."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flashattention_paged_kv_amd import ops
+from flashattention_paged_kv_amd import workloads as wl
+from gpu_cases import bits, check_close, f64, nan_pool, say
+
+pytestmark = pytest.mark.gpu
+
+# (workload over the whole sequences, cached prefix length per sequence)
+CASES = [
+    (wl.PrefillWorkload("fresh_d128_g4_p256", (1200, 300, 77), 8, 2, 128, 256, "bf16", seed=61), (0, 0, 0)),
+    # prefixes of 128 (tile-aligned), 64 (inside a query tile), 100 (inside a
+    # key tile) and 1 token; 64-key pages
+    (wl.PrefillWorkload("chunks_d128_g4_p64", (700, 520, 333, 129), 8, 2, 128, 64, "bf16", seed=62),
+     (128, 64, 100, 1)),
+    (wl.PrefillWorkload("chunks_d64_mha_p128", (513, 260, 64), 4, 4, 64, 128, "bf16", seed=63), (37, 250, 63)),
+    (wl.PrefillWorkload("chunk_g8_p256", (1030,), 8, 1, 128, 256, "bf16", seed=64), (511,)),
+    (wl.PrefillWorkload("window128_runs", (1500, 400), 4, 2, 128, 64, "bf16", seed=65, window_left=128), (0, 200)),
+    (wl.PrefillWorkload("window0_chunk", (300,), 4, 2, 128, 64, "bf16", seed=66, window_left=0), (90,)),
+    (wl.PrefillWorkload("noncausal_runs", (1100, 300), 2, 1, 128, 256, "bf16", seed=67, causal=False), (0, 70)),
+    (wl.PrefillWorkload("two_launch_p16", (300, 77), 8, 2, 128, 16, "bf16", seed=68), (0, 33)),
+    (wl.PrefillWorkload("two_launch_f32", (128, 45), 2, 1, 64, 64, "f32", seed=69), (0, 17)),
+]
+
+
+def _split(inp, w, prefix):
+    """Rows of the cached prefixes and rows of the new chunks, as ragged
+    batches (cu arrays) over the same sequences."""
+    cu = inp["cu_q"].tolist()
+    pre_rows, new_rows, cu_pre, cu_new = [], [], [0], [0]
+    for b, (n, s) in enumerate(zip(w.seq_lens, prefix)):
+        pre_rows += range(cu[b], cu[b] + s)
+        new_rows += range(cu[b] + s, cu[b] + n)
+        cu_pre.append(cu_pre[-1] + s)
+        cu_new.append(cu_new[-1] + n - s)
+    idx = lambda r: torch.tensor(r, dtype=torch.long)
+    return idx(pre_rows), idx(new_rows), torch.tensor(cu_pre, dtype=torch.int32), torch.tensor(cu_new, dtype=torch.int32)
+
+
+def _pools_with_prefix(w, inp, pre, cu_pre, prefix):
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    kp = nan_pool(inp["num_pages"], w.page_size, w.num_kv_heads, w.head_dim, tdt)
+    vp = nan_pool(inp["num_pages"], w.page_size, w.num_kv_heads, w.head_dim, tdt)
+    cache = ops.KVCache(kp, vp)
+    if max(prefix) > 0:
+        ops.kv_cache_append(cache, inp["k"][pre].cuda(), inp["v"][pre].cuda(), inp["block_table"].cuda(),
+                            torch.zeros(w.batch, dtype=torch.int32).cuda(), cu_pre.cuda(), max_new=max(prefix))
+    return cache, kp, vp
+
+
+@pytest.mark.parametrize("w,prefix", CASES, ids=[c[0].name for c in CASES])
+def test_prefill_append_matches_oracle(w, prefix):
+    say(f"prefill_append {w.name} lens={w.seq_lens} prefix={prefix}")
+    inp = wl.prefill_inputs(w)
+    pre, new, cu_pre, cu_new = _split(inp, w, prefix)
+    q_new, k_new, v_new = inp["q"][new], inp["k"][new], inp["v"][new]
+    bt, ctx = inp["block_table"].cuda(), inp["ctx_lens"].cuda()
+    max_q = max(n - s for n, s in zip(w.seq_lens, prefix))
+
+    cache, kp, vp = _pools_with_prefix(w, inp, pre, cu_pre, prefix)
+    out, lse = ops.attn_prefill_paged_append(q_new.cuda(), k_new.cuda(), v_new.cuda(), cu_new.cuda(), cache, bt, ctx,
+                                             max_q_len=max_q, softmax_scale=w.softmax_scale, causal=w.causal,
+                                             window_left=w.window_left, return_lse=True)
+    torch.cuda.synchronize()
+
+    # Pages: the oracle's scatter of every row of every sequence into NaN pages.
+    shape = (inp["num_pages"], w.page_size, w.num_kv_heads, w.head_dim)
+    nan_bits = bits(torch.full(shape, float("nan"), dtype=kp.dtype))
+    ek, ev = oracle.append_pages(nan_bits, nan_bits.copy(), bits(inp["k"]), bits(inp["v"]),
+                                 inp["block_table"].numpy(), inp["start_pos"].numpy(), inp["cu_q"].numpy(),
+                                 w.page_size)
+    assert np.array_equal(bits(kp), ek), "K pages differ from the oracle's append"
+    assert np.array_equal(bits(vp), ev), "V pages differ from the oracle's append"
+
+    # Output: the oracle's attention of the new rows over the whole context.
+    view = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    kp64 = torch.from_numpy(ek).view(view).double().numpy()
+    vp64 = torch.from_numpy(ev).view(view).double().numpy()
+    ref, ref_lse = oracle.attention_paged(f64(q_new), cu_new.numpy(), kp64, vp64, inp["block_table"].numpy(),
+                                          inp["ctx_lens"].numpy(), w.page_size, w.softmax_scale, w.causal,
+                                          w.window_left)
+    check_close(out, ref, w.dtype, "out")
+    err = np.abs(f64(lse) - ref_lse).max()
+    say(f"  lse max|d|={err:.3e}")
+    assert err <= (1e-4 if w.dtype == "f32" else 1e-3)
+
+    # The separate calls (append at ctx - q_len, then prefill) give the same bits.
+    cache2, _, _ = _pools_with_prefix(w, inp, pre, cu_pre, prefix)
+    start = torch.tensor(prefix, dtype=torch.int32).cuda()
+    ops.kv_cache_append(cache2, k_new.cuda(), v_new.cuda(), bt, start, cu_new.cuda(), max_new=max_q)
+    out2, lse2 = ops.attn_prefill_paged(q_new.cuda(), cu_new.cuda(), cache2, bt, ctx, max_q_len=max_q,
+                                        softmax_scale=w.softmax_scale, causal=w.causal, window_left=w.window_left,
+                                        return_lse=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), bits(out2)), "fused and separate calls differ"
+    assert np.array_equal(bits(lse), bits(lse2))
