@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/pagedattn.h"
@@ -163,6 +164,23 @@ static pa_status prefill_args(const void *q, const int32_t *cu_q, const pa_kv_ca
   return ok();
 }
 
+// attn_prefill_paged_append on a bf16 cache with pages of >= 64 keys: one
+// fused kernel, or the append kernel and then the prefill.  Same result
+// either way; the choice follows measured times on MI355X (L = 1k..32k, 32
+// heads, D = 128): with a causal mask and no window (pairs of query tiles)
+// the fused kernel wins up to about 12k query rows and loses beyond (its
+// page stores cost more than the separate copy); with a window or no mask
+// (runs of query tiles) it loses below about 4k rows and wins above.
+// PA_PREFILL_APPEND_ROUTE=fused|separate in the environment forces a route
+// (tests use it to cover both kernels at small sizes).
+static bool prefill_append_fused(int32_t causal, int32_t window_left, int32_t max_q_len) {
+  const char *route = getenv("PA_PREFILL_APPEND_ROUTE");
+  if (route != nullptr && strcmp(route, "fused") == 0) return true;
+  if (route != nullptr && strcmp(route, "separate") == 0) return false;
+  const bool pairs = causal != 0 && window_left < 0;
+  return pairs ? max_q_len <= 12288 : max_q_len > 4096;
+}
+
 extern "C" {
 
 int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
@@ -260,6 +278,12 @@ pa_status attn_prefill_paged(const void *q, const int32_t *cu_q, const pa_kv_cac
   return hip_status(pa::launch_prefill(a, (hipStream_t)stream), "attn_prefill_paged launch");
 }
 
+int32_t attn_prefill_append_is_fused(const pa_kv_cache *cache, int32_t causal, int32_t window_left,
+                                     int32_t max_q_len) {
+  return cache != nullptr && cache->dtype == PA_BF16 && cache->page_size >= 64 &&
+         prefill_append_fused(causal, window_left, max_q_len);
+}
+
 pa_status attn_prefill_paged_append(const void *q, const void *k_new, const void *v_new, const int32_t *cu_q,
                                     const pa_kv_cache *cache, const int32_t *block_table, int32_t max_pages_per_seq,
                                     const int32_t *ctx_lens, int32_t batch, int32_t max_q_len, int32_t num_q_heads,
@@ -273,13 +297,14 @@ pa_status attn_prefill_paged_append(const void *q, const void *k_new, const void
   if (!empty && (k_new == nullptr || v_new == nullptr)) return fail(PA_ERR_INVALID_ARG, "NULL pointer argument");
   if (empty) return ok();
   const hipStream_t s = (hipStream_t)stream;
-  if (cache->dtype == PA_BF16 && cache->page_size >= 64) {
+  if (attn_prefill_append_is_fused(cache, causal, window_left, max_q_len)) {
     a.k_new = k_new;
     a.v_new = v_new;
     return hip_status(pa::launch_prefill(a, s), "attn_prefill_paged_append launch");
   }
-  // Other caches (fp32, or pages smaller than a key tile): the append kernel
-  // (start = ctx_lens[b] - q_len_b) and then the prefill, on the same stream.
+  // Other caches (fp32, or pages smaller than a key tile), and the lengths
+  // where two launches are faster: the append kernel (start = ctx_lens[b] -
+  // q_len_b) and then the prefill, on the same stream.
   pa::AppendArgs ap;
   ap.k_pages = cache->k_pages;
   ap.v_pages = cache->v_pages;

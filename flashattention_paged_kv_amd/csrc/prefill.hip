@@ -98,25 +98,31 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   const int gam = lane >> 4;
   const int tp = lane & 15;
 
+  // Everything the prologue needs from memory (sequence bounds, context
+  // length and, in pair mode, the page of key tile 0, which is every
+  // engine's first tile there: causal, no window) is read first, in one
+  // round trip; readfirstlane keeps these values, and every tile decision
+  // derived from them, in scalar registers, and keeps the loads above the
+  // branches below.
+  const int b = blockIdx.z;
+  const int q0 = __builtin_amdgcn_readfirstlane(a.cu_q[b]);
+  const int q_len = __builtin_amdgcn_readfirstlane(a.cu_q[b + 1]) - q0;
+  const int ctx = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
+  const int pg0 = RUNS ? 0 : __builtin_amdgcn_readfirstlane(block_table[(size_t)b * a.max_pages]);
+  const int grid_x = gridDim.x, grid_y = gridDim.y;
   // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
   // L2): consecutive ids are remapped so that the pairs of one query head run
   // on one XCD and stream that head's K/V tiles together.
   int pair = blockIdx.x;  // pair mode: the pair index; run mode: the run index
   int h = blockIdx.y;
-  const int b = blockIdx.z;
-  if ((gridDim.y & 7) == 0) {
-    const int k = blockIdx.x + gridDim.x * blockIdx.y;  // id inside this sequence
+  if ((grid_y & 7) == 0) {
+    const int k = blockIdx.x + grid_x * blockIdx.y;  // id inside this sequence
     const int k8 = k >> 3;
-    h = (k & 7) + 8 * (k8 / gridDim.x);
-    pair = k8 % gridDim.x;
+    h = (k & 7) + 8 * (k8 / grid_x);
+    pair = k8 % grid_x;
   }
-  // Sequence geometry is the same for every lane: readfirstlane keeps it
-  // (and every tile decision derived from it) in scalar registers.
-  const int q0 = __builtin_amdgcn_readfirstlane(a.cu_q[b]);
-  const int q_len = __builtin_amdgcn_readfirstlane(a.cu_q[b + 1]) - q0;
   const int n_qt = (q_len + kPfRows - 1) / kPfRows;
   if (RUNS ? pair * kPfRun >= n_qt : pair >= (n_qt + 1) / 2) return;  // uniform
-  const int ctx = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
   const int off = ctx - q_len;
   const int hk = h / a.group;
   const int W = a.window_left;
@@ -525,13 +531,16 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       m = m_new;
     }
     const float neg_m = m == -INFINITY ? 0.f : -m;
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    float ps[4];  // four partial row sums, each started at its first term
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = fast_exp2(fmaf(sacc[kb][i], a.scale_log2, neg_m));
-        ps[i & 3] += p;
+        if (kb == 0 && i < 4)
+          ps[i] = p;
+        else
+          ps[i & 3] += p;
         sacc[kb][i] = p;
       }
     lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
@@ -562,7 +571,13 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   if (n_mine > 0) {
     int qt, kt;
     my_item(0, qt, kt);
-    load_tile(kt);
+    if (!RUNS && BIG_PAGE && kt == 0) {
+      pk_off = (size_t)pg0 * P * row_bytes;
+      load_half(kt, pk_off, kbase, knew, pk);
+      load_half(kt, pk_off, vbase, vnew, pv);
+    } else {
+      load_tile(kt);
+    }
     u32x4 qs[kQLoads];
 #pragma unroll
     for (int i = 0; i < kQLoads; ++i) {

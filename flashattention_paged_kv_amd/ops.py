@@ -48,6 +48,7 @@ class _Cache(ctypes.Structure):
 _lib = None
 
 EXPORTED = ("kv_cache_append", "kv_pages_quantize_int8", "attn_prefill_paged", "attn_prefill_paged_append",
+            "attn_prefill_append_is_fused",
             "attn_decode_workspace_bytes",
             "attn_decode_paged", "attn_decode_layered_workspace_bytes", "attn_decode_paged_layered",
             "kv_cache_copy_pages", "attn_backward_workspace_bytes", "attn_backward_paged", "pa_pool_create", "pa_pool_destroy", "pa_pool_extend", "pa_pool_fork",
@@ -69,6 +70,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kv_pages_quantize_int8.argtypes = [P, P, P, I32, I32, I32, I32, P]
     lib.attn_prefill_paged.argtypes = [P, P, CP, P, I32, P, I32, I32, I32, F32, I32, I32, P, P, P]
     lib.attn_prefill_paged_append.argtypes = [P, P, P, P, CP, P, I32, P, I32, I32, I32, F32, I32, I32, P, P, P]
+    lib.attn_prefill_append_is_fused.argtypes = [CP, I32, I32, I32]
+    lib.attn_prefill_append_is_fused.restype = I32
     lib.attn_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.attn_decode_workspace_bytes.restype = SZ
     lib.attn_decode_paged.argtypes = [P, CP, P, I32, P, I32, I32, F32, I32, P, P, P, SZ, P]
@@ -261,6 +264,14 @@ def attn_prefill_paged_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch
                                          max_q_len, hq, scale, int(bool(causal)), int(window_left), _ptr(out),
                                          _ptr(lse), _stream()))
     return (out, lse) if return_lse else out
+
+
+def prefill_append_is_fused(cache: KVCache, causal: bool = True, window_left: int = -1,
+                            max_q_len: int = 1) -> bool:
+    """Whether attn_prefill_paged_append runs as one fused kernel for these
+    arguments (else: the append kernel, then the prefill)."""
+    return bool(load_library().attn_prefill_append_is_fused(ctypes.byref(cache._struct()), int(bool(causal)),
+                                                            int(window_left), int(max_q_len)))
 
 
 def decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

@@ -178,10 +178,10 @@ pa_status attn_prefill_paged(const void *q, const int32_t *cu_q, const pa_kv_cac
  *                position ctx_lens[b] - q_len_b + i (the position of query
  *                row i)
  *   all other arguments: as attn_prefill_paged
- * bf16 caches with page_size >= 64 run as one kernel that reads the new
- * keys from k_new / v_new and writes them into their page slots; fp32
- * caches and smaller pages run the append kernel and then the prefill on
- * the same stream.  The slots of the new positions must not be read by
+ * bf16 caches with page_size >= 64 run, at the lengths where it is faster
+ * (attn_prefill_append_is_fused), as one kernel that reads the new keys
+ * from k_new / v_new and writes them into their page slots; otherwise the
+ * append kernel and then the prefill run on the same stream.  The slots of the new positions must not be read by
  * another sequence of the same call (they are written during it).  int8
  * caches: PA_ERR_UNSUPPORTED (as for attn_prefill_paged). */
 pa_status attn_prefill_paged_append(const void *q, const void *k_new, const void *v_new,
@@ -190,6 +190,16 @@ pa_status attn_prefill_paged_append(const void *q, const void *k_new, const void
                                     const int32_t *ctx_lens, int32_t batch, int32_t max_q_len,
                                     int32_t num_q_heads, float softmax_scale, int32_t causal,
                                     int32_t window_left, void *out, float *lse, void *stream);
+
+/* attn_prefill_append_is_fused - HOST function: 1 if attn_prefill_paged_append
+ * with this cache and these arguments runs as one fused kernel, 0 if it runs
+ * the append kernel and then the prefill (same result either way).  The
+ * fused kernel needs a bf16 cache with page_size >= 64; beyond that the
+ * choice follows measured times (causal without a window: up to 12288 query
+ * rows; a window or no mask: more than 4096), and the environment variable
+ * PA_PREFILL_APPEND_ROUTE=fused or =separate overrides it.  NULL cache: 0. */
+int32_t attn_prefill_append_is_fused(const pa_kv_cache *cache, int32_t causal, int32_t window_left,
+                                     int32_t max_q_len);
 
 /* attn_decode_workspace_bytes - HOST function: bytes of workspace that
  * attn_decode_paged needs for these sizes (an upper bound; 0 on bad input). */

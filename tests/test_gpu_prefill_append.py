@@ -3,9 +3,10 @@ their pages and attended over in one call) against the CPU oracle's append
 followed by its attention, on seeded inputs: fresh prompts, chunks after a
 cached prefix whose first new position falls on a key-tile boundary, inside a
 tile and inside a query tile, windows, no mask, GQA and MHA, D = 64 / 128,
-and the caches that take the two-launch route (16-key pages, fp32).  Pools
-start as NaN, so a slot written twice, missed or written out of place shows
-up in the bit-exact page comparison."""
+and the caches that always take the two-launch route (16-key pages, fp32);
+each with the route forced to the fused kernel, forced to two launches, and
+left to the library.  Pools start as NaN, so a slot written twice, missed or
+written out of place shows up in the bit-exact page comparison."""
 import numpy as np
 import pytest
 import torch
@@ -59,9 +60,16 @@ def _pools_with_prefix(w, inp, pre, cu_pre, prefix):
     return cache, kp, vp
 
 
+@pytest.mark.parametrize("route", ["fused", "separate", "auto"])
 @pytest.mark.parametrize("w,prefix", CASES, ids=[c[0].name for c in CASES])
-def test_prefill_append_matches_oracle(w, prefix):
-    say(f"prefill_append {w.name} lens={w.seq_lens} prefix={prefix}")
+def test_prefill_append_matches_oracle(w, prefix, route, monkeypatch):
+    """route: the library's choice between its fused kernel and two launches,
+    forced either way (both must give the same result), or left to it."""
+    if route == "auto":
+        monkeypatch.delenv("PA_PREFILL_APPEND_ROUTE", raising=False)
+    else:
+        monkeypatch.setenv("PA_PREFILL_APPEND_ROUTE", route)
+    say(f"prefill_append {w.name} route={route} lens={w.seq_lens} prefix={prefix}")
     inp = wl.prefill_inputs(w)
     pre, new, cu_pre, cu_new = _split(inp, w, prefix)
     q_new, k_new, v_new = inp["q"][new], inp["k"][new], inp["v"][new]
