@@ -168,17 +168,17 @@ static pa_status prefill_args(const void *q, const int32_t *cu_q, const pa_kv_ca
 // fused kernel, or the append kernel and then the prefill.  Same result
 // either way; the choice follows measured times on MI355X (L = 1k..32k, 32
 // heads, D = 128): with a causal mask and no window (pairs of query tiles)
-// the fused kernel wins up to about 12k query rows and loses beyond (its
-// page stores cost more than the separate copy); with a window or no mask
-// (runs of query tiles) it loses below about 4k rows and wins above.
-// PA_PREFILL_APPEND_ROUTE=fused|separate in the environment forces a route
-// (tests use it to cover both kernels at small sizes).
+// the fused kernel wins up to about 6k query rows and is level or behind
+// beyond (its page stores cost more than the separate copy); with a window
+// or no mask (runs of query tiles) it is level or ahead at every length.
+// PAGEDATTN_PREFILL_APPEND_ROUTE=fused|separate in the environment forces a
+// route (tests use it to cover both kernels at small sizes).
 static bool prefill_append_fused(int32_t causal, int32_t window_left, int32_t max_q_len) {
-  const char *route = getenv("PA_PREFILL_APPEND_ROUTE");
+  const char *route = getenv("PAGEDATTN_PREFILL_APPEND_ROUTE");
   if (route != nullptr && strcmp(route, "fused") == 0) return true;
   if (route != nullptr && strcmp(route, "separate") == 0) return false;
   const bool pairs = causal != 0 && window_left < 0;
-  return pairs ? max_q_len <= 12288 : max_q_len > 4096;
+  return pairs ? max_q_len <= 6144 : true;
 }
 
 extern "C" {

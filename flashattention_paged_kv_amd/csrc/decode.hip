@@ -49,20 +49,13 @@ constexpr int kDecWaves = 8;
 constexpr int kDecTile = 32;            // keys per wave iteration
 constexpr int kDecWgsPerCu = 1;         // resident split workgroups per CU (register bound)
 
-// kDecWgsPerCu workgroups per CU of the current device (the split kernel's
-// occupancy, so the whole grid is resident at once), cached per device.  PAGEDATTN_DECODE_WGS overrides it (tests use
-// it to exercise other partitions of the same work).
-int decode_grid_size() {
-  if (const char *env = getenv("PAGEDATTN_DECODE_WGS")) {
-    const int v = atoi(env);
-    if (v >= 1 && v <= 65536) return v;
-  }
+int device_cu_count() {
   // Without a queryable device (host-only use of the argument checks) the
-  // size is that of an MI355X: 256 CUs.
+  // count is that of an MI355X.
   constexpr int kDefaultCus = 256;
   static std::atomic<int> cached[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kDecWgsPerCu * kDefaultCus;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kDefaultCus;
   int v = cached[dev].load(std::memory_order_relaxed);
   if (v == 0) {
     int cus = 0;
@@ -71,7 +64,18 @@ int decode_grid_size() {
     v = cus;
     cached[dev].store(v, std::memory_order_relaxed);
   }
-  return kDecWgsPerCu * v;
+  return v;
+}
+
+// kDecWgsPerCu workgroups per CU of the current device (the split kernel's
+// occupancy, so the whole grid is resident at once).  PAGEDATTN_DECODE_WGS
+// overrides it (tests use it to exercise other partitions of the same work).
+int decode_grid_size() {
+  if (const char *env = getenv("PAGEDATTN_DECODE_WGS")) {
+    const int v = atoi(env);
+    if (v >= 1 && v <= 65536) return v;
+  }
+  return kDecWgsPerCu * device_cu_count();
 }
 
 // Tiles of 32 keys that a decode query at position ctx - 1 reads: from the

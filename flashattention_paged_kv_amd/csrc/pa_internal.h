@@ -92,6 +92,7 @@ struct PrefillArgs {
   // writes them into their page slots (c.k / c.v).  NULL: no append.
   const void *k_new;
   const void *v_new;
+  int run_tiles;  // set by the launcher: query tiles per run-mode workgroup
 };
 
 struct DecodeArgs {
@@ -142,6 +143,9 @@ struct BackwardArgs {
   float *delta;              // workspace [total_q, num_q_heads]: dO . O
 };
 
+// Compute units of the current device (256 on an MI355X; also the answer
+// when no device can be queried), cached per device.
+int device_cu_count();
 // Decode grid size (workgroups) on the current device, used by both the
 // workspace query and the call.
 int decode_grid_size();

@@ -46,7 +46,9 @@
 // maximum by at most that much: probabilities stay <= 256, and O and l share
 // the reference, so the result is the same attention).
 #include <math.h>
+#include <stdlib.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -60,7 +62,7 @@ constexpr int kPfRows = 128;         // query rows per query tile (4 waves x 32)
 constexpr int kPfKeys = 64;          // keys per key tile
 constexpr int kPfEngineThreads = 256;
 constexpr float kPfSlack = 8.f;      // log2 of the largest probability allowed
-constexpr int kPfRun = 8;            // query tiles per workgroup in run mode
+constexpr int kPfRun = 8;            // most query tiles per workgroup in run mode (a.run_tiles <= this)
 
 template <int D>
 struct PfCfg {
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     pair = k8 % grid_x;
   }
   const int n_qt = (q_len + kPfRows - 1) / kPfRows;
-  if (RUNS ? pair * kPfRun >= n_qt : pair >= (n_qt + 1) / 2) return;  // uniform
+  if (RUNS ? pair * a.run_tiles >= n_qt : pair >= (n_qt + 1) / 2) return;  // uniform
   const int off = ctx - q_len;
   const int hk = h / a.group;
   const int W = a.window_left;
@@ -182,17 +184,18 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     }
   } else {
     // Run mode (a window, or no causal mask: about the same work for every
-    // query tile): kPfRun consecutive query tiles.  Engine 0 takes the first
-    // half of their items in order; engine 1 takes the second half with its
-    // query tiles in reverse order, so that the tile holding the split comes
-    // last for both.
-    const int q_begin = pair * kPfRun;
+    // query tile): a.run_tiles (<= kPfRun) consecutive query tiles.  Engine
+    // 0 takes the first half of their items in order; engine 1 takes the
+    // second half with its query tiles in reverse order, so that the tile
+    // holding the split comes last for both.
+    const int rt = a.run_tiles;
+    const int q_begin = pair * rt;
     int lo[kPfRun], cum[kPfRun + 1];
     cum[0] = 0;
 #pragma unroll
     for (int r = 0; r < kPfRun; ++r) {
       int l = 0, hh = 0;
-      if (q_begin + r < n_qt) tile_range(q_begin + r, l, hh);
+      if (r < rt && q_begin + r < n_qt) tile_range(q_begin + r, l, hh);
       lo[r] = l;
       cum[r + 1] = cum[r] + (hh - l);
     }
@@ -742,14 +745,31 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     merge(std::integral_constant<int, 1>{});
 }
 
-hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
-  if (a.batch == 0 || a.max_q_len == 0) return hipSuccess;
-  if (a.c.dtype == 0) return launch_rowwise_f32(a, s);
+// Query tiles per run-mode workgroup: as many as kPfRun (fewer, longer
+// workgroups: a 128-key window at 8192 rows ran 121 us with 8 tiles against
+// 132 us with 4) while the grid still has a workgroup per CU, down to one
+// for short prompts (the same window at 1024 rows: 66 us with 8, 25 with 1).  PAGEDATTN_PREFILL_RUN_TILES (1..8) overrides it
+// (tests use it to cover every run length on small inputs).
+static int prefill_run_tiles(int n_qt, int heads, int batch) {
+  if (const char *env = getenv("PAGEDATTN_PREFILL_RUN_TILES")) {
+    const int v = atoi(env);
+    if (v >= 1 && v <= kPfRun) return v;
+  }
+  const long long tiles = (long long)n_qt * heads * batch;
+  return (int)std::min<long long>(kPfRun, std::max<long long>(1, tiles / device_cu_count()));
+}
+
+hipError_t launch_prefill(const PrefillArgs &a_in, hipStream_t s) {
+  if (a_in.batch == 0 || a_in.max_q_len == 0) return hipSuccess;
+  if (a_in.c.dtype == 0) return launch_rowwise_f32(a_in, s);
+  PrefillArgs a = a_in;
   const int n_qt = (a.max_q_len + kPfRows - 1) / kPfRows;
   // Causal without a window: pairs (p, n-1-p) balance the triangle.  A window
-  // or no mask gives every query tile about the same work: runs of kPfRun.
+  // or no mask gives every query tile about the same work: runs of
+  // run_tiles query tiles.
   const bool runs = !(a.causal && a.window_left < 0);
-  dim3 grid(runs ? (n_qt + kPfRun - 1) / kPfRun : (n_qt + 1) / 2, a.num_q_heads, a.batch);
+  a.run_tiles = runs ? prefill_run_tiles(n_qt, a.num_q_heads, a.batch) : 1;
+  dim3 grid(runs ? (n_qt + a.run_tiles - 1) / a.run_tiles : (n_qt + 1) / 2, a.num_q_heads, a.batch);
   const dim3 block(2 * kPfEngineThreads);
   const bool big = a.c.page_size >= kPfKeys;
 #define PA_PREFILL_LAUNCH(DD, BIG, RUN) \

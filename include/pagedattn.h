@@ -195,9 +195,9 @@ pa_status attn_prefill_paged_append(const void *q, const void *k_new, const void
  * with this cache and these arguments runs as one fused kernel, 0 if it runs
  * the append kernel and then the prefill (same result either way).  The
  * fused kernel needs a bf16 cache with page_size >= 64; beyond that the
- * choice follows measured times (causal without a window: up to 12288 query
- * rows; a window or no mask: more than 4096), and the environment variable
- * PA_PREFILL_APPEND_ROUTE=fused or =separate overrides it.  NULL cache: 0. */
+ * choice follows measured times (causal without a window: up to 6144 query
+ * rows; a window or no mask: always), and the environment variable
+ * PAGEDATTN_PREFILL_APPEND_ROUTE=fused or =separate overrides it.  NULL cache: 0. */
 int32_t attn_prefill_append_is_fused(const pa_kv_cache *cache, int32_t causal, int32_t window_left,
                                      int32_t max_q_len);
 

@@ -252,15 +252,16 @@ def test_prefill_append_route_query(monkeypatch):
     fused kernel only for bf16 caches with pages of >= 64 keys, at the
     lengths where it is measured faster, unless the environment forces it."""
     lib = ops.load_library()
-    monkeypatch.delenv("PA_PREFILL_APPEND_ROUTE", raising=False)
+    monkeypatch.delenv("PAGEDATTN_PREFILL_APPEND_ROUTE", raising=False)
     bf = _cache(page_size=256)
     q = lambda c, causal, win, n: lib.attn_prefill_append_is_fused(ctypes.byref(c), causal, win, n)
-    assert q(bf, 1, -1, 2048) == 1 and q(bf, 1, -1, 12288) == 1 and q(bf, 1, -1, 32768) == 0
-    assert q(bf, 1, 128, 1024) == 0 and q(bf, 1, 128, 32768) == 1 and q(bf, 0, -1, 8192) == 1
+    assert q(bf, 1, -1, 2048) == 1 and q(bf, 1, -1, 6144) == 1 and q(bf, 1, -1, 6145) == 0
+    assert q(bf, 1, -1, 32768) == 0
+    assert q(bf, 1, 128, 1024) == 1 and q(bf, 1, 128, 32768) == 1 and q(bf, 0, -1, 8192) == 1
     assert q(_cache(page_size=16), 1, -1, 2048) == 0
     assert q(_cache(page_size=64, dtype=ops.PA_F32), 1, -1, 2048) == 0
     assert lib.attn_prefill_append_is_fused(None, 1, -1, 2048) == 0
-    monkeypatch.setenv("PA_PREFILL_APPEND_ROUTE", "fused")
+    monkeypatch.setenv("PAGEDATTN_PREFILL_APPEND_ROUTE", "fused")
     assert q(bf, 1, -1, 32768) == 1 and q(_cache(page_size=16), 1, -1, 2048) == 0
-    monkeypatch.setenv("PA_PREFILL_APPEND_ROUTE", "separate")
+    monkeypatch.setenv("PAGEDATTN_PREFILL_APPEND_ROUTE", "separate")
     assert q(bf, 1, -1, 2048) == 0

@@ -77,6 +77,26 @@ def test_prefill_matches_oracle(w):
     assert err <= (1e-4 if w.dtype == "f32" else 1e-3)
 
 
+RUN_MODE_CASES = [w for w in PREFILL_CASES if w.name in ("bf16_win200_runs", "bf16_noncausal_runs",
+                                                           "bf16_d128_g8_win128")]
+
+
+@pytest.mark.parametrize("run_tiles", [2, 3, 8])
+@pytest.mark.parametrize("w", RUN_MODE_CASES, ids=lambda w: w.name)
+def test_prefill_run_lengths_match_oracle(w, run_tiles, monkeypatch):
+    """Windowed and unmasked prefill give each workgroup a run of query
+    tiles, as many as the grid allows (one on inputs this small); forced run
+    lengths cover longer runs, partial last runs and the engines' split."""
+    monkeypatch.setenv("PAGEDATTN_PREFILL_RUN_TILES", str(run_tiles))
+    say(f"prefill {w.name} run_tiles={run_tiles}")
+    run = PrefillRun(w)
+    out, lse = run.run()
+    torch.cuda.synchronize()
+    ref, ref_lse = run.oracle()
+    check_close(out, ref, w.dtype, "out")
+    assert np.abs(f64(lse) - ref_lse).max() <= 1e-3
+
+
 def test_chunked_prefill_rows_at_the_end_of_a_context():
     """q_len < ctx: the queries are the last rows of a longer cached context
     (bottom-right causal alignment)."""

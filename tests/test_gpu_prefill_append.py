@@ -66,9 +66,9 @@ def test_prefill_append_matches_oracle(w, prefix, route, monkeypatch):
     """route: the library's choice between its fused kernel and two launches,
     forced either way (both must give the same result), or left to it."""
     if route == "auto":
-        monkeypatch.delenv("PA_PREFILL_APPEND_ROUTE", raising=False)
+        monkeypatch.delenv("PAGEDATTN_PREFILL_APPEND_ROUTE", raising=False)
     else:
-        monkeypatch.setenv("PA_PREFILL_APPEND_ROUTE", route)
+        monkeypatch.setenv("PAGEDATTN_PREFILL_APPEND_ROUTE", route)
     say(f"prefill_append {w.name} route={route} lens={w.seq_lens} prefix={prefix}")
     inp = wl.prefill_inputs(w)
     pre, new, cu_pre, cu_new = _split(inp, w, prefix)
@@ -113,3 +113,13 @@ def test_prefill_append_matches_oracle(w, prefix, route, monkeypatch):
     torch.cuda.synchronize()
     assert np.array_equal(bits(out), bits(out2)), "fused and separate calls differ"
     assert np.array_equal(bits(lse), bits(lse2))
+
+
+@pytest.mark.parametrize("run_tiles", [3, 8])
+@pytest.mark.parametrize("w,prefix", [c for c in CASES if c[0].name in ("window128_runs", "noncausal_runs")],
+                         ids=lambda c: getattr(c, "name", None))
+def test_prefill_append_run_lengths(w, prefix, run_tiles, monkeypatch):
+    """The fused kernel in run mode with longer runs than the grid size picks
+    for these small inputs: same pages and output as the oracle."""
+    monkeypatch.setenv("PAGEDATTN_PREFILL_RUN_TILES", str(run_tiles))
+    test_prefill_append_matches_oracle(w, prefix, "fused", monkeypatch)
