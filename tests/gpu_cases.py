@@ -52,9 +52,10 @@ def nan_pool(num_pages, page_size, hkv, d, dtype, device="cuda"):
 
 class PrefillRun:
     """Append a prefill workload's K/V into NaN-filled pages and run prefill
-    on the GPU; keeps what the oracle needs."""
+    on the GPU; keeps what the oracle needs.  fused=True: no separate append;
+    run() calls attn_prefill_paged_append, which writes the pages itself."""
 
-    def __init__(self, w: wl.PrefillWorkload, ctx_extra=None):
+    def __init__(self, w: wl.PrefillWorkload, ctx_extra=None, fused: bool = False):
         inp = wl.prefill_inputs(w)
         self.w, self.inp = w, inp
         tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
@@ -65,14 +66,33 @@ class PrefillRun:
         self.bt = inp["block_table"].to(dev)
         self.cu = inp["cu_q"].to(dev)
         self.ctx = inp["ctx_lens"].to(dev)
-        ops.kv_cache_append(self.cache, inp["k"].to(dev), inp["v"].to(dev), self.bt, inp["start_pos"].to(dev),
-                            self.cu, max_new=max(w.seq_lens))
+        self.fused = fused
+        if fused:
+            self.k, self.v = inp["k"].to(dev), inp["v"].to(dev)
+        else:
+            ops.kv_cache_append(self.cache, inp["k"].to(dev), inp["v"].to(dev), self.bt, inp["start_pos"].to(dev),
+                                self.cu, max_new=max(w.seq_lens))
         self.q = inp["q"].to(dev)
 
     def run(self, return_lse=True):
+        if self.fused:
+            return ops.attn_prefill_paged_append(self.q, self.k, self.v, self.cu, self.cache, self.bt, self.ctx,
+                                                 max_q_len=max(self.w.seq_lens), softmax_scale=self.w.softmax_scale,
+                                                 causal=self.w.causal, window_left=self.w.window_left,
+                                                 return_lse=return_lse)
         return ops.attn_prefill_paged(self.q, self.cu, self.cache, self.bt, self.ctx, max_q_len=max(self.w.seq_lens),
                                       softmax_scale=self.w.softmax_scale, causal=self.w.causal,
                                       window_left=self.w.window_left, return_lse=return_lse)
+
+    def pages_match_oracle_append(self) -> bool:
+        """The K and V pools, bit for bit, against the oracle's append of every
+        row into NaN pages."""
+        w, inp = self.w, self.inp
+        nan_bits = bits(torch.full(tuple(self.k_pool.shape), float("nan"), dtype=self.k_pool.dtype))
+        ek, ev = oracle.append_pages(nan_bits, nan_bits.copy(), bits(inp["k"]), bits(inp["v"]),
+                                     inp["block_table"].numpy(), inp["start_pos"].numpy(), inp["cu_q"].numpy(),
+                                     w.page_size)
+        return np.array_equal(bits(self.k_pool), ek) and np.array_equal(bits(self.v_pool), ev)
 
     def oracle_pools(self):
         """The pools as the oracle's own append makes them (from NaN pages)."""

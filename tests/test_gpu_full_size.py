@@ -45,6 +45,22 @@ def test_llama7b_prefill_2048_full_oracle():
     assert np.abs(f64(lse) - ref_lse).max() <= 1e-3
 
 
+def test_llama7b_prompt_step_2048_fused_full_oracle():
+    """The step the benchmark times: attn_prefill_paged_append (one fused
+    kernel at this length) writes the pages and attends; every output and
+    every page slot against the oracle."""
+    w = wl.LLAMA7B_PREFILL
+    say(f"full size, fused append: {w.name}")
+    run = PrefillRun(w, fused=True)
+    assert ops.prefill_append_is_fused(run.cache, w.causal, w.window_left, max(w.seq_lens))
+    out, lse = run.run()
+    torch.cuda.synchronize()
+    assert run.pages_match_oracle_append(), "pages differ from the oracle's append"
+    ref, ref_lse = run.oracle()
+    check_close(out, ref, "bf16", "all rows, all heads")
+    assert np.abs(f64(lse) - ref_lse).max() <= 1e-3
+
+
 def test_llama70b_gqa_decode_full_oracle():
     w = wl.LLAMA70B_DECODE
     say(f"full size: {w.name}")
@@ -64,6 +80,18 @@ def test_long_prefill_32k_sampled_rows(w):
     say(f"full size: {w.name}")
     run = PrefillRun(w)
     _sampled_rows_check(run, ROWS_32K, [0, 13, 31])
+
+
+def test_long_window_prompt_step_32k_fused_sampled_rows():
+    """The 128-key-window step at 32k rows as the benchmark times it (the
+    fused kernel): sampled rows against the oracle, every page slot bit for
+    bit."""
+    w = wl.LONG_PREFILL_WINDOW
+    say(f"full size, fused append: {w.name}")
+    run = PrefillRun(w, fused=True)
+    assert ops.prefill_append_is_fused(run.cache, w.causal, w.window_left, max(w.seq_lens))
+    _sampled_rows_check(run, ROWS_32K, [0, 13, 31])
+    assert run.pages_match_oracle_append(), "pages differ from the oracle's append"
 
 
 def test_int8_decode_128k_sampled_sequences():
