@@ -278,9 +278,12 @@ __device__ __forceinline__ void dq_tile(const BackwardArgs &a, int qt, int h, in
   const int p_last = off + min(qt * kBwRows + kBwRows - 1, q_len - 1);
   const int k_lo = a.window_left >= 0 ? max(0, p_first - a.window_left) : 0;
   const int k_hi = a.causal ? min(p_last, ctx - 1) : ctx - 1;
-  // This lane's row sees keys [lo_r, hi_r].
+  // This lane's row sees keys [lo_r, hi_r]; every row of the workgroup
+  // (valid or not) sees [max_lo, min_hi].
   const int hi_r = a.causal ? min(pos, ctx - 1) : ctx - 1;
   const int lo_r = a.window_left >= 0 ? pos - a.window_left : 0;
+  const int min_hi = a.causal ? min(p_first, ctx - 1) : ctx - 1;
+  const int max_lo = a.window_left >= 0 ? off + qt * kBwRows + kBwRows - 1 - a.window_left : 0;
   f32x16 acc[C::kNdb];
 #pragma unroll
   for (int db = 0; db < C::kNdb; ++db)
@@ -319,25 +322,27 @@ __device__ __forceinline__ void dq_tile(const BackwardArgs &a, int qt, int h, in
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = dpacc[kb][i] = 0.f;
-#pragma unroll
-      for (int s = 0; s < C::kNs; ++s) {
+      for (int s = 0; s < C::kNs; ++s) {  // the first product starts from a zero operand
         const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ksm + (kb * 32 + col) * C::kKRow + (16 * s + 8 * g) * 2);
         const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vsm + (kb * 32 + col) * C::kVRow + (16 * s + 8 * g) * 2);
-        sacc[kb] = mfma32(kf, bq[s], sacc[kb]);
-        dpacc[kb] = mfma32(vf, bdo[s], dpacc[kb]);
+        sacc[kb] = mfma32(kf, bq[s], s == 0 ? f32x16{} : sacc[kb]);
+        dpacc[kb] = mfma32(vf, bdo[s], s == 0 ? f32x16{} : dpacc[kb]);
       }
     }
     // dS^T = P^T (dP^T - D), masked; element i of block kb is key
     // key0 + kb*32 + (i/4)*8 + g*4 + i%4 of this lane's row.
     bf16x8 bds[4];
+    // Every key of the tile visible to every row of the workgroup: no mask.
+    const bool interior = key0 >= max_lo && key0 + kBwKeys - 1 <= min_hi;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = key0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        const bool vis = key >= lo_r && key <= hi_r;
-        const float p = vis ? fast_exp2(sacc[kb][i] * a.scale_log2 - lse2) : 0.f;
+        float p = fast_exp2(sacc[kb][i] * a.scale_log2 - lse2);
+        if (!interior) {
+          const int key = key0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+          p = (key >= lo_r && key <= hi_r) ? p : 0.f;
+        }
         bds[2 * kb + (i >> 3)][i & 7] = (__bf16)(p * (dpacc[kb][i] - dlt));
       }
     // dQ^T += K^T . dS^T over four 16-key steps.
@@ -370,7 +375,7 @@ __device__ __forceinline__ void dq_tile(const BackwardArgs &a, int qt, int h, in
 //   P  = exp(s S - lse),  dS = P (dP - D)  (rounded to bf16),
 //   dV^T += dO^T . P,   dK^T += Q^T . dS   (Q^T, dO^T read transposed).
 constexpr int kBwKeyTile = 128;
-constexpr int kBwRowTile = 64;  // query rows per step (two 32-row MFMA blocks)
+constexpr int kBwRowTile = 32;  // query rows per step (one 32-row MFMA block)
 
 template <int D>
 __device__ __forceinline__ void dkv_tile(const BackwardArgs &a, int kt, int hk, int b, unsigned char *qsm,
@@ -451,30 +456,43 @@ __device__ __forceinline__ void dkv_tile(const BackwardArgs &a, int kt, int hk, 
 #pragma unroll
       for (int mb = 0; mb < kMb; ++mb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[mb][i] = dpacc[mb][i] = 0.f;
-#pragma unroll
-        for (int s = 0; s < C::kNs; ++s) {
+        for (int s = 0; s < C::kNs; ++s) {  // the first product starts from a zero operand
           const int ro = (mb * 32 + col) * kPitch + (16 * s + 8 * g) * 2;
-          sacc[mb] = mfma32(*reinterpret_cast<const bf16x8 *>(qsm + ro), bk[s], sacc[mb]);
-          dpacc[mb] = mfma32(*reinterpret_cast<const bf16x8 *>(dosm + ro), bv[s], dpacc[mb]);
+          sacc[mb] = mfma32(*reinterpret_cast<const bf16x8 *>(qsm + ro), bk[s], s == 0 ? f32x16{} : sacc[mb]);
+          dpacc[mb] = mfma32(*reinterpret_cast<const bf16x8 *>(dosm + ro), bv[s], s == 0 ? f32x16{} : dpacc[mb]);
         }
       }
       // Element i of block mb is row rt + mb*32 + (i/4)*8 + g*4 + i%4 against
       // this lane's key; 16-row step t of the products below holds block
       // t/2, elements 8(t%2) .. 8(t%2)+7.
       bf16x8 bp[2 * kMb], bds[2 * kMb];
+      // Every (row, key) pair of the step visible: no mask (the usual case
+      // away from the diagonal and the window's edge).
+      const bool interior = key_first + kBwKeyTile <= ctx && rt + kBwRowTile <= q_len &&
+                            (!a.causal || key_first + kBwKeyTile - 1 <= off + rt) &&
+                            (a.window_left < 0 || off + rt + kBwRowTile - 1 - key_first <= a.window_left);
 #pragma unroll
       for (int mb = 0; mb < kMb; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int rr = mb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-          const int pos = off + rt + rr;
-          bool vis = key < ctx && rt + rr < q_len;
-          if (a.causal) vis = vis && key <= pos;
-          if (a.window_left >= 0) vis = vis && pos - key <= a.window_left;
-          const float p = vis ? fast_exp2(sacc[mb][i] * a.scale_log2 - lse_s[rr]) : 0.f;
-          bp[2 * mb + (i >> 3)][i & 7] = (__bf16)p;
-          bds[2 * mb + (i >> 3)][i & 7] = (__bf16)(p * (dpacc[mb][i] - dl_s[rr]));
+        for (int q4 = 0; q4 < 4; ++q4) {
+          // rows mb*32 + q4*8 + g*4 + (0..3): four consecutive lse / D values
+          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(lse_s + mb * 32 + q4 * 8 + g * 4);
+          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(dl_s + mb * 32 + q4 * 8 + g * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = q4 * 4 + e;
+            const int rr = mb * 32 + q4 * 8 + g * 4 + e;
+            float p = fast_exp2(sacc[mb][i] * a.scale_log2 - l4[e]);
+            if (!interior) {
+              const int pos = off + rt + rr;
+              bool vis = key < ctx && rt + rr < q_len;
+              if (a.causal) vis = vis && key <= pos;
+              if (a.window_left >= 0) vis = vis && pos - key <= a.window_left;
+              p = vis ? p : 0.f;
+            }
+            bp[2 * mb + (i >> 3)][i & 7] = (__bf16)p;
+            bds[2 * mb + (i >> 3)][i & 7] = (__bf16)(p * (dpacc[mb][i] - d4[e]));
+          }
         }
 #pragma unroll
       for (int t = 0; t < 2 * kMb; ++t) {
