@@ -523,10 +523,12 @@ __device__ __forceinline__ void dkv_tile(const BackwardArgs &a, int kt, int hk, 
   }
 }
 
-// dQ: two workgroups share a CU (at most 256 registers per lane), so one's
-// softmax work overlaps the other's MFMAs.  Tiles are taken heaviest first
-// (under a causal mask the last query tile sees the most keys), and the
-// dispatcher hands the lighter ones to whichever CU frees up.
+// dQ: a workgroup takes the pair of query tiles (n-1-p, p), heavier first:
+// under a causal mask the key-tile counts of the two add up to the same
+// total for every p, so all workgroups carry equal work.  (One tile per
+// workgroup, all resident at once, left the kernel as long as its heaviest
+// tile, about twice the average.)  At most 256 registers per lane, so two
+// workgroups can share a CU where the grid is large enough.
 template <int D>
 __global__ __launch_bounds__(256, 2) void dq_mfma_kernel(BackwardArgs a) {
   using C = BwCfg<D>;
@@ -534,8 +536,12 @@ __global__ __launch_bounds__(256, 2) void dq_mfma_kernel(BackwardArgs a) {
   __shared__ __align__(16) unsigned char vsm[kBwKeys * C::kVRow];
   const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n = (a.cu_q[b + 1] - a.cu_q[b] + kBwRows - 1) / kBwRows;
-  if (p >= n) return;  // uniform
+  if (p >= (n + 1) / 2) return;  // uniform
   dq_tile<D>(a, n - 1 - p, h, b, ksm, vsm);
+  if (n - 1 - p != p) {
+    __syncthreads();
+    dq_tile<D>(a, p, h, b, ksm, vsm);
+  }
 }
 
 // dK / dV: one workgroup per CU (its accumulators need more than 256
@@ -566,8 +572,9 @@ hipError_t launch_t(const BackwardArgs &a, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((dq_mfma_kernel<D>), dim3((a.max_q_len + kBwRows - 1) / kBwRows, a.num_q_heads, a.batch),
-                       dim3(256), 0, s, a);
+    hipLaunchKernelGGL((dq_mfma_kernel<D>),
+                       dim3(((a.max_q_len + kBwRows - 1) / kBwRows + 1) / 2, a.num_q_heads, a.batch), dim3(256), 0, s,
+                       a);
   else
     hipLaunchKernelGGL((dq_kernel<D, T>), dim3(a.max_q_len, a.num_q_heads, a.batch), dim3(64), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
