@@ -30,6 +30,8 @@ CASES = [
     (wl.PrefillWorkload("window128_runs", (1500, 400), 4, 2, 128, 64, "bf16", seed=65, window_left=128), (0, 200)),
     (wl.PrefillWorkload("window0_chunk", (300,), 4, 2, 128, 64, "bf16", seed=66, window_left=0), (90,)),
     (wl.PrefillWorkload("noncausal_runs", (1100, 300), 2, 1, 128, 256, "bf16", seed=67, causal=False), (0, 70)),
+    # a sequence with no new rows in the batch (its whole context cached)
+    (wl.PrefillWorkload("empty_chunk_in_batch", (300, 200, 130), 8, 2, 128, 64, "bf16", seed=70), (0, 200, 64)),
     (wl.PrefillWorkload("two_launch_p16", (300, 77), 8, 2, 128, 16, "bf16", seed=68), (0, 33)),
     (wl.PrefillWorkload("two_launch_f32", (128, 45), 2, 1, 64, 64, "f32", seed=69), (0, 17)),
 ]
