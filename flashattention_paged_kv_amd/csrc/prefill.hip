@@ -17,7 +17,8 @@
 // (sequence, query head): their key-tile counts add up to the same total for
 // every p, so all workgroups carry equal work.  With a window or without a
 // mask every query tile has about the same work, and a workgroup takes a run
-// of 8 consecutive query tiles instead (fewer, longer workgroups).  The
+// of consecutive query tiles instead (up to 8: fewer, longer workgroups,
+// while the grid keeps one per CU).  The
 // workgroup is two engines of 4 waves that each take half of the pair's key
 // tiles: engine 0 all of the earlier tile and the top of the later one,
 // engine 1 the bottom of the later one, both ascending, so that the two
@@ -45,6 +46,13 @@
 // more than 2^8 over its reference (the exponent reference may lag the true
 // maximum by at most that much: probabilities stay <= 256, and O and l share
 // the reference, so the result is the same attention).
+//
+// The FUSED instantiation is the prompt step with the append inside (KV
+// Cache section of "大模型推理优化实战：KV Cache + Flash Attention": the new
+// tokens' K/V join the cache, then the queries attend over all of it):
+// tiles of new keys are read from the new rows themselves, and each new row
+// is written to its page slot once, by the item of its own position (see
+// the kernel's comment).
 #include <math.h>
 #include <stdlib.h>
 
