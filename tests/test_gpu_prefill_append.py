@@ -125,3 +125,38 @@ def test_prefill_append_run_lengths(w, prefix, run_tiles, monkeypatch):
     for these small inputs: same pages and output as the oracle."""
     monkeypatch.setenv("PAGEDATTN_PREFILL_RUN_TILES", str(run_tiles))
     test_prefill_append_matches_oracle(w, prefix, "fused", monkeypatch)
+
+
+def _random_cases(n, seed=71):
+    """Seeded random shapes: batch 1-4, prompt lengths 1-700, cached prefixes
+    of any length (0 .. the whole sequence), causal / windowed / unmasked,
+    GQA groups 1-8, D 64 / 128, pages of 64 / 128 / 256 keys."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        batch = int(rng.integers(1, 5))
+        lens = tuple(int(x) for x in rng.integers(1, 701, size=batch))
+        prefix = tuple(int(rng.integers(0, L + 1)) for L in lens)
+        hkv = int(rng.choice([1, 2]))
+        group = int(rng.choice([1, 2, 4, 8]))
+        d = int(rng.choice([64, 128]))
+        page = int(rng.choice([64, 128, 256]))
+        mode = i % 3  # causal, windowed, unmasked in turn
+        causal = mode != 2
+        window = int(rng.integers(0, 300)) if mode == 1 else -1
+        w = wl.PrefillWorkload(f"random{i}", lens, hkv * group, hkv, d, page, "bf16", seed=100 + i, causal=causal,
+                               window_left=window)
+        cases.append((w, prefix))
+    return cases
+
+
+RANDOM_CASES = _random_cases(9)
+
+
+@pytest.mark.parametrize("route", ["fused", "separate"])
+@pytest.mark.parametrize("w,prefix", RANDOM_CASES, ids=[c[0].name for c in RANDOM_CASES])
+def test_prefill_append_random_shapes(w, prefix, route, monkeypatch):
+    """Random ragged batches, prefixes, masks, groups and page sizes, on both
+    routes: pages bit-exact, outputs within tolerance of the oracle, and the
+    same bits as the two separate calls."""
+    test_prefill_append_matches_oracle(w, prefix, route, monkeypatch)
