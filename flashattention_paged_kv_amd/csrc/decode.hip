@@ -381,8 +381,10 @@ __global__ __launch_bounds__(kDecWaves * 64, kDecWaves / 4 * WPC) void decode_sp
       }
     };
 
-    // The first loads are issued even by a wave without tiles (they read
-    // valid rows of the piece), so the wait counts are the same on every path.
+    // The first loads are issued even by a wave without tiles, so the wait
+    // counts are the same on every path.  Every piece holds at least one
+    // tile (the walk below skips sequences without tiles), so k_begin <
+    // k_end and the clamped rows and block indices lie inside the piece.
     // Issue order is pinned (sched_barrier) so that waiting for one tile
     // never waits for a later one.
     TileRegs<D, I8> R[NB];
@@ -444,9 +446,15 @@ __global__ __launch_bounds__(kDecWaves * 64, kDecWaves / 4 * WPC) void decode_sp
     remaining -= len;
     tloc = 0;
     if (++hg == ngr && remaining > 0) {
+      // Next sequence with tiles: one exists, since tiles remain in this
+      // range, so b stays below the batch.  Stepping onto a sequence
+      // without tiles would form an empty piece (k_end = 0), whose clamped
+      // block index would fall before the block-table row.
       hg = 0;
-      ++b;
-      nb = seg_tiles(a.ctx_lens[b], W);
+      do {
+        ++b;
+        nb = seg_tiles(a.ctx_lens[b], W);
+      } while (nb == 0);
     }
   }
 }

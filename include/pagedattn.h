@@ -276,8 +276,9 @@ size_t attn_backward_workspace_bytes(int32_t total_q, int32_t num_q_heads);
  *                      group's query heads summed), other slots untouched.
  *                      Sequences must not share physical pages here.
  *   workspace        : at least attn_backward_workspace_bytes(...) bytes
- * Arithmetic is fp32 on the vector ALUs.  PA_ERR_UNSUPPORTED for an int8
- * cache. */
+ * Arithmetic: bf16 caches run every product on bf16 MFMA with fp32
+ * accumulation (P and dS rounded to bf16 as operands); fp32 caches run in
+ * fp32 on the vector ALUs.  PA_ERR_UNSUPPORTED for an int8 cache. */
 pa_status attn_backward_paged(const void *q, const int32_t *cu_q, const pa_kv_cache *cache, const int32_t *block_table,
                               int32_t max_pages_per_seq, const int32_t *ctx_lens, int32_t batch, int32_t total_q,
                               int32_t max_q_len, int32_t max_ctx, int32_t num_q_heads, float softmax_scale,

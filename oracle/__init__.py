@@ -21,7 +21,6 @@ forms, a library routine, brute force and invariants the pages fix.
 """
 from .attention import (
     gather_sequence,
-    dequantize_pool,
     visible_mask,
     attention_paged,
     decode_paged,
@@ -34,7 +33,7 @@ from .counts import visible_pairs, attention_flops, kv_read_bytes, kv_bytes_per_
 from .twins import brute_force_attention, online_softmax_attention, split_partials, merge_partials
 
 __all__ = [
-    "gather_sequence", "dequantize_pool", "visible_mask", "attention_paged", "decode_paged", "decode_layered",
+    "gather_sequence", "visible_mask", "attention_paged", "decode_paged", "decode_layered",
     "append_pages", "quantize_int8_pages", "dequantize_int8_pages", "visible_pairs",
     "attention_flops", "kv_read_bytes", "kv_bytes_per_token", "brute_force_attention",
     "online_softmax_attention", "split_partials", "merge_partials", "attention_backward_paged",

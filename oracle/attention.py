@@ -56,12 +56,6 @@ def gather_sequence(pool, block_row, n_tokens: int, page_size: int) -> np.ndarra
     return pool[phys, slot]
 
 
-def dequantize_pool(codes, scales) -> np.ndarray:
-    """int8 codes [N, P, Hkv, D] and fp32 scales [N, Hkv] -> float64 values
-    code * scale ([SYS] §3.2, group quantisation, read back)."""
-    return _f64(codes) * _f64(scales)[:, None, :, None]
-
-
 def visible_mask(q_len: int, ctx: int, causal: bool, window_left: int,
                  r0: int = 0, r1: int | None = None) -> np.ndarray:
     """Boolean [r1 - r0, ctx]: True where query row i (r0 <= i < r1) may

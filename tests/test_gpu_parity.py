@@ -350,13 +350,16 @@ def test_int8_append_is_bit_exact_then_decodes():
     check_close(out, ref, "bf16", "decode after int8 appends")
 
 
-def _layered_part(lens, page_size, hkv, d, seed, stream0, int8):
+def _layered_part(lens, page_size, hkv, d, seed, stream0, int8, pad=None):
     """Pools and a permuted block table holding `lens` positions per sequence
-    (int8 parts quantised by the oracle on the CPU)."""
-    pages = [max(1, -(-n // page_size)) for n in lens]
+    (int8 parts quantised by the oracle on the CPU).  pad=None: every
+    sequence holds at least one page and unused entries are 0; else unused
+    entries are `pad` and a sequence without keys holds no page (as a page
+    pool's table has them)."""
+    pages = [(-(-n // page_size)) if pad is not None else max(1, -(-n // page_size)) for n in lens]
     n_pages = sum(pages) + 1
     perm = wl.rng(seed, wl.STREAM_PERM, stream0).permutation(n_pages).astype(np.int32)
-    bt = np.zeros((len(lens), max(pages)), dtype=np.int32)
+    bt = np.full((len(lens), max(1, max(pages))), 0 if pad is None else pad, dtype=np.int32)
     at = 0
     for b, n in enumerate(pages):
         bt[b, :n] = perm[at:at + n]
@@ -419,6 +422,54 @@ def test_decode_empty_context_gives_zero_output():
     check_close(out, ref, "bf16", "decode out")
     for b in (0, 2):
         assert torch.count_nonzero(out[b]).item() == 0 and bool(torch.isneginf(lse[b]).all())
+
+
+@pytest.mark.parametrize("wgs", ["1", "7", "256"])
+def test_decode_walk_over_empty_sequences(monkeypatch, wgs):
+    """Regression: a split workgroup whose range of tiles runs over sequences
+    without keys (here at the start of the batch, twice in a row and between
+    long ones) moves on to the next sequence with keys; block tables padded
+    with -1 as a page pool leaves them.  With 1 or 7 workgroups every range
+    crosses the empty sequences."""
+    P, hq, hkv, d, seed = 16, 8, 2, 128, 73
+    ctx = [0, 300, 0, 0, 4000, 0, 2500, 0]
+    part, cache = _layered_part(ctx, P, hkv, d, seed, 0, False, pad=-1)
+    q = wl.normal((len(ctx), hq, d), "bf16", seed, wl.STREAM_Q)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    monkeypatch.setenv("PAGEDATTN_DECODE_WGS", wgs)
+    say(f"decode over empty sequences, {wgs} workgroups, ctx {ctx}")
+    out, lse = ops.attn_decode_paged(q.cuda(), cache, dev(part["block_table"]), dev(part["lens"]), return_lse=True)
+    torch.cuda.synchronize()
+    empty = dict(part, lens=np.zeros(len(ctx), dtype=np.int32))
+    ref, ref_lse = oracle.decode_layered(f64(q), part, empty)
+    check_close(out, ref, "bf16", "decode out")
+    for b in (0, 2, 3, 5, 7):
+        assert torch.count_nonzero(out[b]).item() == 0 and bool(torch.isneginf(lse[b]).all())
+
+
+def test_layered_decode_int8_part_empty_among_64k_sequences():
+    """Regression: the layered bench shape (first 128 positions bf16 in
+    16-key pages, the rest int8 in 256-key pages, 64 query heads over 8 KV
+    heads) with sequences of at most 128 tokens, whose int8 part is empty,
+    among 64k-70k-token ones: thousands of int8 tiles over the default grid,
+    so workgroups walk across the empty parts.  -1-padded block tables."""
+    F, hq, hkv, d, seed = 128, 64, 8, 128, 74
+    ctx = [65000, 100, 0, 70000, 128, 66000, 5]
+    say(f"layered decode, int8 parts empty among 64k sequences, ctx {ctx}")
+    hi, c_hi = _layered_part([min(F, n) for n in ctx], 16, hkv, d, seed, 0, False, pad=-1)
+    lo, c_lo = _layered_part([max(0, n - F) for n in ctx], 256, hkv, d, seed, 1, True, pad=-1)
+    q = wl.normal((len(ctx), hq, d), "bf16", seed, wl.STREAM_Q)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    out, lse = ops.attn_decode_paged_layered(q.cuda(), c_hi, dev(hi["block_table"]), dev(hi["lens"]), c_lo,
+                                             dev(lo["block_table"]), dev(lo["lens"]), return_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.decode_layered(f64(q), hi, lo)
+    check_close(out[[0, 1, 3, 4, 5, 6]], ref[[0, 1, 3, 4, 5, 6]], "bf16", "layered out")
+    assert torch.count_nonzero(out[2]).item() == 0 and bool(torch.isneginf(lse[2]).all())
+    keep = [0, 1, 3, 4, 5, 6]
+    err = np.abs(f64(lse[keep]) - ref_lse[keep]).max()
+    say(f"  lse max|d|={err:.3e}")
+    assert err <= 1e-3
 
 
 @pytest.mark.parametrize("int8", [False, True])

@@ -39,6 +39,12 @@ QUANT_MUTANTS = [
 ]
 
 
+DEQUANT_MUTANTS = [
+    ("[:, None, :, None]\n", "[None, :, :, None]\n"),                  # scale of the slot's index, not the page's
+    ("np.asarray(codes, dtype=np.float64) *", "np.asarray(codes, dtype=np.float64).clip(-64, 64) *"),  # codes clipped
+]
+
+
 APPEND_MUTANTS = [
     ("* scales[phys, hk]\n", "\n"),                                      # old codes not dequantised
     ("amax = np.abs(vals).max()", "amax = np.abs(new).max() if new.size else np.float32(0)"),  # old rows out of absmax
@@ -103,6 +109,11 @@ def _quant_battery():
     qpins.test_int8_half_way_rounds_to_even()
 
 
+def _dequant_battery():
+    qpins.test_int8_dequantiser_matches_per_element_loop()
+    qpins.test_int8_quantiser_bounds_and_roundtrip()
+
+
 def _append_battery():
     qpins.test_int8_append_of_a_whole_page_is_the_page_quantiser()
     qpins.test_int8_append_with_smaller_rows_keeps_scale_and_old_codes()
@@ -135,6 +146,7 @@ def _backward_battery():
 def test_battery_passes_on_the_real_oracle():
     _attention_battery()
     _quant_battery()
+    _dequant_battery()
     _append_battery()
     _layered_battery()
     _pages_battery()
@@ -156,6 +168,14 @@ def test_quant_mutant_is_caught(monkeypatch, old, new):
     monkeypatch.setattr(oracle, "quantize_int8_pages", mut.quantize_int8_pages)
     with pytest.raises((AssertionError, ValueError, IndexError)):
         _quant_battery()
+
+
+@pytest.mark.parametrize("old,new", DEQUANT_MUTANTS)
+def test_dequant_mutant_is_caught(monkeypatch, old, new):
+    mut = _load_mutant("quant.py", old, new)
+    monkeypatch.setattr(oracle, "dequantize_int8_pages", mut.dequantize_int8_pages)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        _dequant_battery()
 
 
 @pytest.mark.parametrize("old,new", APPEND_MUTANTS)

@@ -59,6 +59,23 @@ def test_int8_quantiser_matches_per_element_fp32_loop():
                     assert codes[n, s, h, d] == c
 
 
+def test_int8_dequantiser_matches_per_element_loop():
+    """code * scale of the code's own (page, KV head) group, element by
+    element, on a pool whose four axes all differ in length (a broadcast
+    over the wrong axis cannot line up) and whose scales all differ."""
+    r = np.random.default_rng(11)
+    N, P, H, D = 3, 5, 2, 7
+    codes = r.integers(-127, 128, size=(N, P, H, D)).astype(np.int8)
+    scales = (r.random((N, H)) + 0.5).astype(np.float32)
+    got = oracle.dequantize_int8_pages(codes, scales)
+    assert got.shape == (N, P, H, D) and got.dtype == np.float64
+    for n in range(N):
+        for p in range(P):
+            for h in range(H):
+                for d in range(D):
+                    assert got[n, p, h, d] == float(int(codes[n, p, h, d])) * float(scales[n, h])
+
+
 def test_int8_half_way_rounds_to_even():
     # absmax 127 -> scale 1 exactly; 2.5 -> 2, 3.5 -> 4, -2.5 -> -2
     x = np.zeros((1, 1, 1, 4), dtype=np.float32)
@@ -122,6 +139,15 @@ def test_counts_match_mask_and_workload_figures():
     assert oracle.visible_pairs(32768, 32768, True, 128) == 4_218_816
     assert oracle.kv_read_bytes([10, 300], 8, 128, 2) == 2 * 310 * 8 * 128 * 2
     assert oracle.kv_read_bytes([10, 300], 8, 128, 1, 4, 256) == 2 * 310 * 8 * 128 + 2 * 3 * 8 * 4
+
+
+def test_bench_pair_counter_is_the_oracle_count():
+    """The benchmark's closed-form pair count (which prices its FLOPs) equals
+    the oracle's row-by-row count for the prefill workloads it times."""
+    import bench
+    for n, w in [(2048, -1), (32768, -1), (32768, 128), (128, -1), (1, -1), (1, 128), (129, 128), (130, 128),
+                 (1000, 0), (64, 127)]:
+        assert bench.causal_pairs(n, w) == oracle.visible_pairs(n, n, True, w), (n, w)
 
 
 def _rows_bf16(n, hkv, d, seed, mag=1.0):
