@@ -181,6 +181,29 @@ static bool prefill_append_fused(int32_t causal, int32_t window_left, int32_t ma
   return pairs ? max_q_len <= 6144 : true;
 }
 
+// Host checks of a single-token decode (attn_decode_paged and its variant
+// without a workspace), before anything touches the device.  PA_OK with
+// batch == 0: nothing to do.
+static pa_status decode_check_args(const void *q, const pa_kv_cache *cache, const int32_t *block_table,
+                                   int32_t max_pages_per_seq, const int32_t *ctx_lens, int32_t batch,
+                                   int32_t num_q_heads, float softmax_scale, const void *out) {
+  pa_status st = check_cache(cache, true);
+  if (st != PA_OK) return st;
+  if (batch < 0) return fail(PA_ERR_INVALID_ARG, "batch must be >= 0");
+  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, cache->num_kv_heads);
+  const int group = num_q_heads / cache->num_kv_heads;
+  if (cache->dtype != PA_F32 && group > 16)
+    return fail(PA_ERR_UNSUPPORTED, "decode supports at most 16 query heads per KV head (got %d)", group);
+  if ((st = check_scale(softmax_scale)) != PA_OK) return st;
+  if (batch == 0) return ok();
+  if (q == nullptr || block_table == nullptr || ctx_lens == nullptr || out == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (max_pages_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq must be > 0");
+  return ok();
+}
+
 extern "C" {
 
 int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
@@ -412,20 +435,10 @@ pa_status attn_decode_paged(const void *q, const pa_kv_cache *cache, const int32
                             int32_t max_pages_per_seq, const int32_t *ctx_lens, int32_t batch, int32_t num_q_heads,
                             float softmax_scale, int32_t window_left, void *out, float *lse, void *workspace,
                             size_t workspace_bytes, void *stream) {
-  pa_status st = check_cache(cache, true);
-  if (st != PA_OK) return st;
-  if (batch < 0) return fail(PA_ERR_INVALID_ARG, "batch must be >= 0");
-  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0)
-    return fail(PA_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
-                num_q_heads, cache->num_kv_heads);
+  pa_status st = decode_check_args(q, cache, block_table, max_pages_per_seq, ctx_lens, batch, num_q_heads,
+                                   softmax_scale, out);
+  if (st != PA_OK || batch == 0) return st;
   const int group = num_q_heads / cache->num_kv_heads;
-  if (cache->dtype != PA_F32 && group > 16)
-    return fail(PA_ERR_UNSUPPORTED, "decode supports at most 16 query heads per KV head (got %d)", group);
-  if ((st = check_scale(softmax_scale)) != PA_OK) return st;
-  if (batch == 0) return ok();
-  if (q == nullptr || block_table == nullptr || ctx_lens == nullptr || out == nullptr)
-    return fail(PA_ERR_INVALID_ARG, "NULL pointer argument");
-  if (max_pages_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq must be > 0");
 
   if (cache->dtype == PA_F32) {
     pa::PrefillArgs a;
@@ -455,6 +468,30 @@ pa_status attn_decode_paged(const void *q, const pa_kv_cache *cache, const int32
   const pa::DecodeArgs a = decode_args(q, cache, block_table, max_pages_per_seq, ctx_lens, batch, num_q_heads,
                                        softmax_scale, window_left, out, lse, workspace, nwg);
   return hip_status(pa::launch_decode(a, (hipStream_t)stream), "attn_decode_paged launch");
+}
+
+pa_status attn_decode_paged_noalloc(const void *q, const pa_kv_cache *cache, const int32_t *block_table,
+                                    int32_t max_pages_per_seq, const int32_t *ctx_lens, int32_t batch,
+                                    int32_t num_q_heads, float softmax_scale, int32_t window_left, void *out,
+                                    float *lse, void *stream) {
+  pa_status st = decode_check_args(q, cache, block_table, max_pages_per_seq, ctx_lens, batch, num_q_heads,
+                                   softmax_scale, out);
+  if (st != PA_OK || batch == 0) return st;
+  if (cache->dtype == PA_F32)  // fp32 caches decode without partials (no scratch)
+    return attn_decode_paged(q, cache, block_table, max_pages_per_seq, ctx_lens, batch, num_q_heads, softmax_scale,
+                             window_left, out, lse, nullptr, 0, stream);
+  const size_t cap = pa::noalloc_scratch_bytes();
+  const size_t need = attn_decode_workspace_bytes(batch, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                                                  max_pages_per_seq, cache->page_size);
+  if (need > cap)
+    return fail(PA_ERR_WORKSPACE,
+                "attn_decode_paged_noalloc: batch %d with %d query heads over %d KV heads needs %zu bytes of "
+                "scratch, more than the %zu the library holds (use attn_decode_paged with a workspace)",
+                batch, num_q_heads, cache->num_kv_heads, need, cap);
+  void *ws = nullptr;
+  if ((st = hip_status(pa::noalloc_scratch(&ws), "attn_decode_paged_noalloc scratch address")) != PA_OK) return st;
+  return attn_decode_paged(q, cache, block_table, max_pages_per_seq, ctx_lens, batch, num_q_heads, softmax_scale,
+                           window_left, out, lse, ws, cap, stream);
 }
 
 size_t attn_decode_layered_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -158,6 +158,12 @@ inline int decode_heads_per_wg(int hkv) {
   return h;
 }
 
+// Decode scratch held by the library itself (a device array per GPU, for
+// the entry point that allocates nothing): its size, and its address on the
+// current device (taken once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void **ptr);
+
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);

@@ -50,7 +50,7 @@ _lib = None
 EXPORTED = ("kv_cache_append", "kv_pages_quantize_int8", "attn_prefill_paged", "attn_prefill_paged_append",
             "attn_prefill_append_is_fused",
             "attn_decode_workspace_bytes",
-            "attn_decode_paged", "attn_decode_layered_workspace_bytes", "attn_decode_paged_layered",
+            "attn_decode_paged", "attn_decode_paged_noalloc", "attn_decode_layered_workspace_bytes", "attn_decode_paged_layered",
             "kv_cache_copy_pages", "attn_backward_workspace_bytes", "attn_backward_paged", "pa_pool_create", "pa_pool_destroy", "pa_pool_extend", "pa_pool_fork",
             "pa_pool_release", "pa_pool_export", "pa_pool_free_pages", "pa_pool_refcount",
             "pa_status_string", "pa_last_error_detail", "pa_abi_version")
@@ -75,6 +75,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.attn_decode_workspace_bytes.restype = SZ
     lib.attn_decode_paged.argtypes = [P, CP, P, I32, P, I32, I32, F32, I32, P, P, P, SZ, P]
+    lib.attn_decode_paged_noalloc.argtypes = [P, CP, P, I32, P, I32, I32, F32, I32, P, P, P]
     lib.attn_decode_layered_workspace_bytes.argtypes = [I32, I32, I32, I32]
     lib.attn_decode_layered_workspace_bytes.restype = SZ
     lib.attn_decode_paged_layered.argtypes = [P, CP, P, I32, P, CP, P, I32, P, I32, I32, F32, P, P, P, SZ, P]
@@ -96,6 +97,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("pa_pool_free_pages", "pa_pool_refcount"):
         getattr(lib, name).restype = I32
     for name in ("kv_cache_append", "kv_pages_quantize_int8", "attn_prefill_paged", "attn_decode_paged",
+                 "attn_decode_paged_noalloc",
                  "attn_decode_paged_layered", "kv_cache_copy_pages", "attn_backward_paged", "pa_pool_create",
                  "pa_pool_extend",
                  "pa_pool_fork", "pa_pool_release", "pa_pool_export"):
@@ -304,6 +306,36 @@ def attn_decode_paged(q: torch.Tensor, cache: KVCache, block_table: torch.Tensor
                                  _ptr(ctx_lens), batch, hq, scale, int(window_left), _ptr(out), _ptr(lse),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
     return (out, lse) if return_lse else out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PA_NOALLOC_SCRATCH_BYTES of the header
+
+
+def attn_decode_paged_noalloc(q: torch.Tensor, cache: KVCache, block_table: torch.Tensor, ctx_lens: torch.Tensor,
+                              out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                              softmax_scale: Optional[float] = None, window_left: int = -1) -> torch.Tensor:
+    """attn_decode_paged with the library's own scratch instead of a
+    workspace: the call allocates nothing (the caller passes ``out`` and,
+    optionally, ``lse`` [B, Hq] float32).  Calls on one GPU share the
+    scratch, so overlapping calls race."""
+    lib = load_library()
+    cs = cache._struct()
+    _dev(q, "q")
+    _dev(block_table, "block_table", torch.int32)
+    _dev(ctx_lens, "ctx_lens", torch.int32)
+    _dev(out, "out", q.dtype)
+    batch, hq, d = q.shape
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+        if tuple(lse.shape) != (batch, hq):
+            raise ValueError(f"lse must be [{batch}, {hq}]")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    _check(lib.attn_decode_paged_noalloc(_ptr(q), ctypes.byref(cs), _ptr(block_table), block_table.shape[1],
+                                         _ptr(ctx_lens), batch, hq, scale, int(window_left), _ptr(out), _ptr(lse),
+                                         _stream()))
+    return out
 
 
 def decode_layered_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:

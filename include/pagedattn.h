@@ -225,6 +225,24 @@ pa_status attn_decode_paged(const void *q, const pa_kv_cache *cache, const int32
                             int32_t num_q_heads, float softmax_scale, int32_t window_left, void *out,
                             float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
+/* attn_decode_paged_noalloc - attn_decode_paged without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * split partials go to a scratch array the library holds on each GPU
+ * (PA_NOALLOC_SCRATCH_BYTES, reserved from the first use of the library on
+ * that GPU until the process ends); the call allocates nothing.  Arguments,
+ * result and errors are those of attn_decode_paged, plus PA_ERR_WORKSPACE
+ * when attn_decode_workspace_bytes(...) of these sizes exceeds
+ * PA_NOALLOC_SCRATCH_BYTES.  Every call on one GPU shares that GPU's array
+ * (which keeps the last call's contents; nothing in it needs to start at
+ * zero): calls that overlap on one GPU, from several streams or threads,
+ * race and must be serialised by the caller. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pa_status attn_decode_paged_noalloc(const void *q, const pa_kv_cache *cache, const int32_t *block_table,
+                                    int32_t max_pages_per_seq, const int32_t *ctx_lens, int32_t batch,
+                                    int32_t num_q_heads, float softmax_scale, int32_t window_left, void *out,
+                                    float *lse, void *stream);
+
 /* attn_decode_layered_workspace_bytes - HOST function: workspace bytes that
  * attn_decode_paged_layered needs for these sizes (0 on bad input). */
 size_t attn_decode_layered_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -152,6 +152,29 @@ def test_workspace_size_query():
                    ws_bytes=lib.attn_decode_workspace_bytes(2, 4, 2, 128, 4, 16) - 1) == 4
 
 
+def test_noalloc_decode_rejects_sizes_beyond_its_scratch():
+    """attn_decode_paged_noalloc checks the scratch its sizes need against
+    the library's fixed array before anything else happens (no device
+    call), and runs attn_decode_paged's own checks otherwise."""
+    lib = ops.load_library()
+    cap = ops.NOALLOC_SCRATCH_BYTES
+    # 1024 sequences x 64 query heads over 8 KV heads need ~ 34 MB > 32 MiB
+    need = lib.attn_decode_workspace_bytes(1024, 64, 8, 128, 32, 256)
+    assert need > cap
+    c = _cache(num_kv_heads=8, page_size=256)
+    st = lib.attn_decode_paged_noalloc(FAKE, ctypes.byref(c), FAKE, 32, FAKE, 1024, 64, 0.1, -1, FAKE, None, None)
+    assert st == 4 and b"scratch" in lib.pa_last_error_detail()
+    # ordinary argument errors are attn_decode_paged's
+    assert lib.attn_decode_paged_noalloc(FAKE, ctypes.byref(c), FAKE, 32, FAKE, 4, 60, 0.1, -1, FAKE, None,
+                                         None) == 1
+    assert lib.attn_decode_paged_noalloc(FAKE, ctypes.byref(c), FAKE, 32, FAKE, 4, 64, 0.0, -1, FAKE, None,
+                                         None) == 1
+    assert lib.attn_decode_paged_noalloc(FAKE, ctypes.byref(_cache(head_dim=96)), FAKE, 32, FAKE, 4, 64, 0.1, -1,
+                                         FAKE, None, None) == 2
+    assert lib.attn_decode_paged_noalloc(FAKE, ctypes.byref(c), FAKE, 32, FAKE, 0, 64, 0.1, -1, None, None,
+                                         None) == 0
+
+
 def test_append_rejects_bad_args():
     lib = ops.load_library()
     c = _cache(dtype=ops.PA_I8)                       # int8 cache without scales
