@@ -1,32 +1,42 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--workload NAME]
 
-One step is one pass of the hot path over one batch of synthetic input:
-  * prefill step (the headline workload): a 2048-token Llama-2-7B-shaped
-    prompt (32 heads, D=128, bf16) appended into 256-token pages with a
-    permuted block table and attended over causally, by
-    attn_prefill_paged_append (the append fused into the prefill kernel; the
-    two separate calls, kv_cache_append then attn_prefill_paged, are timed
-    beside it);
-  * decode step (reported beside it): kv_cache_append of one new token for
-    each of 64 Llama-2-70B-shaped GQA sequences (64 q heads, 8 KV heads,
-    contexts uniform in [512, 8192]) and attn_decode_paged over their pages.
+One step is one pass of the hot path over one batch of synthetic input.  The
+headline (``value``) is the prompt step of the largest single-GPU prefill
+configuration: a 32768-token causal prompt (32 heads, D=128, bf16) whose K/V
+are appended into 256-token pages with a permuted block table and attended
+over causally, by ``attn_prefill_paged_append`` (at this length the library
+runs the append kernel and then the prefill kernel; the prefill kernel is the
+dominant one and carries ``roofline``).  Beside it, under ``workloads``:
+  * the 2048-token Llama-2-7B-shaped prompt step (append fused into the
+    prefill kernel at this length);
+  * the 32768-token prompt with a 128-key left window (below the ridge point:
+    HBM-bound, timed with a cold cache);
+  * the Llama-2-70B-shaped GQA decode step (64 sequences, 64 query heads over
+    8 KV heads, contexts uniform in [512, 8192], bf16 pages): the new token's
+    append, then attn_decode_paged;
+  * the 128k-context int8 decode (16 sequences, contexts uniform in
+    [65536, 131072], int8 pages with one fp32 scale per (page, KV head)).
 
-``value`` is prefill TFLOP/s over the whole prefill step (algorithmic FLOPs:
-4 * D * Hq per visible (query, key) pair); the decode object gives KV-read
-GB/s (each valid K/V element once per KV head).  Inputs are resident in HBM
-before timing.  Kernel durations for the roofline objects come from HIP
-events around back-to-back launches on the stream the library launches on
-(torch's current stream).  One JSON line is printed.
+Prefill throughput is TFLOP/s of algorithmic work (4 * D * Hq per visible
+(query, key) pair); decode throughput is KV-read GB/s (each valid K/V element
+once per KV head, plus the int8 scales of the pages touched).  Inputs are
+resident in HBM before timing.  Kernel times come from HIP events on the
+stream the library launches on (torch's current stream): warm timings run
+back to back; cold timings read a 1 GiB buffer (untimed) before every rep
+so that neither L2 nor the 256 MB MALL holds the inputs, and report the
+mean, median and min over the reps.  One JSON line is printed.
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
+import statistics
 import sys
+import threading
 import time
 
 import numpy as np
@@ -40,10 +50,18 @@ from flashattention_paged_kv_amd import workloads as wl  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector: 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (dual issue) x 2.4 GHz
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+FLUSH_BYTES = 1 << 30         # read before each cold rep (> L2 + MALL)
+
+HEADLINE = wl.LONG_PREFILL
+PAGE_COPY = "page_copy_512_pages_p256_hkv8_d128_bf16"
+BACKWARD = "backward_causal_L2048_h32_d128_p256_bf16"
 
 
 def causal_pairs(n: int, window_left: int = -1) -> int:
+    """Visible (query, key) pairs of an n-token causal prompt, closed form:
+    row i sees min(i + 1, window_left + 1) keys."""
     if window_left < 0:
         return n * (n + 1) // 2
     w1 = window_left + 1
@@ -65,94 +83,218 @@ def _traffic(kernel: str, workload: str):
     return round(t["hbm_bytes_per_launch"])
 
 
-def _time_loop(fn, steps: int, warmup: int, min_warm_s: float = 0.2) -> float:
-    """Average ms per call of fn() over `steps` back-to-back calls.  The
-    untimed warm-up runs `warmup` calls and then keeps calling until at least
-    `min_warm_s` seconds of work have run, so the clocks have settled before
-    the timed region (a 50-call loop of a 60 us kernel is over in 3 ms)."""
+class _Flush:
+    """A 1 GiB device buffer read (summed) before each cold rep: it evicts the
+    inputs from L2 and the MALL and leaves only clean lines behind (a
+    writing flush would leave 1 GiB of dirty lines whose write-back then
+    competes with the timed kernel's reads)."""
+
+    def __init__(self):
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        self.acc = torch.zeros((), dtype=torch.int64, device="cuda")
+
+    def __call__(self):
+        torch.sum(self.buf, dtype=torch.int64, out=self.acc)
+
+
+_FLUSH = None
+
+
+def _flush():
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = _Flush()
+    return _FLUSH
+
+
+def _settle(fn, warmup: int, min_s: float = 0.2):
+    """Untimed warm-up: `warmup` calls, then calls until `min_s` seconds of
+    work have run (so the clocks have settled before the timed region)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < min_warm_s:
-        for _ in range(10):
+    while time.perf_counter() - t0 < min_s:
+        for _ in range(5):
             fn()
         torch.cuda.synchronize()
+
+
+def time_warm(fn, reps: int, warmup: int) -> dict:
+    """`reps` back-to-back calls bracketed by one pair of HIP events (mean =
+    span / reps), then `reps` more with an event pair around each call
+    (median and min per call), in ms."""
+    _settle(fn, warmup)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     s.record()
-    for _ in range(steps):
+    for _ in range(reps):
         fn()
     e.record()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
     torch.cuda.synchronize()
-    return s.elapsed_time(e) / steps
+    per = [a.elapsed_time(b) for a, b in ev]
+    return dict(mean_ms=s.elapsed_time(e) / reps, median_ms=statistics.median(per), min_ms=min(per), reps=reps)
 
 
-def bench_prefill(w: wl.PrefillWorkload, steps: int, warmup: int) -> dict:
+def time_cold(fn, reps: int, warmup: int) -> dict:
+    """Each rep: read 1 GiB (untimed), then one call between HIP events;
+    mean, median and min per call, in ms."""
+    flush = _flush()
+    _settle(fn, warmup)
+    per = []
+    for _ in range(reps):
+        flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b))
+    return dict(mean_ms=statistics.fmean(per), median_ms=statistics.median(per), min_ms=min(per), reps=reps)
+
+
+def _r(d: dict) -> dict:
+    return {k: (round(v, 5) if isinstance(v, float) else v) for k, v in d.items()}
+
+
+class ClockSampler:
+    """Samples the GPU's current shader (sclk) and memory (mclk) clock levels
+    from the amdgpu sysfs files of the device torch runs on, every 20 ms in a
+    thread, while a timed region runs.  Reports null where the files are not
+    readable."""
+
+    def __init__(self):
+        self.path = None
+        try:
+            p = torch.cuda.get_device_properties(0)
+            cand = f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+            if os.path.exists(os.path.join(cand, "pp_dpm_sclk")):
+                self.path = cand
+        except Exception:
+            self.path = None
+        self.samples = {"sclk": [], "mclk": []}
+        self._stop = threading.Event()
+        self._t = None
+
+    @staticmethod
+    def _current_mhz(path: str):
+        try:
+            for line in open(path):
+                if line.rstrip().endswith("*"):
+                    tok = line.split(":", 1)[1].strip().split()[0].lower()
+                    return float(tok.replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            for k in ("sclk", "mclk"):
+                v = self._current_mhz(os.path.join(self.path, f"pp_dpm_{k}"))
+                if v is not None:
+                    self.samples[k].append(v)
+            self._stop.wait(0.02)
+
+    def __enter__(self):
+        if self.path:
+            self._t = threading.Thread(target=self._run, daemon=True)
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._t is not None:
+            self._t.join()
+
+    def summary(self) -> dict:
+        out = {"source": self.path and (self.path + "/pp_dpm_{sclk,mclk}")}
+        for k, v in self.samples.items():
+            out[k + "_mhz"] = (dict(min=min(v), median=statistics.median(v), max=max(v), samples=len(v))
+                               if v else None)
+        return out
+
+
+def bench_prefill(w: wl.PrefillWorkload, steps: int, warmup: int, cold: bool = False,
+                  sampler: ClockSampler | None = None) -> dict:
+    """The prompt step (attn_prefill_paged_append) and the prefill kernel alone
+    (attn_prefill_paged) on one workload.  cold=True (HBM-bound shapes) times
+    both with L2 and the MALL flushed (a 1 GiB read) before every rep."""
     dev = torch.device("cuda")
     inp = wl.prefill_inputs(w)
     tdt = torch.bfloat16
     shape = (inp["num_pages"], w.page_size, w.num_kv_heads, w.head_dim)
     cache = ops.KVCache(torch.zeros(shape, dtype=tdt, device=dev), torch.zeros(shape, dtype=tdt, device=dev))
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
-    bt, cu, ctx, start = (inp[n].to(dev) for n in ("block_table", "cu_q", "ctx_lens", "start_pos"))
+    bt, cu, ctx = (inp[n].to(dev) for n in ("block_table", "cu_q", "ctx_lens"))
     out = torch.empty_like(q)
     max_len = max(w.seq_lens)
-
-    def append():
-        ops.kv_cache_append(cache, k, v, bt, start, cu, max_new=max_len)
+    del inp
 
     def prefill():
         ops.attn_prefill_paged(q, cu, cache, bt, ctx, max_q_len=max_len, softmax_scale=w.softmax_scale,
                                causal=w.causal, window_left=w.window_left, out=out)
 
-    def separate():
-        append()
-        prefill()
-
-    def step():  # the append fused into the prefill kernel: one launch
+    def step():
         ops.attn_prefill_paged_append(q, k, v, cu, cache, bt, ctx, max_q_len=max_len, softmax_scale=w.softmax_scale,
                                       causal=w.causal, window_left=w.window_left, out=out)
 
-    ms_step = _time_loop(step, steps, warmup)
-    ms_separate = _time_loop(separate, steps, warmup)
-    ms_attn_only = _time_loop(prefill, steps, warmup)
-    # The dominant kernel: the step itself when it is one fused launch, else
-    # the attention kernel (the step is then the append kernel + it).
+    timer = time_cold if cold else time_warm
+    t_step = timer(step, steps, warmup)
+    if sampler is not None:
+        with sampler:
+            t_attn = timer(prefill, steps, warmup)
+    else:
+        t_attn = timer(prefill, steps, warmup)
     fused = ops.prefill_append_is_fused(cache, w.causal, w.window_left, max_len)
-    ms_kernel = ms_step if fused else ms_attn_only
+    # The dominant kernel: the step itself when it is one fused launch, else
+    # the prefill kernel (the step is then the append kernel + it).
+    t_kernel = t_step if fused else t_attn
     pairs = sum(causal_pairs(n, w.window_left) for n in w.seq_lens)
     flops = 4 * w.head_dim * w.num_q_heads * pairs
     kv_bytes = 2 * sum(w.seq_lens) * w.num_kv_heads * w.head_dim * 2
     # Algorithmic HBM bytes: Q and O once per query row, K and V once per key.
     io_bytes = 2 * sum(w.seq_lens) * w.num_q_heads * w.head_dim * 2 + kv_bytes
-    achieved = flops / (ms_kernel * 1e-3) / 1e12
-    if flops / io_bytes >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / PEAK_BF16_TFLOPS, 4))
-    else:  # below the ridge point (a short window): bytes bound it
-        gbs = io_bytes / (ms_kernel * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4))
-    roof["traffic"] = _traffic("prefill_bf16_kernel_fused" if fused else "prefill_bf16_kernel", w.name)
-    # The same for attention alone (attn_prefill_paged, no append), for reference.
-    attn = flops / (ms_attn_only * 1e-3) / 1e12
-    roof_attn = dict(bound=roof["bound"], achieved=round(attn, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                     frac=round(attn / PEAK_BF16_TFLOPS, 4), traffic=_traffic("prefill_bf16_kernel", w.name))
-    if roof["bound"] == "hbm":
-        gbs = io_bytes / (ms_attn_only * 1e-3) / 1e9
-        roof_attn.update(achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4))
-    return dict(workload=w.name, fused=fused, ms_per_step=ms_step, ms_prefill_kernel=ms_kernel,
-                ms_separate_calls=ms_separate,
-                ms_attention_only=ms_attn_only, flops=flops,
-                tflops_step=flops / (ms_step * 1e-3) / 1e12, tflops_kernel=achieved, kv_bytes=kv_bytes,
-                io_bytes=io_bytes, roofline=roof, attention_only_roofline=roof_attn)
+    hbm_bound = flops / io_bytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+    def roof(ms, kernel):
+        if hbm_bound:   # below the ridge point (a short window): bytes bound it
+            gbs = io_bytes / (ms * 1e-3) / 1e9
+            r = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                     frac=round(gbs / PEAK_HBM_GBS, 4))
+        else:
+            tf = flops / (ms * 1e-3) / 1e12
+            r = dict(bound="mfma", achieved=round(tf, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                     frac=round(tf / PEAK_BF16_TFLOPS, 4))
+        r["traffic"] = _traffic(kernel, w.name)
+        return r
+
+    kname = "prefill_bf16_kernel_fused" if fused else "prefill_bf16_kernel"
+    return dict(workload=w.name, fused=fused, timing="cold" if cold else "warm",
+                step=_r(t_step), prefill_kernel=_r(t_attn), flops=flops, io_bytes=io_bytes,
+                tflops_step=flops / (t_step["mean_ms"] * 1e-3) / 1e12,
+                roofline=roof(t_kernel["mean_ms"], kname),
+                prefill_kernel_roofline=roof(t_attn["mean_ms"], "prefill_bf16_kernel"),
+                config=dict(batch=w.batch, seq_len=max_len, num_q_heads=w.num_q_heads,
+                            num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, page_size=w.page_size,
+                            causal=w.causal, window_left=w.window_left))
 
 
 def bench_decode(w: wl.DecodeWorkload, steps: int, warmup: int) -> dict:
+    """The decode step (bf16: the new token's append, then attn_decode_paged;
+    int8: attn_decode_paged over pages quantised once) timed cold (headline)
+    and warm, and the decode call alone (split + merge kernels)."""
     dev = torch.device("cuda")
     inp = wl.decode_inputs(w)
     bt, ctx, start, cun = (inp[n].to(dev) for n in ("block_table", "ctx_lens", "start_pos", "cu_new"))
     q, k_new, v_new = (inp[n].to(dev) for n in ("q", "k_new", "v_new"))
     kd, vd = inp["k_pool"].to(dev), inp["v_pool"].to(dev)
+    ctx_np = inp["ctx_lens"].numpy().astype(np.int64)
+    del inp
     if w.kv_dtype == "i8":
         ops.kv_cache_append(ops.KVCache(kd, vd), k_new, v_new, bt, start, cun, max_new=1)
         kc, ks = ops.kv_pages_quantize_int8(kd)
@@ -179,19 +321,27 @@ def bench_decode(w: wl.DecodeWorkload, steps: int, warmup: int) -> dict:
             append()
         decode()
 
-    ms_step = _time_loop(step, steps, warmup)
-    ms_kernel = _time_loop(decode, steps, warmup)
-    ctx_np = inp["ctx_lens"].numpy().astype(np.int64)
+    reps = max(steps, 100) if w.batch >= 64 else max(steps, 20)
+    cold_step = time_cold(step, reps, warmup)
+    cold = time_cold(decode, reps, warmup)
+    warm = time_warm(decode, reps, warmup)
     esz = 1 if w.kv_dtype == "i8" else 2
     kv_bytes = int(2 * ctx_np.sum() * w.num_kv_heads * w.head_dim * esz)
     if w.kv_dtype == "i8":
         kv_bytes += int(2 * sum(-(-int(c) // w.page_size) for c in ctx_np) * w.num_kv_heads * 4)
-    gbs = kv_bytes / (ms_kernel * 1e-3) / 1e9
-    return dict(workload=w.name, ms_per_step=ms_step, ms_decode_kernels=ms_kernel, kv_bytes=kv_bytes,
-                gbs_step=kv_bytes / (ms_step * 1e-3) / 1e9, gbs_kernel=gbs, sum_ctx=int(ctx_np.sum()),
-                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                              frac=round(gbs / PEAK_HBM_GBS, 4),
-                              traffic=_traffic("decode_split_kernel", w.name)))
+    gbs = lambda ms: kv_bytes / (ms * 1e-3) / 1e9
+    return dict(workload=w.name, metric="decode KV-read GB/s", value=round(gbs(cold_step["median_ms"]), 1),
+                unit="GB/s", timing="cold (1 GiB read before each rep); value from the step's median",
+                step_cold=_r(cold_step), decode_cold=_r(cold), decode_warm=_r(warm), kv_bytes=kv_bytes,
+                sum_ctx=int(ctx_np.sum()),
+                step=("kv_cache_append + attn_decode_paged" if append is not None else "attn_decode_paged"),
+                roofline=dict(bound="hbm", achieved=round(gbs(cold["mean_ms"]), 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                              frac=round(gbs(cold["mean_ms"]) / PEAK_HBM_GBS, 4),
+                              traffic=_traffic("decode_split_kernel", w.name)),
+                warm_roofline_frac=round(gbs(warm["mean_ms"]) / PEAK_HBM_GBS, 4),
+                config=dict(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                            head_dim=w.head_dim, page_size=w.page_size, kv_dtype=w.kv_dtype,
+                            ctx_range=[w.ctx_lo, w.ctx_hi]))
 
 
 def bench_layered(w: wl.DecodeWorkload, steps: int, warmup: int) -> dict:
@@ -218,20 +368,15 @@ def bench_layered(w: wl.DecodeWorkload, steps: int, warmup: int) -> dict:
         ops.attn_decode_paged_layered(q, hi, bt_hi, lh, lo, bt_lo, ll, softmax_scale=w.softmax_scale, out=out,
                                       workspace=ws)
 
-    ms = _time_loop(decode, steps, warmup)
+    cold = time_cold(decode, max(steps, 20), warmup)
     row = w.num_kv_heads * w.head_dim
     kv_bytes = int(2 * len_hi.sum() * row * 2 + 2 * len_lo.sum() * row
                    + 2 * sum(-(-int(c) // w.page_size) for c in len_lo) * w.num_kv_heads * 4)
-    gbs = kv_bytes / (ms * 1e-3) / 1e9
-    return dict(workload=w.name, ms_decode_kernels=ms, kv_bytes=kv_bytes, gbs_kernel=gbs,
-                sum_ctx=int(ctx_np.sum()), full_tokens=w.full_tokens,
+    gbs = kv_bytes / (cold["mean_ms"] * 1e-3) / 1e9
+    return dict(workload=w.name, decode_cold=_r(cold), kv_bytes=kv_bytes, sum_ctx=int(ctx_np.sum()),
+                full_tokens=w.full_tokens,
                 roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                               frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
-
-
-PAGE_COPY = "page_copy_512_pages_p256_hkv8_d128_bf16"
-BACKWARD = "backward_causal_L2048_h32_d128_p256_bf16"
-PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector: 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (dual issue) x 2.4 GHz
 
 
 def bench_backward(steps: int, warmup: int) -> dict:
@@ -257,13 +402,13 @@ def bench_backward(steps: int, warmup: int) -> dict:
                      device=dev)
     fn = lambda: ops.attn_backward_paged(q, cu, cache, bt, ctx, out, lse, d_out, max_q_len=L, max_ctx=L, dk=dk, dv=dv,
                                          workspace=ws)
-    ms = _time_loop(fn, steps, warmup)
+    t = time_warm(fn, steps, warmup)
     pairs = sum(causal_pairs(n, w.window_left) for n in w.seq_lens)
     flops = 10 * w.head_dim * w.num_q_heads * pairs
-    tf = flops / (ms * 1e-3) / 1e12
+    tf = flops / (t["mean_ms"] * 1e-3) / 1e12
     # bf16 caches run the dQ and dK/dV products on MFMA (fp32 caches on the
     # vector ALUs, whose peak is PEAK_FP32_VALU_TFLOPS).
-    return dict(workload=BACKWARD, ms_backward_kernels=ms, flops=flops, tflops=tf,
+    return dict(workload=BACKWARD, backward=_r(t), flops=flops, tflops=tf,
                 roofline=dict(bound="mfma", achieved=round(tf, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                               frac=round(tf / PEAK_BF16_TFLOPS, 4), traffic=None))
 
@@ -278,52 +423,70 @@ def bench_page_copy(steps: int, warmup: int) -> dict:
     cache = ops.KVCache(torch.randn(shape, device=dev).to(torch.bfloat16), torch.randn(shape, device=dev).to(torch.bfloat16))
     perm = torch.randperm(2 * n, generator=torch.Generator().manual_seed(9)).to(torch.int32)
     src, dst = perm[:n].to(dev), perm[n:].to(dev)
-    ms = _time_loop(lambda: ops.kv_cache_copy_pages(cache, src, dst), steps, warmup)
+    t = time_cold(lambda: ops.kv_cache_copy_pages(cache, src, dst), max(steps, 20), warmup)
     nbytes = 2 * 2 * n * P * hkv * d * 2     # K and V, read and written
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    return dict(workload=PAGE_COPY, ms_copy_kernel=ms, bytes=nbytes,
+    gbs = nbytes / (t["mean_ms"] * 1e-3) / 1e9
+    return dict(workload=PAGE_COPY, copy_cold=_r(t), bytes=nbytes,
                 roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                               frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
 
 
 def cpu_baseline(w: wl.PrefillWorkload, budget_s: float = 15.0) -> dict:
     """The CPU oracle (float64 numpy) on a bounded sample of the prefill
-    workload: the whole prompt's append, then as many heads of the causal
-    attention as fit in about `budget_s` seconds (heads are independent)."""
+    workload: the whole prompt's append into pages, then blocks of 256
+    consecutive query rows of head 0 (each block at its own causal
+    positions, spread over the prompt) until about `budget_s` seconds have
+    run; TFLOP/s of the algorithmic work of the rows done."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = 1
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
     inp = wl.prefill_inputs(w)
     f64 = lambda t: t.float().numpy().astype(np.float64)
-    t0 = time.perf_counter()
-    shape = (inp["num_pages"], w.page_size, w.num_kv_heads, w.head_dim)
-    kp, vp = oracle.append_pages(np.zeros(shape), np.zeros(shape), f64(inp["k"]), f64(inp["v"]),
-                                 inp["block_table"].numpy(), inp["start_pos"].numpy(), inp["cu_q"].numpy(),
-                                 w.page_size)
-    q = f64(inp["q"])
-    heads = 0
-    while heads < w.num_q_heads and time.perf_counter() - t0 < budget_s:
-        h = heads
-        oracle.attention_paged(q[:, h:h + 1], inp["cu_q"].numpy(), kp[:, :, h:h + 1], vp[:, :, h:h + 1],
-                               inp["block_table"].numpy(), inp["ctx_lens"].numpy(), w.page_size,
-                               w.softmax_scale, w.causal, w.window_left)
+    L = max(w.seq_lens)
+    bt = inp["block_table"].numpy()
+    blk = 256
+    starts = list(range(0, L, blk))
+    order = starts[::2] + starts[1::2]   # spread over the prompt first, then the rest
+    pairs, rows, heads, t_append, t_attn = 0, 0, 0, 0.0, 0.0
+    shape = (inp["num_pages"], w.page_size, 1, w.head_dim)
+    for h in range(w.num_q_heads):
+        if t_attn >= budget_s:
+            break
+        t0 = time.perf_counter()
+        g = h // (w.num_q_heads // w.num_kv_heads)
+        kp, vp = oracle.append_pages(np.zeros(shape), np.zeros(shape), f64(inp["k"][:, g:g + 1]),
+                                     f64(inp["v"][:, g:g + 1]), bt, inp["start_pos"].numpy(), inp["cu_q"].numpy(),
+                                     w.page_size)
+        q = f64(inp["q"][:, h:h + 1])
+        t1 = time.perf_counter()
+        t_append += t1 - t0
+        for r0 in order:
+            if t_attn + (time.perf_counter() - t1) >= budget_s:
+                break
+            r1 = min(L, r0 + blk)
+            oracle.attention_paged(q[r0:r1], np.array([0, r1 - r0]), kp, vp, bt, np.array([r1]), w.page_size,
+                                   w.softmax_scale, w.causal, w.window_left)
+            pairs += oracle.visible_pairs(r1 - r0, r1, w.causal, w.window_left)
+            rows += r1 - r0
+        t_attn += time.perf_counter() - t1
         heads += 1
-    dt = time.perf_counter() - t0
-    pairs = sum(causal_pairs(n, w.window_left) for n in w.seq_lens)
-    flops = 4 * w.head_dim * heads * pairs
-    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=int(threads), kind="oracle",
-                sample=f"{w.name}: append of all {sum(w.seq_lens)} tokens + causal attention of {heads} of "
-                       f"{w.num_q_heads} heads ({dt:.1f} s, float64 numpy)")
+    flops = 4 * w.head_dim * pairs
+    return dict(value=round(flops / t_attn / 1e12, 6), unit="TFLOP/s", cores=cores, kind="oracle",
+                sample=f"{w.name}: {rows} query rows (blocks of {blk} at their causal positions, spread over the "
+                       f"prompt) over {heads} of {w.num_q_heads} heads, {pairs} visible pairs in {t_attn:.1f} s "
+                       f"of float64 numpy (BLAS threads {blas_threads}); each head's append into pages took "
+                       f"{t_append:.1f} s more in all")
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=None, help="bench a single named workload instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -358,7 +521,7 @@ def main() -> int:
     if args.workload:
         w = wl.WORKLOADS[args.workload]
         if isinstance(w, wl.PrefillWorkload):
-            r = bench_prefill(w, args.steps, args.warmup)
+            r = bench_prefill(w, args.steps, args.warmup, cold=w.window_left >= 0)
         elif w.full_tokens:
             r = bench_layered(w, args.steps, args.warmup)
         else:
@@ -366,38 +529,49 @@ def main() -> int:
         print(json.dumps(r), flush=True)
         return 0
 
-    pre = bench_prefill(wl.LLAMA7B_PREFILL, args.steps, args.warmup)
-    dec = bench_decode(wl.LLAMA70B_DECODE, args.steps, args.warmup)
+    sampler = ClockSampler()
+    head = bench_prefill(HEADLINE, args.steps, args.warmup, sampler=sampler)
+    print(f"[bench] {HEADLINE.name}: step {head['step']['mean_ms']:.3f} ms", file=sys.stderr, flush=True)
+    others = {}
+    for w, fn in ((wl.LLAMA7B_PREFILL, lambda w: bench_prefill(w, max(args.steps, 100), args.warmup)),
+                  (wl.LONG_PREFILL_WINDOW, lambda w: bench_prefill(w, args.steps, args.warmup, cold=True)),
+                  (wl.LLAMA70B_DECODE, lambda w: bench_decode(w, args.steps, args.warmup)),
+                  (wl.DECODE_128K_INT8, lambda w: bench_decode(w, args.steps, args.warmup))):
+        r = fn(w)
+        others[w.name] = r
+        print(f"[bench] {w.name}: done", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
     line = {
         "metric": "prefill TFLOP/s & decode KV-read GB/s, as % of MI355X MFMA/HBM peak",
-        "value": round(pre["tflops_step"], 2),
+        "value": round(head["tflops_step"], 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(pre["ms_per_step"], 5),
+        "ms_per_step": round(head["step"]["mean_ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16, permuted page tables)",
-        "config": {"workload": pre["workload"], "batch": 1, "seq_len": 2048, "num_q_heads": 32,
-                   "num_kv_heads": 32, "head_dim": 128, "page_size": 256, "causal": True,
-                   "step": "attn_prefill_paged_append" + (" (append fused into the prefill kernel)" if pre["fused"]
-                                                            else " (append kernel, then the prefill)")},
-        "roofline": pre["roofline"],
-        "prefill_kernel_ms": round(pre["ms_prefill_kernel"], 5),
-        "separate_calls_ms": round(pre["ms_separate_calls"], 5),
-        "attention_only_kernel_ms": round(pre["ms_attention_only"], 5),
-        "attention_only_roofline": pre["attention_only_roofline"],
-        "decode": {"metric": "decode KV-read GB/s", "value": round(dec["gbs_step"], 1), "unit": "GB/s",
-                   "ms_per_step": round(dec["ms_per_step"], 5), "kernel_ms": round(dec["ms_decode_kernels"], 5),
-                   "kv_bytes": dec["kv_bytes"], "sum_ctx": dec["sum_ctx"],
-                   "config": {"workload": dec["workload"], "step": "kv_cache_append + attn_decode_paged"},
-                   "roofline": dec["roofline"]},
+        "config": dict(workload=HEADLINE.name, **head["config"],
+                       step="attn_prefill_paged_append" + (" (append fused into the prefill kernel)" if head["fused"]
+                                                            else " (append kernel, then the prefill kernel)")),
+        "roofline": head["roofline"],
+        "step_ms": head["step"],
+        "prefill_kernel_ms": head["prefill_kernel"],
+        "clocks": sampler.summary(),
+        "workloads": {
+            name: ({k: r[k] for k in ("timing", "fused", "step", "prefill_kernel", "roofline", "prefill_kernel_roofline")}
+                   | {"tflops_step": round(r["tflops_step"], 2)})
+            if "prefill_kernel" in r else
+            {k: r[k] for k in ("metric", "value", "unit", "timing", "step", "step_cold", "decode_cold", "decode_warm",
+                               "kv_bytes", "sum_ctx", "roofline", "warm_roofline_frac")}
+            for name, r in others.items()
+        },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl.LLAMA7B_PREFILL)
+        line["cpu_baseline"] = cpu_baseline(HEADLINE)
     print(json.dumps(line), flush=True)
     return 0
 

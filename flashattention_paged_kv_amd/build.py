@@ -1,10 +1,16 @@
 """Build libpagedattn.so (all HIP sources, gfx950) in place, with hipcc.
 
-    python -m flashattention_paged_kv_amd.build [--debug]
+    python -m flashattention_paged_kv_amd.build [--debug | --sanitize]
 
 Compiles each csrc/*.hip to an object (in parallel) and links the shared
 library next to this file.  Packed fp32 instructions are disabled for the
 device code.
+
+--sanitize builds libpagedattn_hostsan.so beside it: the host-side sources
+(argument checks, dispatch, the page pool) compiled with AddressSanitizer
+and UndefinedBehaviorSanitizer on the host pass only (device code is built
+as usual), linked against the shared ASan runtime, which the process must
+preload (tests/test_host_sanitizers.py does).
 """
 from __future__ import annotations
 
@@ -22,14 +28,19 @@ OUT = os.path.join(HERE, "libpagedattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Host-pass-only sanitizers (each flag applies to the host compilation alone).
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+HOST_SANITIZED_SOURCES = ("api.hip", "page_pool.hip", "noalloc.hip")
+SAN_OUT = os.path.join(HERE, "libpagedattn_hostsan.so")
 
 
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str, obj: str, opt: str) -> None:
-    cmd = [HIPCC, *DEVICE_FLAGS, opt, "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+def _compile(src: str, obj: str, opt: str, extra=()) -> None:
+    cmd = [HIPCC, *DEVICE_FLAGS, opt, "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", *extra,
            "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
@@ -59,7 +70,48 @@ def build(debug: bool = False, verbose: bool = True) -> str:
     return OUT
 
 
+def asan_runtime() -> str:
+    """Path of clang's shared ASan runtime next to hipcc's compiler, or ''."""
+    llvm = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "lib", "clang")
+    for root, _, files in os.walk(os.path.normpath(llvm)):
+        if "libclang_rt.asan-x86_64.so" in files:
+            return os.path.join(root, "libclang_rt.asan-x86_64.so")
+    return ""
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    """libpagedattn_hostsan.so: the host-side sources with ASan + UBSan (host
+    pass), the kernels' sources as in the release build."""
+    objdir = os.path.join(HERE, "_build_hostsan")
+    os.makedirs(objdir, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+
+    def one(so):
+        src, obj = so
+        san = os.path.basename(src) in HOST_SANITIZED_SOURCES
+        _compile(src, obj, "-O1" if san else "-O3", HOST_SANITIZE if san else ())
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        list(ex.map(one, zip(srcs, objs)))
+    tmp = SAN_OUT + ".tmp"
+    cmd = [HIPCC, *DEVICE_FLAGS, "-shared", "-fPIC", "-Xarch_host", "-shared-libasan", *HOST_SANITIZE, *objs,
+           "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    os.replace(tmp, SAN_OUT)
+    if verbose:
+        print(f"built {SAN_OUT}")
+    return SAN_OUT
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--debug", action="store_true")
-    build(debug=ap.parse_args().debug)
+    ap.add_argument("--sanitize", action="store_true")
+    a = ap.parse_args()
+    if a.sanitize:
+        build_sanitized()
+    else:
+        build(debug=a.debug)

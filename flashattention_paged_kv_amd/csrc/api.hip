@@ -208,7 +208,7 @@ extern "C" {
 
 int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
 
-const char *pa_status_string(pa_status status) {
+const char *pa_status_string(int32_t status) {
   switch (status) {
     case PA_OK: return "ok";
     case PA_ERR_INVALID_ARG: return "invalid argument";

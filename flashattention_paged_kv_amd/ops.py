@@ -18,7 +18,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+# PAGEDATTN_LIB selects another build of the library (e.g. the host-sanitizer
+# build, libpagedattn_hostsan.so); by default the one built in place.
+LIB_PATH = os.environ.get("PAGEDATTN_LIB") or os.path.join(_HERE, "libpagedattn.so")
 
 PA_F32, PA_BF16, PA_I8 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8}

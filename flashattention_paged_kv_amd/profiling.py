@@ -4,6 +4,9 @@ never touches the GPU).
     # kernel durations (from `rocprofv3 --kernel-trace --stats -f csv`)
     python -m flashattention_paged_kv_amd.profiling stats KT_kernel_stats.csv \\
         --cmd "<the rocprofv3 command>" --title "..." --out profiles/<name>.md
+    # the same per (kernel, grid) from the kernel trace itself
+    python -m flashattention_paged_kv_amd.profiling trace KT_kernel_trace.csv \\
+        --cmd "<the rocprofv3 command>" --title "..." --out profiles/<name>.md
 
     # HBM traffic per launch (from `rocprofv3 --pmc FETCH_SIZE` and
     # `--pmc WRITE_SIZE` runs of the benchmark and of its copy calibration)
@@ -68,6 +71,27 @@ def stats_markdown(stats_csv: str, cmd: str, title: str) -> str:
     return "\n".join(out) + "\n"
 
 
+def trace_markdown(trace_csv: str, cmd: str, title: str, min_calls: int = 1) -> str:
+    """Per (kernel, grid) launch statistics from a `--kernel-trace` CSV: one
+    kernel instantiation launched with different grids (the same prefill
+    kernel at 2k and at 32k rows) gets one row per grid.  Grid sizes are in
+    work items, as rocprofv3 reports them."""
+    groups = defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        grid = (int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
+        groups[(_short(r["Kernel_Name"]), grid)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = [f"# {title}", "", "Command (from the repository root, on one MI355X):", "", "```", cmd, "```", "",
+           "| kernel | grid (work items) | calls | avg µs | median µs | min µs | max µs |",
+           "|---|---|---|---|---|---|---|"]
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
+    for (name, grid), d in rows:
+        if len(d) < min_calls:
+            continue
+        out.append(f"| `{name}` | {grid[0]}×{grid[1]}×{grid[2]} | {len(d)} | {statistics.fmean(d):.1f} | "
+                   f"{statistics.median(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
+    return "\n".join(out) + "\n"
+
+
 def counter_per_dispatch(path: str, counter: str) -> dict:
     """Mean value of `counter` per dispatch, by kernel name."""
     vals = defaultdict(list)
@@ -107,6 +131,12 @@ def main(argv=None) -> int:
     s.add_argument("--cmd", required=True)
     s.add_argument("--title", required=True)
     s.add_argument("--out", required=True)
+    k = sub.add_parser("trace")
+    k.add_argument("trace_csv")
+    k.add_argument("--cmd", required=True)
+    k.add_argument("--title", required=True)
+    k.add_argument("--out", required=True)
+    k.add_argument("--min-calls", type=int, default=1)
     t = sub.add_parser("traffic")
     for n in ("fetch", "write", "copy-fetch", "copy-write"):
         t.add_argument("--" + n, required=True)
@@ -118,6 +148,10 @@ def main(argv=None) -> int:
     t.add_argument("--workload", required=True)
     t.add_argument("--out", required=True)
     args = ap.parse_args(argv)
+    if args.action == "trace":
+        with open(args.out, "w") as f:
+            f.write(trace_markdown(args.trace_csv, args.cmd, args.title, args.min_calls))
+        return 0
     if args.action == "stats":
         with open(args.out, "w") as f:
             f.write(stats_markdown(args.stats_csv, args.cmd, args.title))

@@ -357,8 +357,9 @@ pa_status pa_pool_export(pa_page_pool *pool, int32_t *block_table, int32_t *lens
 int32_t pa_pool_free_pages(pa_page_pool *pool);
 int32_t pa_pool_refcount(pa_page_pool *pool, int32_t page);
 
-/* Static description of a status code. */
-const char *pa_status_string(pa_status status);
+/* Static description of a status code (a pa_status value, passed as an int
+ * so that any value is well defined; others give "unknown status"). */
+const char *pa_status_string(int32_t status);
 
 /* Message of the last failure on the calling thread ("" if none). */
 const char *pa_last_error_detail(void);
