@@ -92,6 +92,39 @@ def trace_markdown(trace_csv: str, cmd: str, title: str, min_calls: int = 1) -> 
     return "\n".join(out) + "\n"
 
 
+def pmc_markdown(paths, cmds, title: str, simds: int, match: str = "") -> str:
+    """Counters per dispatch, averaged per (kernel, grid), from one or more
+    `rocprofv3 --pmc` runs (one counter set each), with the MFMA utilisation
+    they give: SQ_VALU_MFMA_BUSY_CYCLES summed over the SIMDs / (GRBM_GUI_ACTIVE
+    x SIMDs), the expression of rocprofv3's own MfmaUtil metric, and the
+    bf16 MFMA work executed (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOPs)."""
+    vals = defaultdict(lambda: defaultdict(list))
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            if match and match not in r["Kernel_Name"]:
+                continue
+            key = (_short(r["Kernel_Name"]), r.get("Grid_Size", "?"))
+            vals[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = [f"# {title}", "", "Commands (from the repository root, on one MI355X; one counter set per run):", "",
+           "```", *cmds, "```", "",
+           f"Per dispatch, averaged over the dispatches of each (kernel, grid); {simds} SIMDs.", ""]
+    for (name, grid), cs in sorted(vals.items()):
+        out.append(f"## `{name}`, grid {grid} work items")
+        out.append("")
+        out.append("| counter | dispatches | mean per dispatch |")
+        out.append("|---|---|---|")
+        for c, v in sorted(cs.items()):
+            out.append(f"| {c} | {len(v)} | {statistics.fmean(v):.6g} |")
+        m = {c: statistics.fmean(v) for c, v in cs.items()}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m and "GRBM_GUI_ACTIVE" in m and m["GRBM_GUI_ACTIVE"] > 0:
+            out.append(f"| **MFMA utilisation** (busy / (GUI_ACTIVE x SIMDs)) | | "
+                       f"**{100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (m['GRBM_GUI_ACTIVE'] * simds):.1f}%** |")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in m:
+            out.append(f"| bf16 MFMA FLOPs executed (MOPS x 512) | | {m['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.6g} |")
+        out.append("")
+    return "\n".join(out)
+
+
 def counter_per_dispatch(path: str, counter: str) -> dict:
     """Mean value of `counter` per dispatch, by kernel name."""
     vals = defaultdict(list)
@@ -137,6 +170,13 @@ def main(argv=None) -> int:
     k.add_argument("--title", required=True)
     k.add_argument("--out", required=True)
     k.add_argument("--min-calls", type=int, default=1)
+    pm = sub.add_parser("pmc")
+    pm.add_argument("csv", nargs="+", help="counter_collection.csv of each --pmc run")
+    pm.add_argument("--cmd", action="append", required=True, help="the rocprofv3 command of each run")
+    pm.add_argument("--title", required=True)
+    pm.add_argument("--simds", type=int, default=1024, help="SIMDs of the device (MI355X: 256 CUs x 4)")
+    pm.add_argument("--match", default="", help="only kernels whose name contains this")
+    pm.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     for n in ("fetch", "write", "copy-fetch", "copy-write"):
         t.add_argument("--" + n, required=True)
@@ -148,6 +188,10 @@ def main(argv=None) -> int:
     t.add_argument("--workload", required=True)
     t.add_argument("--out", required=True)
     args = ap.parse_args(argv)
+    if args.action == "pmc":
+        with open(args.out, "w") as f:
+            f.write(pmc_markdown(args.csv, args.cmd, args.title, args.simds, args.match))
+        return 0
     if args.action == "trace":
         with open(args.out, "w") as f:
             f.write(trace_markdown(args.trace_csv, args.cmd, args.title, args.min_calls))
