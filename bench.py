@@ -94,7 +94,7 @@ class _Flush:
         self.acc = torch.zeros((), dtype=torch.int64, device="cuda")
 
     def __call__(self):
-        torch.sum(self.buf, dtype=torch.int64, out=self.acc)
+        torch.sum(self.buf, dim=0, dtype=torch.int64, out=self.acc)
 
 
 _FLUSH = None

@@ -6,6 +6,11 @@ Compiles each csrc/*.hip to an object (in parallel) and links the shared
 library next to this file.  Packed fp32 instructions are disabled for the
 device code.
 
+--debug builds libpagedattn_debug.so beside it: the same kernels with the
+device-side range checks of block-table entries, lengths and prefix sums
+compiled in (PA_DEVICE_CHECKS=1; each call then waits for its kernels and
+reports PA_ERR_DEVICE_ASSERT).
+
 --sanitize builds libpagedattn_hostsan.so beside it: the host-side sources
 (argument checks, dispatch, the page pool) compiled with AddressSanitizer
 and UndefinedBehaviorSanitizer on the host pass only (device code is built
@@ -51,23 +56,27 @@ def _compile(src: str, obj: str, opt: str, extra=()) -> None:
         print(err, file=sys.stderr)
 
 
+DEBUG_OUT = os.path.join(HERE, "libpagedattn_debug.so")
+
+
 def build(debug: bool = False, verbose: bool = True) -> str:
-    objdir = os.path.join(HERE, "_build")
+    objdir = os.path.join(HERE, "_build_debug" if debug else "_build")
     os.makedirs(objdir, exist_ok=True)
-    opt = "-O1" if debug else "-O3"
+    extra = ["-DPA_DEVICE_CHECKS=1"] if debug else []
+    out = DEBUG_OUT if debug else OUT
     srcs = sources()
     objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        list(ex.map(lambda so: _compile(so[0], so[1], opt), zip(srcs, objs)))
-    tmp = OUT + ".tmp"
+        list(ex.map(lambda so: _compile(so[0], so[1], "-O3", extra), zip(srcs, objs)))
+    tmp = out + ".tmp"
     cmd = [HIPCC, *DEVICE_FLAGS, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT}")
-    return OUT
+        print(f"built {out}")
+    return out
 
 
 def asan_runtime() -> str:

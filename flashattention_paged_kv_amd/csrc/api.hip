@@ -32,6 +32,34 @@ pa_status hip_status(hipError_t e, const char *what) {
   return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// The status of a call whose kernels have been enqueued on `s`.  Debug
+// builds (PA_DEVICE_CHECKS=1) wait for them and report the first
+// device-resident integer they found out of range (PA_ERR_DEVICE_ASSERT);
+// release builds return at once.
+pa_status launched(hipError_t e, hipStream_t s, const char *what) {
+  if (e != hipSuccess) return hip_status(e, what);
+#if PA_DEVICE_CHECKS
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_status(e, what);
+  static const char *const kSite[] = {"-", "page id", "context length", "query count", "new-row count",
+                                      "append start position", "row offset"};
+  hipError_t (*const readers[])(pa::DeviceFault *) = {pa::take_fault_append, pa::take_fault_prefill,
+                                                      pa::take_fault_decode, pa::take_fault_backward,
+                                                      pa::take_fault_page_pool};
+  for (auto read : readers) {
+    pa::DeviceFault f = {};
+    if ((e = read(&f)) != hipSuccess) return hip_status(e, what);
+    if (f.flag != 0) {
+      const int site = f.site >= 0 && f.site <= 6 ? f.site : 0;
+      return fail(PA_ERR_DEVICE_ASSERT, "%s: device check: %s %d of sequence %d outside [%d, %d]", what,
+                  kSite[site], f.value, f.batch, f.lo, f.hi);
+    }
+  }
+#else
+  (void)s;
+#endif
+  return ok();
+}
+
 int log2_exact(int v) {
   int l = 0;
   while ((1 << l) < v) ++l;
@@ -208,6 +236,8 @@ extern "C" {
 
 int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
 
+int32_t pa_device_checks(void) { return PA_DEVICE_CHECKS; }
+
 const char *pa_status_string(int32_t status) {
   switch (status) {
     case PA_OK: return "ok";
@@ -216,6 +246,7 @@ const char *pa_status_string(int32_t status) {
     case PA_ERR_HIP: return "HIP runtime error";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_OUT_OF_PAGES: return "not enough free pages in the pool";
+    case PA_ERR_DEVICE_ASSERT: return "a device-side check failed (debug build)";
   }
   return "unknown status";
 }
@@ -250,7 +281,8 @@ pa_status kv_cache_append(const pa_kv_cache *cache, const void *k_new, const voi
     a.log2_page = log2_exact(cache->page_size);
     a.num_kv_heads = cache->num_kv_heads;
     a.head_dim = cache->head_dim;
-    return hip_status(pa::launch_append_i8(a, (hipStream_t)stream), "kv_cache_append launch");
+    a.num_pages = cache->num_pages;
+    return launched(pa::launch_append_i8(a, (hipStream_t)stream), (hipStream_t)stream, "kv_cache_append");
   }
   pa::AppendArgs a;
   a.k_pages = cache->k_pages;
@@ -267,7 +299,8 @@ pa_status kv_cache_append(const pa_kv_cache *cache, const void *k_new, const voi
   a.page_size = cache->page_size;
   a.log2_page = log2_exact(cache->page_size);
   a.row_bytes = cache->num_kv_heads * cache->head_dim * (cache->dtype == PA_F32 ? 4 : 2);
-  return hip_status(pa::launch_append(a, (hipStream_t)stream), "kv_cache_append launch");
+  a.num_pages = cache->num_pages;
+  return launched(pa::launch_append(a, (hipStream_t)stream), (hipStream_t)stream, "kv_cache_append");
 }
 
 pa_status kv_pages_quantize_int8(const void *src, int8_t *codes, float *scales, int32_t num_pages,
@@ -286,7 +319,7 @@ pa_status kv_pages_quantize_int8(const void *src, int8_t *codes, float *scales, 
   a.page_size = page_size;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
-  return hip_status(pa::launch_quantize(a, (hipStream_t)stream), "kv_pages_quantize_int8 launch");
+  return launched(pa::launch_quantize(a, (hipStream_t)stream), (hipStream_t)stream, "kv_pages_quantize_int8");
 }
 
 pa_status attn_prefill_paged(const void *q, const int32_t *cu_q, const pa_kv_cache *cache,
@@ -298,7 +331,7 @@ pa_status attn_prefill_paged(const void *q, const int32_t *cu_q, const pa_kv_cac
   pa_status st = prefill_args(q, cu_q, cache, block_table, max_pages_per_seq, ctx_lens, batch, max_q_len, num_q_heads,
                               softmax_scale, causal, window_left, out, lse, &a, &empty);
   if (st != PA_OK || empty) return st;
-  return hip_status(pa::launch_prefill(a, (hipStream_t)stream), "attn_prefill_paged launch");
+  return launched(pa::launch_prefill(a, (hipStream_t)stream), (hipStream_t)stream, "attn_prefill_paged");
 }
 
 int32_t attn_prefill_append_is_fused(const pa_kv_cache *cache, int32_t causal, int32_t window_left,
@@ -323,7 +356,7 @@ pa_status attn_prefill_paged_append(const void *q, const void *k_new, const void
   if (attn_prefill_append_is_fused(cache, causal, window_left, max_q_len)) {
     a.k_new = k_new;
     a.v_new = v_new;
-    return hip_status(pa::launch_prefill(a, s), "attn_prefill_paged_append launch");
+    return launched(pa::launch_prefill(a, s), s, "attn_prefill_paged_append");
   }
   // Other caches (fp32, or pages smaller than a key tile), and the lengths
   // where two launches are faster: the append kernel (start = ctx_lens[b] -
@@ -343,8 +376,9 @@ pa_status attn_prefill_paged_append(const void *q, const void *k_new, const void
   ap.page_size = cache->page_size;
   ap.log2_page = log2_exact(cache->page_size);
   ap.row_bytes = cache->num_kv_heads * cache->head_dim * (cache->dtype == PA_F32 ? 4 : 2);
-  if ((st = hip_status(pa::launch_append(ap, s), "attn_prefill_paged_append (append) launch")) != PA_OK) return st;
-  return hip_status(pa::launch_prefill(a, s), "attn_prefill_paged_append launch");
+  ap.num_pages = cache->num_pages;
+  if ((st = launched(pa::launch_append(ap, s), s, "attn_prefill_paged_append (append)")) != PA_OK) return st;
+  return launched(pa::launch_prefill(a, s), s, "attn_prefill_paged_append");
 }
 
 pa_status kv_cache_copy_pages(const pa_kv_cache *cache, const int32_t *src_pages, const int32_t *dst_pages,
@@ -358,10 +392,11 @@ pa_status kv_cache_copy_pages(const pa_kv_cache *cache, const int32_t *src_pages
   const size_t esz = cache->dtype == PA_F32 ? 4 : cache->dtype == PA_BF16 ? 2 : 1;
   const size_t page_bytes = (size_t)cache->page_size * cache->num_kv_heads * cache->head_dim * esz;
   const bool i8 = cache->dtype == PA_I8;
-  return hip_status(pa::launch_copy_pages(cache->k_pages, cache->v_pages, i8 ? cache->k_scales : nullptr,
+  return launched(pa::launch_copy_pages(cache->k_pages, cache->v_pages, i8 ? cache->k_scales : nullptr,
                                           i8 ? cache->v_scales : nullptr, cache->num_kv_heads, src_pages, dst_pages,
-                                          n, page_bytes, (hipStream_t)stream),
-                    "kv_cache_copy_pages launch");
+                                          n, page_bytes, cache->num_pages, (hipStream_t)stream),
+                  (hipStream_t)stream,
+                    "kv_cache_copy_pages");
 }
 
 size_t attn_backward_workspace_bytes(int32_t total_q, int32_t num_q_heads) {
@@ -418,7 +453,7 @@ pa_status attn_backward_paged(const void *q, const int32_t *cu_q, const pa_kv_ca
   a.dk = dk_pages;
   a.dv = dv_pages;
   a.delta = (float *)workspace;
-  return hip_status(pa::launch_backward(a, (hipStream_t)stream), "attn_backward_paged launch");
+  return launched(pa::launch_backward(a, (hipStream_t)stream), (hipStream_t)stream, "attn_backward_paged");
 }
 
 size_t attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -457,7 +492,7 @@ pa_status attn_decode_paged(const void *q, const pa_kv_cache *cache, const int32
     a.window_left = window_left < 0 ? -1 : window_left;
     a.out = out;
     a.lse = lse;
-    return hip_status(pa::launch_prefill(a, (hipStream_t)stream), "attn_decode_paged launch");
+    return launched(pa::launch_prefill(a, (hipStream_t)stream), (hipStream_t)stream, "attn_decode_paged");
   }
 
   const int nwg = pa::decode_grid_size();
@@ -467,7 +502,7 @@ pa_status attn_decode_paged(const void *q, const pa_kv_cache *cache, const int32
     return fail(PA_ERR_WORKSPACE, "decode needs %zu workspace bytes (got %zu)", need, workspace_bytes);
   const pa::DecodeArgs a = decode_args(q, cache, block_table, max_pages_per_seq, ctx_lens, batch, num_q_heads,
                                        softmax_scale, window_left, out, lse, workspace, nwg);
-  return hip_status(pa::launch_decode(a, (hipStream_t)stream), "attn_decode_paged launch");
+  return launched(pa::launch_decode(a, (hipStream_t)stream), (hipStream_t)stream, "attn_decode_paged");
 }
 
 pa_status attn_decode_paged_noalloc(const void *q, const pa_kv_cache *cache, const int32_t *block_table,
@@ -537,7 +572,7 @@ pa_status attn_decode_paged_layered(const void *q, const pa_kv_cache *cache_hi, 
                                         softmax_scale, -1, out, lse, workspace, nwg);
   const pa::DecodeArgs lo = decode_args(q, cache_lo, block_table_lo, max_pages_lo, len_lo, batch, num_q_heads,
                                         softmax_scale, -1, out, lse, (char *)workspace + part, nwg);
-  return hip_status(pa::launch_decode_layered(hi, lo, (hipStream_t)stream), "attn_decode_paged_layered launch");
+  return launched(pa::launch_decode_layered(hi, lo, (hipStream_t)stream), (hipStream_t)stream, "attn_decode_paged_layered");
 }
 
 }  // extern "C"

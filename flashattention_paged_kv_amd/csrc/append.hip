@@ -24,18 +24,20 @@ constexpr int kAppendRowsPerBlock = 4;
 
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int b = blockIdx.y;
-  const int n0 = a.cu_new[b];
-  const int n_new = a.cu_new[b + 1] - n0;
+  const int n0 = checked(a.cu_new[b], 0, 0x7fffffff, kSiteRowOffset, b);
+  const int n_new = checked(a.cu_new[b + 1] - n0, 0, min(a.max_new, a.max_pages << a.log2_page), kSiteNewLen, b);
   const int r_begin = blockIdx.x * kAppendRowsPerBlock;
   if (r_begin >= n_new) return;
-  const int start = a.start_pos != nullptr ? a.start_pos[b] : a.ctx_lens[b] - n_new;
+  const int start = checked(a.start_pos != nullptr ? a.start_pos[b] : a.ctx_lens[b] - n_new, 0,
+                            (a.max_pages << a.log2_page) - n_new, kSiteStartPos, b);
   const int chunks = a.row_bytes >> 4;
   const int rows = min(kAppendRowsPerBlock, n_new - r_begin);
   for (int c = threadIdx.x; c < rows * chunks; c += blockDim.x) {
     const int r = r_begin + c / chunks;
     const int ch = c % chunks;
     const int pos = start + r;
-    const int page = a.block_table[(size_t)b * a.max_pages + (pos >> a.log2_page)];
+    const int page = checked(a.block_table[(size_t)b * a.max_pages + (pos >> a.log2_page)], 0, a.num_pages - 1,
+                             kSitePageId, b);
     const size_t dst_row = (size_t)page * a.page_size + (pos & (a.page_size - 1));
     const size_t src_row = (size_t)(n0 + r);
     const uint4 kv = reinterpret_cast<const uint4 *>(a.k_new)[src_row * chunks + ch];
@@ -44,6 +46,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     reinterpret_cast<uint4 *>(a.v_pages)[dst_row * chunks + ch] = vv;
   }
 }
+
+PA_DEFINE_FAULT_READER(take_fault_append)
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
   if (a.batch == 0 || a.max_new == 0) return hipSuccess;
@@ -113,16 +117,16 @@ __global__ __launch_bounds__(256) void append_i8_kernel(AppendI8Args a) {
   const int j = blockIdx.x;
   const int hk = blockIdx.y;
   const int b = blockIdx.z;
-  const int r0 = a.cu_new[b];
-  const int n = a.cu_new[b + 1] - r0;
+  const int r0 = checked(a.cu_new[b], 0, 0x7fffffff, kSiteRowOffset, b);
+  const int n = checked(a.cu_new[b + 1] - r0, 0, min(a.max_new, a.max_pages << a.log2_page), kSiteNewLen, b);
   if (n <= 0) return;
   const int P = a.page_size;
-  const int s0 = a.start_pos[b];
+  const int s0 = checked(a.start_pos[b], 0, (a.max_pages << a.log2_page) - n, kSiteStartPos, b);
   const int end = s0 + n;
   const int lp = (s0 >> a.log2_page) + j;
   const int p0 = lp * P;
   if (p0 >= end) return;  // uniform
-  const int phys = a.block_table[(size_t)b * a.max_pages + lp];
+  const int phys = checked(a.block_table[(size_t)b * a.max_pages + lp], 0, a.num_pages - 1, kSitePageId, b);
   const int n_old = max(0, min(s0, p0 + P) - p0);  // old valid slots [0, n_old)
   const int hi = min(end, p0 + P) - p0;            // valid slots after the append: [0, hi)
   const int first_row = r0 + (p0 + n_old - s0);    // input row of slot n_old

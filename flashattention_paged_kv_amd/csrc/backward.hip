@@ -94,19 +94,37 @@ __global__ __launch_bounds__(256) void delta_kernel(BackwardArgs a) {
   }
 }
 
+// Device-resident integers of sequence b (checked in debug builds against
+// the ranges the entry point documents).
+__device__ __forceinline__ int bw_q0(const BackwardArgs &a, int b) {
+  return checked(a.cu_q[b], 0, 0x7fffffff, kSiteRowOffset, b);
+}
+__device__ __forceinline__ int bw_qlen(const BackwardArgs &a, int b, int q0) {
+  // also bounded by the context bound below, so a valid context exists
+  const int hi = min(a.max_q_len, min(a.max_ctx, a.max_pages << a.c.log2_page));
+  return checked(a.cu_q[b + 1] - q0, 0, hi, kSiteQueryLen, b);
+}
+__device__ __forceinline__ int bw_ctx(const BackwardArgs &a, int b, int q_len) {
+  return checked(a.ctx_lens[b], q_len, min(a.max_ctx, a.max_pages << a.c.log2_page), kSiteCtxLen, b);
+}
+// Physical page of logical page n of sequence b.
+__device__ __forceinline__ int bw_page(const BackwardArgs &a, int b, int n) {
+  return checked(a.block_table[(size_t)b * a.max_pages + n], 0, a.c.num_pages - 1, kSitePageId, b);
+}
+
 // Row offset of token `key` of sequence b, KV head hk, in a pool.
 __device__ __forceinline__ size_t key_row(const BackwardArgs &a, int b, int key, int hk, int D) {
-  const int page = a.block_table[(size_t)b * a.max_pages + (key >> a.c.log2_page)];
+  const int page = bw_page(a, b, key >> a.c.log2_page);
   return (((size_t)page * a.c.page_size + (key & (a.c.page_size - 1))) * a.c.num_kv_heads + hk) * D;
 }
 
 template <int D, typename T>
 __global__ __launch_bounds__(64) void dq_kernel(BackwardArgs a) {
   const int row = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int q0 = a.cu_q[b];
-  const int q_len = a.cu_q[b + 1] - q0;
+  const int q0 = bw_q0(a, b);
+  const int q_len = bw_qlen(a, b, q0);
   if (row >= q_len) return;
-  const int ctx = a.ctx_lens[b];
+  const int ctx = bw_ctx(a, b, q_len);
   const int pos = ctx - q_len + row;
   const int hk = h / a.group;
   const int hi = a.causal ? min(pos, ctx - 1) : ctx - 1;
@@ -154,10 +172,10 @@ __global__ __launch_bounds__(64) void dq_kernel(BackwardArgs a) {
 template <int D, typename T>
 __global__ __launch_bounds__(64) void dkv_kernel(BackwardArgs a) {
   const int key = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
-  const int ctx = a.ctx_lens[b];
+  const int q0 = bw_q0(a, b);
+  const int q_len = bw_qlen(a, b, q0);
+  const int ctx = bw_ctx(a, b, q_len);
   if (key >= ctx) return;
-  const int q0 = a.cu_q[b];
-  const int q_len = a.cu_q[b + 1] - q0;
   const int off = ctx - q_len;  // position of query row 0
   // Rows whose position p sees this key: p >= key (causal), p - key <= W.
   int r_lo = 0, r_hi = q_len - 1;
@@ -238,10 +256,10 @@ template <int D>
 __device__ __forceinline__ void dq_tile(const BackwardArgs &a, int qt, int h, int b, unsigned char *ksm,
                                         unsigned char *vsm) {
   using C = BwCfg<D>;
-  const int q0 = a.cu_q[b];
-  const int q_len = a.cu_q[b + 1] - q0;
+  const int q0 = bw_q0(a, b);
+  const int q_len = bw_qlen(a, b, q0);
   if (qt * kBwRows >= q_len) return;  // uniform
-  const int ctx = a.ctx_lens[b];
+  const int ctx = bw_ctx(a, b, q_len);
   const int off = ctx - q_len;
   const int hk = h / a.group;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -301,7 +319,7 @@ __device__ __forceinline__ void dq_tile(const BackwardArgs &a, int qt, int h, in
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
       const int key = min(kt * kBwKeys + lrow + i * kRowsPerPass, ctx - 1);
-      const int page = a.block_table[(size_t)b * a.max_pages + (key >> a.c.log2_page)];
+      const int page = bw_page(a, b, key >> a.c.log2_page);
       const size_t ro = ((size_t)page * a.c.page_size + (key & (a.c.page_size - 1))) * row_elems + lch * 8;
       kreg[i] = *reinterpret_cast<const u32x4 *>(kpool + ro);
       vreg[i] = *reinterpret_cast<const u32x4 *>(vpool + ro);
@@ -382,17 +400,17 @@ __device__ __forceinline__ void dkv_tile(const BackwardArgs &a, int kt, int hk, 
                                          unsigned char *dosm, float *lse_s, float *dl_s) {
   using C = BwCfg<D>;
   constexpr int kPitch = C::kKRow;
-  const int ctx = a.ctx_lens[b];
+  const int q0 = bw_q0(a, b);
+  const int q_len = bw_qlen(a, b, q0);
+  const int ctx = bw_ctx(a, b, q_len);
   if (kt * kBwKeyTile >= ctx) return;  // uniform
-  const int q0 = a.cu_q[b];
-  const int q_len = a.cu_q[b + 1] - q0;
   const int off = ctx - q_len;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, g = lane >> 5, gam = lane >> 4, tp = lane & 15;
   const int key = kt * kBwKeyTile + w * 32 + col;  // this lane's key (B-operand column)
   const int keyc = min(key, ctx - 1);
   const size_t row_elems = (size_t)a.c.num_kv_heads * D;
-  const int kpage = a.block_table[(size_t)b * a.max_pages + (keyc >> a.c.log2_page)];
+  const int kpage = bw_page(a, b, keyc >> a.c.log2_page);
   const size_t krow = ((size_t)kpage * a.c.page_size + (keyc & (a.c.page_size - 1))) * row_elems + (size_t)hk * D;
   bf16x8 bk[C::kNs], bv[C::kNs];
 #pragma unroll
@@ -535,7 +553,7 @@ __global__ __launch_bounds__(256, 2) void dq_mfma_kernel(BackwardArgs a) {
   __shared__ __align__(16) unsigned char ksm[kBwKeys * C::kKRow];
   __shared__ __align__(16) unsigned char vsm[kBwKeys * C::kVRow];
   const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int n = (a.cu_q[b + 1] - a.cu_q[b] + kBwRows - 1) / kBwRows;
+  const int n = (bw_qlen(a, b, bw_q0(a, b)) + kBwRows - 1) / kBwRows;
   if (p >= (n + 1) / 2) return;  // uniform
   dq_tile<D>(a, n - 1 - p, h, b, ksm, vsm);
   if (n - 1 - p != p) {
@@ -555,7 +573,7 @@ __global__ __launch_bounds__(256) void dkv_mfma_kernel(BackwardArgs a) {
   __shared__ __align__(16) unsigned char dosm[kBwRowTile * C::kKRow];
   __shared__ float lse_s[kBwRowTile], dl_s[kBwRowTile];
   const int p = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
-  const int n = (a.ctx_lens[b] + kBwKeyTile - 1) / kBwKeyTile;
+  const int n = (bw_ctx(a, b, bw_qlen(a, b, bw_q0(a, b))) + kBwKeyTile - 1) / kBwKeyTile;
   if (p >= (n + 1) / 2) return;  // uniform
   dkv_tile<D>(a, p, hk, b, qsm, dosm, lse_s, dl_s);
   if (n - 1 - p != p) {
@@ -588,6 +606,8 @@ hipError_t launch_t(const BackwardArgs &a, hipStream_t s) {
 }
 
 }  // namespace
+
+PA_DEFINE_FAULT_READER(take_fault_backward)
 
 hipError_t launch_backward(const BackwardArgs &a, hipStream_t s) {
   if (a.batch == 0 || a.total_q == 0) return hipSuccess;

@@ -87,6 +87,12 @@ __device__ __forceinline__ int seg_tiles(int ctx, int window_left) {
   return (ctx + kDecTile - 1) / kDecTile - lo / kDecTile;
 }
 
+// ctx_lens[b] of a decode (checked in debug builds against [0, the keys its
+// block-table row can address]).
+__device__ __forceinline__ int ctx_len(const DecodeArgs &a, int b) {
+  return checked(a.ctx_lens[b], 0, a.max_pages << a.c.log2_page, kSiteCtxLen, b);
+}
+
 // Workgroups that actually take tiles: at least kMinTilesPerWg tiles each.
 // One: a small problem (a few short contexts) is spread over as many
 // workgroups as it has tiles, so its time is about one tile's latency rather
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(kDecWaves * 64, kDecWaves / 4 * WPC) void decode_sp
   const int b_lo = min(a.batch, (int)threadIdx.x * per);
   const int b_hi = min(a.batch, b_lo + per);
   int mine = 0;
-  for (int bb = b_lo; bb < b_hi; ++bb) mine += seg_tiles(a.ctx_lens[bb], W);
+  for (int bb = b_lo; bb < b_hi; ++bb) mine += seg_tiles(ctx_len(a, bb), W);
   int incl = mine;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -186,7 +192,7 @@ __global__ __launch_bounds__(kDecWaves * 64, kDecWaves / 4 * WPC) void decode_sp
     int acc = excl;
     for (int bb = b_lo; bb < b_hi; ++bb) {
       a.ws_prefix[bb] = acc;
-      acc += seg_tiles(a.ctx_lens[bb], W);
+      acc += seg_tiles(ctx_len(a, bb), W);
     }
     if (threadIdx.x == 0) a.ws_prefix[a.batch] = per_group_total;
   }
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(kDecWaves * 64, kDecWaves / 4 * WPC) void decode_sp
   if ((long long)ngr * excl <= start && start < (long long)ngr * (excl + mine)) {
     int acc = excl;
     for (int bb = b_lo; bb < b_hi; ++bb) {
-      const int n = seg_tiles(a.ctx_lens[bb], W);
+      const int n = seg_tiles(ctx_len(a, bb), W);
       if (start < (long long)ngr * (acc + n)) {
         s_first[0] = bb;
         s_first[1] = acc;
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(kDecWaves * 64, kDecWaves / 4 * WPC) void decode_sp
   unsigned char *vs = smem + w * kDecTile * C::kVRow;
 
   int b = s_first[0];
-  int nb = seg_tiles(a.ctx_lens[b], W);
+  int nb = seg_tiles(ctx_len(a, b), W);
   const int r0 = (int)(start - (long long)ngr * s_first[1]);
   int hg = r0 / nb;
   int tloc = r0 - hg * nb;
@@ -224,7 +230,7 @@ __global__ __launch_bounds__(kDecWaves * 64, kDecWaves / 4 * WPC) void decode_sp
 
   while (remaining > 0) {
     const int len = (int)min((long long)(nb - tloc), remaining);
-    const int ctx = a.ctx_lens[b];
+    const int ctx = ctx_len(a, b);
     const int lo = W >= 0 ? max(0, ctx - 1 - W) : 0;
     const int t_first = lo / kDecTile + tloc;  // first tile of this piece
     const int k_begin = max(lo, t_first * kDecTile);
@@ -258,7 +264,7 @@ __global__ __launch_bounds__(kDecWaves * 64, kDecWaves / 4 * WPC) void decode_sp
       const int t = t_first + sub + wph * min(i, n_w - 1);
       const int bs = min(max(t * kDecTile + 16 * kb, lo16), hi16);
       const int key = min(max(t * kDecTile + 16 * kb + r16, k_begin), k_end - 1);
-      const size_t pbase = (size_t)bt[bs >> lp] * page_bytes + head_off;
+      const size_t pbase = (size_t)checked(bt[bs >> lp], 0, a.c.num_pages - 1, kSitePageId, b) * page_bytes + head_off;
       off = (uint32_t)(key & ((1 << lp) - 1)) * row_bytes + 16 * g;
       return make_rsrc((const char *)pool + pbase, page_bytes - head_off);
     };
@@ -323,7 +329,7 @@ __global__ __launch_bounds__(kDecWaves * 64, kDecWaves / 4 * WPC) void decode_sp
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const int bs = min(max(key0 + 16 * kb, lo16), hi16);
-          const int page = bt[bs >> lp];
+          const int page = checked(bt[bs >> lp], 0, a.c.num_pages - 1, kSitePageId, b);
           sl[kb] *= k_scales[(size_t)page * hkv + hk];
           vsc[kb] = v_scales[(size_t)page * hkv + hk];
         }
@@ -453,7 +459,7 @@ __global__ __launch_bounds__(kDecWaves * 64, kDecWaves / 4 * WPC) void decode_sp
       hg = 0;
       do {
         ++b;
-        nb = seg_tiles(a.ctx_lens[b], W);
+        nb = seg_tiles(ctx_len(a, b), W);
       } while (nb == 0);
     }
   }
@@ -476,7 +482,7 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs &a, int b, int h
   const int hh = hk - hg * hpw;
   const int G = a.group;
   const long long total = (long long)ngr * a.ws_prefix[a.batch];
-  const int nb = seg_tiles(a.ctx_lens[b], a.window_left);
+  const int nb = seg_tiles(ctx_len(a, b), a.window_left);
   if (total == 0 || nb == 0) return;
   const int nwg = active_wgs(total, a.nwg);
   const long long f0 = (long long)ngr * a.ws_prefix[b] + (long long)hg * nb;
@@ -538,10 +544,14 @@ __global__ __launch_bounds__(64) void rowwise_f32_kernel(const float *q, const i
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   // cu_q == nullptr: one query per sequence (decode), row b of q.
-  const int q0 = cu_q != nullptr ? cu_q[b] : b;
-  const int q_len = cu_q != nullptr ? cu_q[b + 1] - q0 : 1;
+  const int q0 = cu_q != nullptr ? checked(cu_q[b], 0, 0x7fffffff, kSiteRowOffset, b) : b;
+  const int q_len = cu_q != nullptr
+                        ? checked(cu_q[b + 1] - q0, 0, min((int)gridDim.x, max_pages << c.log2_page), kSiteQueryLen, b)
+                        : 1;
   if (row >= q_len) return;
-  const int ctx = ctx_lens[b];
+  // prefill rows need their own positions in the context; a decode query
+  // may have none (ctx 0: O = 0, lse = -inf)
+  const int ctx = checked(ctx_lens[b], cu_q != nullptr ? q_len : 0, max_pages << c.log2_page, kSiteCtxLen, b);
   const int pos = ctx - q_len + row;
   const int hk = h / group;
   const int hi = causal ? pos : ctx - 1;                      // last visible key
@@ -553,7 +563,8 @@ __global__ __launch_bounds__(64) void rowwise_f32_kernel(const float *q, const i
   const size_t row_elems = (size_t)c.num_kv_heads * D;
   const int P = c.page_size;
   auto row_off = [&](int key) {
-    const int page = block_table[(size_t)b * max_pages + (key >> c.log2_page)];
+    const int page = checked(block_table[(size_t)b * max_pages + (key >> c.log2_page)], 0, c.num_pages - 1,
+                             kSitePageId, b);
     return ((size_t)page * P + (key & (P - 1))) * row_elems + (size_t)hk * D;
   };
   constexpr int kPer = D / 64;
@@ -637,6 +648,8 @@ static hipError_t launch_reduce(const DecodeArgs &a, const DecodeArgs &a2, hipSt
     hipLaunchKernelGGL((decode_reduce_kernel<128, NP>), grid, dim3(256), 0, s, a, a2);
   return hipGetLastError();
 }
+
+PA_DEFINE_FAULT_READER(take_fault_decode)
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa_internal.h"
+
 namespace pa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -122,6 +124,50 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   r[6] = (__bf16)(float)(int8_t)((hi >> 16) & 0xff);
   r[7] = (__bf16)(float)(int8_t)(hi >> 24);
   return r;
+}
+
+// ---- Device checks of device-resident integers (debug builds) -----------
+//
+// checked(v, lo, hi, site, b): v when lo <= v <= hi.  In a build with
+// PA_DEVICE_CHECKS=1 an out-of-range v is recorded in this source file's
+// fault record (the first one wins) and lo is returned instead, so that the
+// kernel's accesses stay inside the caller's buffers (callers choose ranges
+// with lo <= hi, lo itself safe); the host reads the record after the
+// launch and reports it.  Release builds return v.
+#if PA_DEVICE_CHECKS
+static __device__ DeviceFault g_device_fault;
+
+__device__ __noinline__ void record_fault(int site, int v, int lo, int hi, int b) {
+  if (atomicCAS(&g_device_fault.flag, 0, -1) == 0) {
+    g_device_fault.site = site;
+    g_device_fault.value = v;
+    g_device_fault.lo = lo;
+    g_device_fault.hi = hi;
+    g_device_fault.batch = b;
+    __threadfence();
+    atomicExch(&g_device_fault.flag, 1);
+  }
+}
+
+#define PA_DEFINE_FAULT_READER(NAME)                                                          \
+  hipError_t NAME(DeviceFault *f) {                                                           \
+    hipError_t e = hipMemcpyFromSymbol(f, HIP_SYMBOL(g_device_fault), sizeof(DeviceFault));   \
+    if (e != hipSuccess || f->flag == 0) return e;                                            \
+    const DeviceFault zero = {};                                                              \
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_device_fault), &zero, sizeof(DeviceFault));         \
+  }
+#else
+#define PA_DEFINE_FAULT_READER(NAME)
+#endif
+
+__device__ __forceinline__ int checked(int v, int lo, int hi, int site, int b) {
+#if PA_DEVICE_CHECKS
+  if (v < lo || v > hi) {
+    record_fault(site, v, lo, hi, b);
+    return lo;
+  }
+#endif
+  return v;
 }
 
 }  // namespace pa

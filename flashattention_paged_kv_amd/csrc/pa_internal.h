@@ -8,6 +8,34 @@
 
 namespace pa {
 
+// Debug builds (PA_DEVICE_CHECKS=1) check, on the device, every
+// device-resident integer a kernel reads against the range its entry point
+// documents; the first violation in a source file is kept in that file's
+// fault record, which the host reads after the launch.  Release builds
+// compile the checks away.
+#ifndef PA_DEVICE_CHECKS
+#define PA_DEVICE_CHECKS 0
+#endif
+
+// What was out of range.
+enum CheckSite : int {
+  kSiteNone = 0,
+  kSitePageId = 1,     // a block-table entry (or a page id to copy) outside [0, num_pages)
+  kSiteCtxLen = 2,     // a context length outside [q_len, max_pages_per_seq * page_size]
+  kSiteQueryLen = 3,   // a query count (prefix-sum difference) outside [0, max_q_len]
+  kSiteNewLen = 4,     // a new-row count outside [0, max_new]
+  kSiteStartPos = 5,   // an append's first position outside [0, max_pages_per_seq * page_size - rows]
+  kSiteRowOffset = 6,  // a prefix sum (first row of a sequence) below 0
+};
+
+struct DeviceFault {
+  int flag;   // 0: nothing recorded
+  int site;   // a CheckSite
+  int value;  // the value read
+  int lo, hi; // the range it had to lie in
+  int batch;  // the sequence (or page pair) it belongs to
+};
+
 // A paged cache as the kernels see it.
 struct CacheView {
   const void *k;
@@ -37,6 +65,7 @@ struct AppendArgs {
   int page_size;
   int log2_page;
   int row_bytes;  // num_kv_heads * head_dim * element size
+  int num_pages;  // pages of the pools (device checks only)
 };
 
 // Append into an int8 cache: bf16 rows in, codes and scales requantised
@@ -58,6 +87,7 @@ struct AppendI8Args {
   int log2_page;
   int num_kv_heads;
   int head_dim;
+  int num_pages;  // pages of the pools (device checks only)
 };
 
 struct QuantArgs {
@@ -175,6 +205,17 @@ hipError_t launch_append_i8(const AppendI8Args &a, hipStream_t s);
 hipError_t launch_backward(const BackwardArgs &a, hipStream_t s);
 // Copy whole pages src[i] -> dst[i] (K, V and, when given, their scales).
 hipError_t launch_copy_pages(void *k, void *v, float *k_scales, float *v_scales, int num_kv_heads,
-                             const int32_t *src, const int32_t *dst, int n, size_t page_bytes, hipStream_t s);
+                             const int32_t *src, const int32_t *dst, int n, size_t page_bytes, int num_pages,
+                             hipStream_t s);
+
+#if PA_DEVICE_CHECKS
+// Each kernel source file's fault record: copied to *f and cleared (if a
+// fault was recorded).  Call after the launches have completed.
+hipError_t take_fault_append(DeviceFault *f);
+hipError_t take_fault_prefill(DeviceFault *f);
+hipError_t take_fault_decode(DeviceFault *f);
+hipError_t take_fault_backward(DeviceFault *f);
+hipError_t take_fault_page_pool(DeviceFault *f);
+#endif
 
 }  // namespace pa

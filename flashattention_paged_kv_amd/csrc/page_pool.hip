@@ -23,6 +23,7 @@
 #include <vector>
 
 #include "../../include/pagedattn.h"
+#include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -67,18 +68,21 @@ pa_status check_seq(const pa_page_pool *pool, int32_t seq) {
 // chunks, and (int8 caches) the page's per-head scales.
 __global__ __launch_bounds__(256) void copy_pages_kernel(uint4 *k, uint4 *v, float *k_scales, float *v_scales,
                                                          int num_kv_heads, const int32_t *src_pages,
-                                                         const int32_t *dst_pages, size_t page_chunks) {
+                                                         const int32_t *dst_pages, size_t page_chunks,
+                                                         int num_pages) {
   const int i = blockIdx.y;
-  const size_t src = (size_t)src_pages[i] * page_chunks;
-  const size_t dst = (size_t)dst_pages[i] * page_chunks;
+  const int sp = pa::checked(src_pages[i], 0, num_pages - 1, pa::kSitePageId, i);
+  const int dp = pa::checked(dst_pages[i], 0, num_pages - 1, pa::kSitePageId, i);
+  const size_t src = (size_t)sp * page_chunks;
+  const size_t dst = (size_t)dp * page_chunks;
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < page_chunks; e += (size_t)gridDim.x * blockDim.x) {
     k[dst + e] = k[src + e];
     v[dst + e] = v[src + e];
   }
   if (k_scales != nullptr && blockIdx.x == 0 && (int)threadIdx.x < num_kv_heads) {
     const size_t h = threadIdx.x;
-    k_scales[(size_t)dst_pages[i] * num_kv_heads + h] = k_scales[(size_t)src_pages[i] * num_kv_heads + h];
-    v_scales[(size_t)dst_pages[i] * num_kv_heads + h] = v_scales[(size_t)src_pages[i] * num_kv_heads + h];
+    k_scales[(size_t)dp * num_kv_heads + h] = k_scales[(size_t)sp * num_kv_heads + h];
+    v_scales[(size_t)dp * num_kv_heads + h] = v_scales[(size_t)sp * num_kv_heads + h];
   }
 }
 
@@ -86,13 +90,16 @@ __global__ __launch_bounds__(256) void copy_pages_kernel(uint4 *k, uint4 *v, flo
 
 namespace pa {
 
+PA_DEFINE_FAULT_READER(take_fault_page_pool)
+
 hipError_t launch_copy_pages(void *k, void *v, float *k_scales, float *v_scales, int num_kv_heads,
-                             const int32_t *src, const int32_t *dst, int n, size_t page_bytes, hipStream_t s) {
+                             const int32_t *src, const int32_t *dst, int n, size_t page_bytes, int num_pages,
+                             hipStream_t s) {
   if (n == 0) return hipSuccess;
   const size_t chunks = page_bytes / 16;
   const int gx = (int)((chunks + 255) / 256 < 16 ? (chunks + 255) / 256 : 16);
   hipLaunchKernelGGL(copy_pages_kernel, dim3(gx, n), dim3(256), 0, s, (uint4 *)k, (uint4 *)v, k_scales, v_scales,
-                     num_kv_heads, src, dst, chunks);
+                     num_kv_heads, src, dst, chunks, num_pages);
   return hipGetLastError();
 }
 

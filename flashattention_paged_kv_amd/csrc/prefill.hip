@@ -115,10 +115,18 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // derived from them, in scalar registers, and keeps the loads above the
   // branches below.
   const int b = blockIdx.z;
-  const int q0 = __builtin_amdgcn_readfirstlane(a.cu_q[b]);
-  const int q_len = __builtin_amdgcn_readfirstlane(a.cu_q[b + 1]) - q0;
-  const int ctx = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
-  const int pg0 = RUNS ? 0 : __builtin_amdgcn_readfirstlane(block_table[(size_t)b * a.max_pages]);
+  const int q0_raw = __builtin_amdgcn_readfirstlane(a.cu_q[b]);
+  const int q_end = __builtin_amdgcn_readfirstlane(a.cu_q[b + 1]);
+  const int ctx_raw = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
+  const int pg0_raw = RUNS ? 0 : __builtin_amdgcn_readfirstlane(block_table[(size_t)b * a.max_pages]);
+  // Debug builds: the ranges the entry point documents (no-ops otherwise);
+  // q_len is also bounded by the keys the block-table row can address, so
+  // that a context in [q_len, that bound] exists to stand in for a bad one.
+  const int max_keys = a.max_pages << a.c.log2_page;
+  const int q0 = checked(q0_raw, 0, 0x7fffffff, kSiteRowOffset, b);
+  const int q_len = checked(q_end - q0, 0, min(a.max_q_len, max_keys), kSiteQueryLen, b);
+  const int ctx = checked(ctx_raw, q_len, max_keys, kSiteCtxLen, b);
+  const int pg0 = RUNS || q_len == 0 ? pg0_raw : checked(pg0_raw, 0, a.c.num_pages - 1, kSitePageId, b);
   const int grid_x = gridDim.x, grid_y = gridDim.y;
   // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
   // L2): consecutive ids are remapped so that the pairs of one query head run
@@ -285,7 +293,8 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // Byte offset of key tile kt inside the K (or V) pool (BIG_PAGE: one page).
   auto tile_page_off = [&](int kt) __attribute__((always_inline)) {
     const int key0 = kt * kPfKeys;
-    return ((size_t)block_table[(size_t)b * a.max_pages + (key0 >> lp)] * P + (key0 & (P - 1))) * row_bytes;
+    const int page = checked(block_table[(size_t)b * a.max_pages + (key0 >> lp)], 0, a.c.num_pages - 1, kSitePageId, b);
+    return ((size_t)page * P + (key0 & (P - 1))) * row_bytes;
   };
   auto load_half = [&](int kt, size_t tile_off, const char *base, const char *nbase, uint4 *dst)
       __attribute__((always_inline)) {
@@ -314,7 +323,8 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
         const int key = key0 + lrow + i * kRowsPerPass;
         dst[i] = make_uint4(0, 0, 0, 0);
         if (key < ctx) {
-          const size_t ro = ((size_t)bt[key >> lp] * P + (key & (P - 1))) * row_bytes + lch * 16;
+          const int page = checked(bt[key >> lp], 0, a.c.num_pages - 1, kSitePageId, b);
+          const size_t ro = ((size_t)page * P + (key & (P - 1))) * row_bytes + lch * 16;
           dst[i] = *reinterpret_cast<const uint4 *>(base + ro);
         }
       }
@@ -766,6 +776,8 @@ static int prefill_run_tiles(int n_qt, int heads, int batch) {
   const long long tiles = (long long)n_qt * heads * batch;
   return (int)std::min<long long>(kPfRun, std::max<long long>(1, tiles / device_cu_count()));
 }
+
+PA_DEFINE_FAULT_READER(take_fault_prefill)
 
 hipError_t launch_prefill(const PrefillArgs &a_in, hipStream_t s) {
   if (a_in.batch == 0 || a_in.max_q_len == 0) return hipSuccess;

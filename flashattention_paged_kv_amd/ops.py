@@ -55,7 +55,7 @@ EXPORTED = ("kv_cache_append", "kv_pages_quantize_int8", "attn_prefill_paged", "
             "attn_decode_paged", "attn_decode_paged_noalloc", "attn_decode_layered_workspace_bytes", "attn_decode_paged_layered",
             "kv_cache_copy_pages", "attn_backward_workspace_bytes", "attn_backward_paged", "pa_pool_create", "pa_pool_destroy", "pa_pool_extend", "pa_pool_fork",
             "pa_pool_release", "pa_pool_export", "pa_pool_free_pages", "pa_pool_refcount",
-            "pa_status_string", "pa_last_error_detail", "pa_abi_version")
+            "pa_status_string", "pa_last_error_detail", "pa_abi_version", "pa_device_checks")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -63,6 +63,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """A build of the library at `path` with its argument types declared (not
+    cached: e.g. the debug build beside the release one)."""
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m flashattention_paged_kv_amd.build`")
     lib = ctypes.CDLL(path)
@@ -109,7 +116,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_last_error_detail.argtypes = []
     lib.pa_last_error_detail.restype = ctypes.c_char_p
     lib.pa_abi_version.restype = I32
-    _lib = lib
+    lib.pa_device_checks.restype = I32
     return lib
 
 

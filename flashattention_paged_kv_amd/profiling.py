@@ -92,22 +92,33 @@ def trace_markdown(trace_csv: str, cmd: str, title: str, min_calls: int = 1) -> 
     return "\n".join(out) + "\n"
 
 
-def pmc_markdown(paths, cmds, title: str, simds: int, match: str = "") -> str:
+def pmc_markdown(paths, cmds, title: str, simds: int, xccs: int, match: str = "") -> str:
     """Counters per dispatch, averaged per (kernel, grid), from one or more
     `rocprofv3 --pmc` runs (one counter set each), with the MFMA utilisation
-    they give: SQ_VALU_MFMA_BUSY_CYCLES summed over the SIMDs / (GRBM_GUI_ACTIVE
-    x SIMDs), the expression of rocprofv3's own MfmaUtil metric, and the
-    bf16 MFMA work executed (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOPs)."""
+    they give and the bf16 MFMA work executed (SQ_INSTS_VALU_MFMA_MOPS_BF16 x
+    512 FLOPs).
+
+    SQ_VALU_MFMA_BUSY_CYCLES arrives summed over every SIMD of the device
+    (for v_mfma_f32_32x32x16_bf16 it equals 32 cycles x the MFMAs executed),
+    GRBM_GUI_ACTIVE summed over the XCDs (each counts the cycles its XCD was
+    busy), so the utilisation is busy / (SIMDs x GRBM_GUI_ACTIVE / XCDs):
+    rocprofv3's own MfmaUtil expression, which takes the largest XCD's count
+    instead of the sum.  The shader clock implied by GRBM_GUI_ACTIVE / XCDs
+    over the dispatch's duration is shown beside it."""
     vals = defaultdict(lambda: defaultdict(list))
+    durs = defaultdict(dict)
     for path in paths:
         for r in csv.DictReader(open(path)):
             if match and match not in r["Kernel_Name"]:
                 continue
             key = (_short(r["Kernel_Name"]), r.get("Grid_Size", "?"))
             vals[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                durs[key][len(vals[key]["GRBM_GUI_ACTIVE"]) - 1] = (
+                    float(r["Counter_Value"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     out = [f"# {title}", "", "Commands (from the repository root, on one MI355X; one counter set per run):", "",
            "```", *cmds, "```", "",
-           f"Per dispatch, averaged over the dispatches of each (kernel, grid); {simds} SIMDs.", ""]
+           f"Per dispatch, averaged over the dispatches of each (kernel, grid); {simds} SIMDs in {xccs} XCDs.", ""]
     for (name, grid), cs in sorted(vals.items()):
         out.append(f"## `{name}`, grid {grid} work items")
         out.append("")
@@ -116,9 +127,17 @@ def pmc_markdown(paths, cmds, title: str, simds: int, match: str = "") -> str:
         for c, v in sorted(cs.items()):
             out.append(f"| {c} | {len(v)} | {statistics.fmean(v):.6g} |")
         m = {c: statistics.fmean(v) for c, v in cs.items()}
+        if "GRBM_GUI_ACTIVE" in m and durs[(name, grid)]:
+            ghz = statistics.fmean(g / xccs / max(1, d) for g, d in durs[(name, grid)].values())
+            out.append(f"| shader clock implied (GRBM_GUI_ACTIVE / XCDs / duration) | | {ghz:.2f} GHz |")
         if "SQ_VALU_MFMA_BUSY_CYCLES" in m and "GRBM_GUI_ACTIVE" in m and m["GRBM_GUI_ACTIVE"] > 0:
-            out.append(f"| **MFMA utilisation** (busy / (GUI_ACTIVE x SIMDs)) | | "
-                       f"**{100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (m['GRBM_GUI_ACTIVE'] * simds):.1f}%** |")
+            out.append(f"| **MFMA utilisation** (busy / (SIMDs x GRBM_GUI_ACTIVE / XCDs)) | | "
+                       f"**{100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (m['GRBM_GUI_ACTIVE'] / xccs * simds):.1f}%** |")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m and durs[(name, grid)]:
+            dur_ns = statistics.fmean(d for _, d in durs[(name, grid)].values())
+            out.append(f"| MFMA busy / (SIMDs x dispatch duration x 2.4 GHz): share of the nominal peak | | "
+                       f"{100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / simds / (dur_ns * 2.4):.1f}% "
+                       f"(duration {dur_ns / 1e3:.1f} µs) |")
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in m:
             out.append(f"| bf16 MFMA FLOPs executed (MOPS x 512) | | {m['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.6g} |")
         out.append("")
@@ -175,6 +194,7 @@ def main(argv=None) -> int:
     pm.add_argument("--cmd", action="append", required=True, help="the rocprofv3 command of each run")
     pm.add_argument("--title", required=True)
     pm.add_argument("--simds", type=int, default=1024, help="SIMDs of the device (MI355X: 256 CUs x 4)")
+    pm.add_argument("--xccs", type=int, default=8, help="XCDs of the device (MI355X: 8)")
     pm.add_argument("--match", default="", help="only kernels whose name contains this")
     pm.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
@@ -190,7 +210,7 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
     if args.action == "pmc":
         with open(args.out, "w") as f:
-            f.write(pmc_markdown(args.csv, args.cmd, args.title, args.simds, args.match))
+            f.write(pmc_markdown(args.csv, args.cmd, args.title, args.simds, args.xccs, args.match))
         return 0
     if args.action == "trace":
         with open(args.out, "w") as f:

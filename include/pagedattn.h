@@ -43,9 +43,15 @@
  *     check are checked before any work is enqueued (PA_ERR_INVALID_ARG,
  *     PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE); a failed launch returns
  *     PA_ERR_HIP.  Device-resident integers (block-table entries, lengths,
- *     prefix sums) are not validated: out-of-range values are undefined
- *     behaviour.  pa_last_error_detail() gives a message for the last failure
- *     on the calling thread.
+ *     prefix sums) are not validated in release builds: out-of-range values
+ *     are undefined behaviour.  A debug build (pa_device_checks() == 1)
+ *     checks each of them on the device against the range the entry point
+ *     documents, keeps every access inside the caller's buffers, waits for
+ *     its kernels at the end of each call and returns PA_ERR_DEVICE_ASSERT
+ *     for the first violation (what, which sequence, value and range in
+ *     pa_last_error_detail(); the outputs are then undefined).
+ *     pa_last_error_detail() gives a message for the last failure on the
+ *     calling thread.
  *   - Thread safety: no global mutable state apart from a per-thread error
  *     string and a once-initialised device-property cache.
  */
@@ -67,7 +73,8 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, page_size, dtype  */
   PA_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed        */
   PA_ERR_WORKSPACE = 4,   /* decode workspace missing or too small             */
-  PA_ERR_OUT_OF_PAGES = 5 /* a page pool has too few free pages (no change)    */
+  PA_ERR_OUT_OF_PAGES = 5, /* a page pool has too few free pages (no change)   */
+  PA_ERR_DEVICE_ASSERT = 6 /* debug builds: a device-side range check failed   */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -366,6 +373,11 @@ const char *pa_last_error_detail(void);
 
 /* PA_ABI_VERSION of the built library. */
 int32_t pa_abi_version(void);
+
+/* 1 for a debug build with device-side checks of block-table entries,
+ * lengths and prefix sums (synchronous calls, PA_ERR_DEVICE_ASSERT), 0 for
+ * a release build. */
+int32_t pa_device_checks(void);
 
 #ifdef __cplusplus
 }
