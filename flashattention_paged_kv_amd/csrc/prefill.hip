@@ -98,6 +98,17 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   static_assert(!FUSED || BIG_PAGE, "the fused append needs whole key tiles inside one page");
   using C = PfCfg<D>;
   __shared__ __align__(16) unsigned char smem[2 * C::kEngine];
+  // kDirect: K/V tiles go from global memory straight into LDS (16-byte
+  // buffer loads with the LDS as destination) instead of through registers;
+  // their rows are then unpadded (2D bytes) and XOR-swizzled in 16-byte
+  // chunks (see direct_k_chunk / direct_v_chunk).  Tiles of new keys (the
+  // fused append) and pages smaller than a tile keep the register path.
+  constexpr bool kDirect = BIG_PAGE && !FUSED && D == 128;
+  constexpr int kKRowL = kDirect ? 2 * D : C::kKRow;  // LDS row pitch of staged K
+  constexpr int kVRowL = kDirect ? 2 * D : C::kVRow;  // and of staged V
+  constexpr int kKBufL = kPfKeys * kKRowL;
+  constexpr int kVBufL = kPfKeys * kVRowL;
+  static_assert(2 * (kKBufL + kVBufL) <= C::kEngine, "an engine's two K/V buffers must fit its LDS share");
 
   const int eng = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);  // 0: forward, 1: backward
   const int tid = threadIdx.x & (kPfEngineThreads - 1);
@@ -332,8 +343,48 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   };
   const uint32_t lane_koff = (uint32_t)lrow * C::kKRow + lch * 16;
   const uint32_t lane_voff = (uint32_t)lrow * C::kVRow + lch * 16;
-  auto kbuf = [&](int buf) __attribute__((always_inline)) { return ebase + buf * (C::kKBuf + C::kVBuf); };
-  auto vbuf = [&](int buf) __attribute__((always_inline)) { return ebase + buf * (C::kKBuf + C::kVBuf) + C::kKBuf; };
+  auto kbuf = [&](int buf) __attribute__((always_inline)) { return ebase + buf * (kKBufL + kVBufL); };
+  auto vbuf = [&](int buf) __attribute__((always_inline)) { return ebase + buf * (kKBufL + kVBufL) + kKBufL; };
+  // Direct path: wave w's load i of a tile fills rows 16 i + 4 w .. +3 (1 KiB,
+  // lane l: row 16 i + 4 w + l / 16, physical chunk l % 16).  The lane loads
+  // the logical chunk that the swizzle puts there, from its row in the page.
+  // K: chunk c of row r sits at chunk c ^ (r % 16), so the 16 rows an MFMA
+  // operand read touches at one logical chunk fall in 16 different bank
+  // groups.  V: chunk c of row r sits at c ^ 2 (r % 4), so the four rows a
+  // transposed read takes two adjacent chunks from fall in four different
+  // 32-byte bank groups.  Both are the same for every i, so each lane's
+  // source offset inside a tile is fixed.
+  const int drow = 4 * w + (lane >> 4);
+  const uint32_t lane_dk = (uint32_t)drow * (uint32_t)row_bytes + (uint32_t)(((lane & 15) ^ (drow & 15)) * 16);
+  const uint32_t lane_dv = (uint32_t)drow * (uint32_t)row_bytes + (uint32_t)(((lane & 15) ^ ((drow & 3) << 1)) * 16);
+  // Tile kt (its page offset tile_off) of the pool at `base` into the LDS
+  // buffer `dst`: four 16-byte loads per lane, through a descriptor whose
+  // range ends at the context's last key (rows past it arrive as zeros).
+  auto issue_direct = [&](int kt, size_t tile_off, const char *base, unsigned char *dst, uint32_t lane_off)
+      __attribute__((always_inline)) {
+    if constexpr (kDirect) {
+      const int key0 = kt * kPfKeys;
+      const uint32_t span = (uint32_t)(min(kPfKeys, ctx - key0) * row_bytes);
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(base + tile_off, span);
+#pragma unroll
+      for (int i = 0; i < C::kLoads; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PA_LDS void *)(dst + (16 * i + 4 * w) * kKRowL), 16,
+                                                 lane_off + (uint32_t)(16 * i) * (uint32_t)row_bytes, 0, 0, 0);
+    }
+  };
+  // Direct path, reading side: the byte offset inside a row of this lane's
+  // K operand chunk for k-step s (logical chunk 2 s + g, swizzled by the row
+  // col % 16), and the offset of its transposed V read for output block db
+  // from the first of the 16-row group (row g * 4 + tp / 4, logical chunk
+  // 4 db + 2 (gam % 2) + (tp % 4) / 2, swizzled by the row % 4 = tp / 4,
+  // plus the 8-byte half (tp % 2)).
+  uint32_t kd_off[C::kNs], vd_off[C::kNdb];
+#pragma unroll
+  for (int s2 = 0; s2 < C::kNs; ++s2) kd_off[s2] = (uint32_t)((((2 * s2 + g) ^ (col & 15)) & 15) * 16);
+#pragma unroll
+  for (int db = 0; db < C::kNdb; ++db)
+    vd_off[db] = (uint32_t)((g * 4 + (tp >> 2)) * kVRowL +
+                            (((4 * db + 2 * (gam & 1) + ((tp & 3) >> 1)) ^ ((tp >> 2) << 1)) & 15) * 16 + 8 * (tp & 1));
   auto store_k = [&](int buf, const uint4 *src) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i)
@@ -468,7 +519,10 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     constexpr int kAhead = 6;
     auto rd = [&](int u) __attribute__((always_inline)) {
       const int kb = u / C::kNs, s = u % C::kNs;
-      return *reinterpret_cast<const bf16x8 *>(ks + (kb * 32 + col) * C::kKRow + (16 * s + 8 * g) * 2);
+      if constexpr (kDirect)  // logical chunk 2 s + g of row kb * 32 + col, swizzled by the row
+        return *reinterpret_cast<const bf16x8 *>(ks + (kb * 32 + col) * kKRowL + kd_off[s]);
+      else
+        return *reinterpret_cast<const bf16x8 *>(ks + (kb * 32 + col) * C::kKRow + (16 * s + 8 * g) * 2);
     };
     bf16x8 ka[kAhead];
 #pragma unroll
@@ -491,8 +545,13 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     const int r0 = (t >> 1) * 32 + (t & 1) * 16 + g * 4;
 #pragma unroll
     for (int db = 0; db < C::kNdb; ++db) {
-      const unsigned char *p1 = vs + (r0 + (tp >> 2)) * C::kVRow + (db * 32 + 16 * (gam & 1) + 4 * (tp & 3)) * 2;
-      va[db] = cat(lds_read_tr16(p1), lds_read_tr16(p1 + 8 * C::kVRow));
+      if constexpr (kDirect) {
+        const unsigned char *p1 = vs + ((t >> 1) * 32 + (t & 1) * 16) * kVRowL + vd_off[db];
+        va[db] = cat(lds_read_tr16(p1), lds_read_tr16(p1 + 8 * kVRowL));
+      } else {
+        const unsigned char *p1 = vs + (r0 + (tp >> 2)) * C::kVRow + (db * 32 + 16 * (gam & 1) + 4 * (tp & 3)) * 2;
+        va[db] = cat(lds_read_tr16(p1), lds_read_tr16(p1 + 8 * C::kVRow));
+      }
     }
   };
   auto pv_mfma = [&](int buf) __attribute__((always_inline)) {
@@ -589,7 +648,54 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // tile 1 there; G(0) reads Q^T from it.
   constexpr int kQLoads = kPfRows * C::kCpr / kPfEngineThreads;
   static_assert(kPfRows * C::kKRow <= C::kKBuf + C::kVBuf, "Q tile must fit one K/V buffer");
-  if (n_mine > 0) {
+  // Direct path barriers: a bare s_barrier (a workgroup fence would also
+  // wait for every LDS-bound load in flight) with the waits it needs made
+  // explicit; the empty asm statements keep the compiler from moving memory
+  // accesses across it.  After a GEMM phase: this wave's LDS reads are done
+  // (the buffers they read are reloaded in the next phase).  After a softmax
+  // phase and after the prologue: every load but the last 8 (those of this
+  // phase: the next-but-one K tile and the next V tile) has landed.  (The
+  // compiler, which cannot tell those 8 LDS writes from the next GEMM
+  // phase's LDS reads, also waits for them before its first read: their
+  // latency hides behind the softmax phase.)
+  constexpr int kWaitLgkm0 = 0xC07F;  // vmcnt(63) expcnt(7) lgkmcnt(0)
+  constexpr int kWaitVm8 = 0x0F78;    // vmcnt(8) expcnt(7) lgkmcnt(15)
+  auto bar_after_gemm = [&]() __attribute__((always_inline)) {
+    if constexpr (kDirect) {
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __asm__ volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+    } else {
+      __syncthreads();
+    }
+  };
+  auto bar_after_loads = [&]() __attribute__((always_inline)) {
+    if constexpr (kDirect) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm8);
+      __asm__ volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+    } else {
+      __syncthreads();
+    }
+  };
+  if constexpr (kDirect) {
+    // Q^T of the first query tile straight into registers, then K(0), V(0)
+    // and K(1) into LDS buffers 0, 0 and 1 (K(t + 2) and V(t + 1) follow in
+    // softmax phase t, once the buffers' previous tiles have been read).
+    if (n_mine > 0) {
+      int qt, kt, q1, k1;
+      my_item(0, qt, kt);
+      load_q_async(qt);
+      qt_q = qt;
+      const size_t off0 = (!RUNS && kt == 0) ? (size_t)pg0 * P * row_bytes : tile_page_off(kt);
+      issue_direct(kt, off0, kbase, kbuf(0), lane_dk);
+      issue_direct(kt, off0, vbase, vbuf(0), lane_dv);
+      my_item(min(1, n_mine - 1), q1, k1);
+      issue_direct(k1, tile_page_off(k1), kbase, kbuf(1), lane_dk);
+    }
+  } else if (n_mine > 0) {
     int qt, kt;
     my_item(0, qt, kt);
     if (!RUNS && BIG_PAGE && kt == 0) {
@@ -613,7 +719,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       *reinterpret_cast<u32x4 *>(kbuf(1) + (lrow + i * kRowsPerPass) * C::kKRow + lch * 16) = qs[i];
     write_new(0);
   }
-  __syncthreads();
+  bar_after_loads();
   // Wave priorities: the GEMM wave's MFMAs are the critical path of each
   // half-step, so its instructions win issue slots over the other engine's
   // softmax on the same SIMD.
@@ -622,16 +728,18 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     // Inside the loop the next tile's loads are unconditional (the last step
     // re-reads its own tile, never stored): the same loads are in flight on
     // every path, so the wait counts stay exact.
-    if (t < n_mine) {
-      int qt, kt;
-      my_item(min(t + 1, n_mine - 1), qt, kt);
-      load_tile(kt);
+    if constexpr (!kDirect) {
+      if (t < n_mine) {
+        int qt, kt;
+        my_item(min(t + 1, n_mine - 1), qt, kt);
+        load_tile(kt);
+      }
     }
     if (t >= 1) pv_mfma((t - 1) & 1);
     if (t < n_mine) {
       int qt, kt;
       my_item(t, qt, kt);
-      if (t == 0) {
+      if (!kDirect && t == 0) {
 #pragma unroll
         for (int s = 0; s < C::kNs; ++s)
           bq[s] = *reinterpret_cast<const bf16x8 *>(kbuf(1) + (w * 32 + col) * C::kKRow + (16 * s + 8 * g) * 2);
@@ -672,10 +780,24 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       reset_o();
       qt_o = qt;
     }
+    if constexpr (kDirect) {
+      // K buffer t % 2 (K(t), read in G(t)) takes K(t + 2); V buffer
+      // (t + 1) % 2 (V(t - 1), read in G(t)) takes V(t + 1).  The softmax
+      // wave issues them, off the GEMM wave's path.  Past the engine's last
+      // item the last tile is loaded again into buffers no later phase
+      // reads, so every phase issues the same loads.
+      int q2, k2, q1, k1;
+      my_item(min(t + 2, n_mine - 1), q2, k2);
+      my_item(min(t + 1, n_mine - 1), q1, k1);
+      issue_direct(k2, tile_page_off(k2), kbase, kbuf(t & 1), lane_dk);
+      issue_direct(k1, tile_page_off(k1), vbase, vbuf((t + 1) & 1), lane_dv);
+    }
     softmax(qt, kt);
-    if (t + 1 < n_mine) {
-      store_k((t + 1) & 1, pk);
-      store_v((t + 1) & 1, pv);
+    if constexpr (!kDirect) {
+      if (t + 1 < n_mine) {
+        store_k((t + 1) & 1, pk);
+        store_v((t + 1) & 1, pv);
+      }
     }
   };
   // Engine 0 passes 2 * half + 1 barriers in its loop, engine 1 one leading
@@ -685,22 +807,24 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   if (eng == 0) {
     for (int t = 0; t < n_mine; ++t) {
       gemm_phase(t);
-      __syncthreads();
+      bar_after_gemm();
       softmax_phase(t);
-      __syncthreads();
+      bar_after_loads();
     }
     gemm_phase(n_mine);
+    if constexpr (kDirect) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes the LDS
     __syncthreads();
     if (half == n1) __syncthreads();
   } else {
-    __syncthreads();
+    bar_after_gemm();
     for (int t = 0; t < n_mine; ++t) {
       gemm_phase(t);
-      __syncthreads();
+      bar_after_gemm();
       softmax_phase(t);
-      __syncthreads();
+      bar_after_loads();
     }
     gemm_phase(n_mine);
+    if constexpr (kDirect) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes the LDS
     __syncthreads();
     if (half > n1) __syncthreads();
   }
