@@ -108,7 +108,8 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   constexpr int kVRowL = kDirect ? 2 * D : C::kVRow;  // and of staged V
   constexpr int kKBufL = kPfKeys * kKRowL;
   constexpr int kVBufL = kPfKeys * kVRowL;
-  static_assert(2 * (kKBufL + kVBufL) <= C::kEngine, "an engine's two K/V buffers must fit its LDS share");
+  static_assert(2 * (kKBufL + kVBufL) + (kDirect ? 4 * 1024 : 0) <= C::kEngine,
+                "an engine's two K/V buffers (and, direct, its waves' scratch) must fit its LDS share");
 
   const int eng = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);  // 0: forward, 1: backward
   const int tid = threadIdx.x & (kPfEngineThreads - 1);
@@ -241,6 +242,9 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
         rk[r] = lo[r];
       }
     } else {
+      // Engine 1 also walks each query tile's key tiles downward (rk: the
+      // highest), so that consecutive query tiles of a window meet the key
+      // tiles they share as neighbouring items (see `resident`).
       int at = 0;
 #pragma unroll
       for (int j = 0; j < kPfRun; ++j) {
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
         const int first = max(cum[r], half);
         st[j] = at;
         rq[j] = q_begin + r;
-        rk[j] = lo[r] + (first - cum[r]);
+        rk[j] = lo[r] + (cum[r + 1] - cum[r]) - 1;
         at += max(0, cum[r + 1] - first);
       }
     }
@@ -257,17 +261,20 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // my_item(t): run j applies when t >= st[j] (runs in increasing start
   // order, empty ones telescoping away).  Written as sums of "value or zero"
   // offsets between consecutive runs, kept in scalar registers.
+  // Run j's key tile at item t is rk[j] + ks (t - st[j]), ks = 1 (upward)
+  // or -1 (downward: engine 1 in run mode).
+  const int ks = (RUNS && eng == 1) ? -1 : 1;
   int dst[kRuns], ddq[kRuns], ddk[kRuns];
   const int q_base = __builtin_amdgcn_readfirstlane(rq[0]);
-  const int k_base = __builtin_amdgcn_readfirstlane(rk[0] - st[0]);
+  const int k_base = __builtin_amdgcn_readfirstlane(rk[0] - ks * st[0]);
 #pragma unroll
   for (int j = 1; j < kRuns; ++j) {
     dst[j] = __builtin_amdgcn_readfirstlane(st[j]);
     ddq[j] = __builtin_amdgcn_readfirstlane(rq[j] - rq[j - 1]);
-    ddk[j] = __builtin_amdgcn_readfirstlane((rk[j] - st[j]) - (rk[j - 1] - st[j - 1]));
+    ddk[j] = __builtin_amdgcn_readfirstlane((rk[j] - ks * st[j]) - (rk[j - 1] - ks * st[j - 1]));
   }
   auto my_item = [=](int t, int &qt, int &kt) __attribute__((always_inline)) {
-    int q = q_base, k = t + k_base;
+    int q = q_base, k = ks * t + k_base;
 #pragma unroll
     for (int j = 1; j < kRuns; ++j) {
       const bool in = t >= dst[j];
@@ -307,7 +314,11 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     const int page = checked(block_table[(size_t)b * a.max_pages + (key0 >> lp)], 0, a.c.num_pages - 1, kSitePageId, b);
     return ((size_t)page * P + (key0 & (P - 1))) * row_bytes;
   };
-  auto load_half = [&](int kt, size_t tile_off, const char *base, const char *nbase, uint4 *dst)
+  // res: the tile is already resident in its LDS buffers (see `resident`):
+  // the same loads are issued through a descriptor of length 0, so they
+  // move no data (and return zeros) but keep the count of loads in flight
+  // the same on every path.
+  auto load_half = [&](int kt, size_t tile_off, const char *base, const char *nbase, uint4 *dst, bool res)
       __attribute__((always_inline)) {
     const int key0 = kt * kPfKeys;
     if constexpr (BIG_PAGE) {
@@ -323,7 +334,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
         tb = (const char *)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(u >> 32)) << 32) |
                                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u));
       }
-      const uint32_t span = (uint32_t)(min(kPfKeys, ctx - key0) * row_bytes);
+      const uint32_t span = res ? 0u : (uint32_t)(min(kPfKeys, ctx - key0) * row_bytes);
       const __amdgpu_buffer_rsrc_t r = make_rsrc(tb, span);
 #pragma unroll
       for (int i = 0; i < C::kLoads; ++i)
@@ -333,7 +344,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       for (int i = 0; i < C::kLoads; ++i) {
         const int key = key0 + lrow + i * kRowsPerPass;
         dst[i] = make_uint4(0, 0, 0, 0);
-        if (key < ctx) {
+        if (!res && key < ctx) {
           const int page = checked(bt[key >> lp], 0, a.c.num_pages - 1, kSitePageId, b);
           const size_t ro = ((size_t)page * P + (key & (P - 1))) * row_bytes + lch * 16;
           dst[i] = *reinterpret_cast<const uint4 *>(base + ro);
@@ -360,16 +371,22 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // Tile kt (its page offset tile_off) of the pool at `base` into the LDS
   // buffer `dst`: four 16-byte loads per lane, through a descriptor whose
   // range ends at the context's last key (rows past it arrive as zeros).
-  auto issue_direct = [&](int kt, size_t tile_off, const char *base, unsigned char *dst, uint32_t lane_off)
-      __attribute__((always_inline)) {
+  // res: the tile is resident already (see `resident`); the same loads then
+  // go through a descriptor of length 0 (no memory traffic) into this
+  // wave's 1 KiB of scratch LDS beyond the engine's buffers, so the count of
+  // loads in flight is the same on every path.
+  auto issue_direct = [&](int kt, size_t tile_off, const char *base, unsigned char *dst, uint32_t lane_off,
+                          bool res) __attribute__((always_inline)) {
     if constexpr (kDirect) {
       const int key0 = kt * kPfKeys;
-      const uint32_t span = (uint32_t)(min(kPfKeys, ctx - key0) * row_bytes);
+      const uint32_t span = res ? 0u : (uint32_t)(min(kPfKeys, ctx - key0) * row_bytes);
       const __amdgpu_buffer_rsrc_t r = make_rsrc(base + tile_off, span);
+      unsigned char *scratch = ebase + 2 * (kKBufL + kVBufL) + w * 1024;
 #pragma unroll
       for (int i = 0; i < C::kLoads; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PA_LDS void *)(dst + (16 * i + 4 * w) * kKRowL), 16,
-                                                 lane_off + (uint32_t)(16 * i) * (uint32_t)row_bytes, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (PA_LDS void *)(res ? scratch : dst + (16 * i + 4 * w) * kKRowL), 16,
+            lane_off + (uint32_t)(16 * i) * (uint32_t)row_bytes, 0, 0, 0);
     }
   };
   // Direct path, reading side: the byte offset inside a row of this lane's
@@ -397,10 +414,10 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   };
   uint4 pk[C::kLoads], pv[C::kLoads];  // K / V of a tile in flight
   size_t pk_off = 0;  // BIG_PAGE: tile_page_off of the tile in pk / pv
-  auto load_tile = [&](int kt) __attribute__((always_inline)) {
-    pk_off = BIG_PAGE ? tile_page_off(kt) : 0;
-    load_half(kt, pk_off, kbase, knew, pk);
-    load_half(kt, pk_off, vbase, vnew, pv);
+  auto load_tile = [&](int kt, bool res) __attribute__((always_inline)) {
+    if (!res) pk_off = BIG_PAGE ? tile_page_off(kt) : 0;
+    load_half(kt, pk_off, kbase, knew, pk, res);
+    load_half(kt, pk_off, vbase, vnew, pv, res);
   };
   // Fused append, tile kt holding both cached and new keys (only the first
   // new position's tile): once its page loads have landed in pk / pv, the
@@ -422,6 +439,32 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
         }
       }
     }
+  };
+  // Fused append: whether item idx writes new rows into their pages (rows
+  // that are new and belong to the item's query tile, in a workgroup of the
+  // first query head of the KV group).
+  auto writes_new = [&](int idx) __attribute__((always_inline)) {
+    if constexpr (FUSED) {
+      int qt, kt;
+      my_item(idx, qt, kt);
+      const int key0 = kt * kPfKeys;
+      return kv_writer && max(key0, off + qt * kPfRows) < min(min(key0 + kPfKeys, off + qt * kPfRows + kPfRows), ctx);
+    }
+    return false;
+  };
+  // Item t (t >= 2) finds its key tile still in its LDS buffers when item
+  // t - 2, the previous user of buffers t % 2, had the same key tile (same
+  // sequence and KV head: the same data).  Consecutive query tiles of a
+  // window share two key tiles, which the items meet this way (engine 0
+  // walking keys upward, engine 1 downward), so each tile is read from
+  // memory about once per run instead of once per query tile.  Fused: an
+  // item that writes new rows needs its tile in registers and always loads.
+  auto resident = [&](int t) __attribute__((always_inline)) {
+    if (!RUNS || t < 2) return false;  // pair mode: query tiles share no key-tile pairs
+    int qa_, ka_, qb_, kb_;
+    my_item(t, qa_, ka_);
+    my_item(t - 2, qb_, kb_);
+    return ka_ == kb_ && !writes_new(t);
   };
   // Fused append: the tile of item idx is in pk / pv; write the rows that
   // are new and belong to the item's query tile into their page slots.
@@ -690,20 +733,21 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       load_q_async(qt);
       qt_q = qt;
       const size_t off0 = (!RUNS && kt == 0) ? (size_t)pg0 * P * row_bytes : tile_page_off(kt);
-      issue_direct(kt, off0, kbase, kbuf(0), lane_dk);
-      issue_direct(kt, off0, vbase, vbuf(0), lane_dv);
+      issue_direct(kt, off0, kbase, kbuf(0), lane_dk, false);
+      issue_direct(kt, off0, vbase, vbuf(0), lane_dv, false);
       my_item(min(1, n_mine - 1), q1, k1);
-      issue_direct(k1, tile_page_off(k1), kbase, kbuf(1), lane_dk);
+      const bool r1 = RUNS && n_mine < 2;
+      issue_direct(k1, r1 ? 0 : tile_page_off(k1), kbase, kbuf(1), lane_dk, r1);
     }
   } else if (n_mine > 0) {
     int qt, kt;
     my_item(0, qt, kt);
     if (!RUNS && BIG_PAGE && kt == 0) {
       pk_off = (size_t)pg0 * P * row_bytes;
-      load_half(kt, pk_off, kbase, knew, pk);
-      load_half(kt, pk_off, vbase, vnew, pv);
+      load_half(kt, pk_off, kbase, knew, pk, false);
+      load_half(kt, pk_off, vbase, vnew, pv, false);
     } else {
-      load_tile(kt);
+      load_tile(kt, false);
     }
     u32x4 qs[kQLoads];
 #pragma unroll
@@ -732,7 +776,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       if (t < n_mine) {
         int qt, kt;
         my_item(min(t + 1, n_mine - 1), qt, kt);
-        load_tile(kt);
+        load_tile(kt, RUNS && (t + 1 >= n_mine || resident(t + 1)));
       }
     }
     if (t >= 1) pv_mfma((t - 1) & 1);
@@ -766,7 +810,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       // softmax hides the stores' completion: the memory counter drains in
       // order, and the wait for the next tile's loads at the end of the
       // phase includes them.
-      if (t + 1 < n_mine) {
+      if (t + 1 < n_mine && !resident(t + 1)) {
         int qn, kn;
         my_item(t + 1, qn, kn);
         fix_new_rows(kn);
@@ -783,18 +827,21 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     if constexpr (kDirect) {
       // K buffer t % 2 (K(t), read in G(t)) takes K(t + 2); V buffer
       // (t + 1) % 2 (V(t - 1), read in G(t)) takes V(t + 1).  The softmax
-      // wave issues them, off the GEMM wave's path.  Past the engine's last
-      // item the last tile is loaded again into buffers no later phase
-      // reads, so every phase issues the same loads.
+      // wave issues them, off the GEMM wave's path.  A tile already
+      // resident, or an index past the engine's last item, gets the same
+      // loads with no data (see issue_direct), so every phase issues the
+      // same number of loads.
       int q2, k2, q1, k1;
       my_item(min(t + 2, n_mine - 1), q2, k2);
       my_item(min(t + 1, n_mine - 1), q1, k1);
-      issue_direct(k2, tile_page_off(k2), kbase, kbuf(t & 1), lane_dk);
-      issue_direct(k1, tile_page_off(k1), vbase, vbuf((t + 1) & 1), lane_dv);
+      const bool r2 = RUNS && (t + 2 >= n_mine || resident(t + 2));
+      const bool r1 = RUNS && (t + 1 >= n_mine || resident(t + 1));
+      issue_direct(k2, r2 ? 0 : tile_page_off(k2), kbase, kbuf(t & 1), lane_dk, r2);
+      issue_direct(k1, r1 ? 0 : tile_page_off(k1), vbase, vbuf((t + 1) & 1), lane_dv, r1);
     }
     softmax(qt, kt);
     if constexpr (!kDirect) {
-      if (t + 1 < n_mine) {
+      if (t + 1 < n_mine && !resident(t + 1)) {
         store_k((t + 1) & 1, pk);
         store_v((t + 1) & 1, pv);
       }
