@@ -101,9 +101,9 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // kDirect: K/V tiles go from global memory straight into LDS (16-byte
   // buffer loads with the LDS as destination) instead of through registers;
   // their rows are then unpadded (2D bytes) and XOR-swizzled in 16-byte
-  // chunks (see direct_k_chunk / direct_v_chunk).  Tiles of new keys (the
-  // fused append) and pages smaller than a tile keep the register path.
-  constexpr bool kDirect = BIG_PAGE && !FUSED && D == 128;
+  // chunks (see lane_dk / lane_dv).  Pages smaller than a tile, and head
+  // dimension 64, keep the register path.
+  constexpr bool kDirect = BIG_PAGE && D == 128;
   constexpr int kKRowL = kDirect ? 2 * D : C::kKRow;  // LDS row pitch of staged K
   constexpr int kVRowL = kDirect ? 2 * D : C::kVRow;  // and of staged V
   constexpr int kKBufL = kPfKeys * kKRowL;
@@ -297,6 +297,14 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   const char *vnew = FUSED ? (const char *)a.v_new + ((size_t)q0 * a.c.num_kv_heads + hk) * D * 2 : nullptr;
   // Of the query heads sharing KV head hk, the first writes its new rows.
   const bool kv_writer = h % a.group == 0;
+  // A pointer the same for every lane, said so (a buffer descriptor built
+  // from a pointer the compiler takes as per-lane becomes a loop over its
+  // distinct values).
+  auto uniform_ptr = [](const char *p) __attribute__((always_inline)) {
+    const uint64_t u = (uint64_t)(uintptr_t)p;
+    return (const char *)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(u >> 32)) << 32) |
+                                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u));
+  };
 
   // Prefetch of one key tile, K and V separately: thread `tid` moves chunks
   // tid + 256 i, i.e. row tid / kCpr + i * kRowsPerPass, chunk tid % kCpr.
@@ -328,11 +336,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       const char *tb = base + tile_off;
       if constexpr (FUSED) {
         if (key0 >= off) tb = nbase + (size_t)(key0 - off) * row_bytes;
-        // The choice is the same for every lane; say so, or the descriptor
-        // is treated as per-lane (a loop over its distinct values).
-        const uint64_t u = (uint64_t)(uintptr_t)tb;
-        tb = (const char *)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(u >> 32)) << 32) |
-                                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u));
+        tb = uniform_ptr(tb);
       }
       const uint32_t span = res ? 0u : (uint32_t)(min(kPfKeys, ctx - key0) * row_bytes);
       const __amdgpu_buffer_rsrc_t r = make_rsrc(tb, span);
@@ -375,18 +379,73 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // go through a descriptor of length 0 (no memory traffic) into this
   // wave's 1 KiB of scratch LDS beyond the engine's buffers, so the count of
   // loads in flight is the same on every path.
-  auto issue_direct = [&](int kt, size_t tile_off, const char *base, unsigned char *dst, uint32_t lane_off,
-                          bool res) __attribute__((always_inline)) {
+  // Fused: a tile of new keys comes from the new rows at nbase; the one tile
+  // that holds both cached and new keys (when the first new position is not
+  // a multiple of 64) takes each row from where it is, every lane loading
+  // through one of two descriptors, so each LDS slot is written once.
+  auto issue_direct = [&](int kt, size_t tile_off, const char *base, const char *nbase, unsigned char *dst,
+                          uint32_t lane_off, bool res) __attribute__((always_inline)) {
     if constexpr (kDirect) {
       const int key0 = kt * kPfKeys;
       const uint32_t span = res ? 0u : (uint32_t)(min(kPfKeys, ctx - key0) * row_bytes);
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(base + tile_off, span);
+      const char *tb = base + tile_off;
+      bool mixed = false;
+      if constexpr (FUSED) {
+        if (key0 >= off) tb = uniform_ptr(nbase + (size_t)(key0 - off) * row_bytes);
+        mixed = !res && key0 < off && key0 + kPfKeys > off;
+      }
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(tb, span);
       unsigned char *scratch = ebase + 2 * (kKBufL + kVBufL) + w * 1024;
+      if (FUSED && mixed) {
+        // New rows from nbase (row index key - off), the rest from the page.
+        const __amdgpu_buffer_rsrc_t rn = make_rsrc(uniform_ptr(nbase), (uint32_t)(min(kPfKeys, ctx - off) * row_bytes));
 #pragma unroll
-      for (int i = 0; i < C::kLoads; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (PA_LDS void *)(res ? scratch : dst + (16 * i + 4 * w) * kKRowL), 16,
-            lane_off + (uint32_t)(16 * i) * (uint32_t)row_bytes, 0, 0, 0);
+        for (int i = 0; i < C::kLoads; ++i) {
+          PA_LDS void *d = (PA_LDS void *)(dst + (16 * i + 4 * w) * kKRowL);
+          // (The distinct asm markers keep the two loads apart: merged into
+          // one, its descriptor would be chosen per lane.)
+          if (key0 + 16 * i + drow < off) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, lane_off + (uint32_t)(16 * i) * (uint32_t)row_bytes, 0,
+                                                     0, 0);
+            __asm__ volatile("; cached rows" ::: "memory");
+          } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rn, d, 16, lane_off + (uint32_t)((key0 - off + 16 * i) * (int)row_bytes), 0, 0, 0);
+            __asm__ volatile("; new rows" ::: "memory");
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::kLoads; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              r, (PA_LDS void *)(res ? scratch : dst + (16 * i + 4 * w) * kKRowL), 16,
+              lane_off + (uint32_t)(16 * i) * (uint32_t)row_bytes, 0, 0, 0);
+      }
+    }
+  };
+  // Fused append, direct path: item idx's tile is in the LDS buffer `src`
+  // (K or V), each wave's rows put there by its own loads.  The rows that are
+  // new and belong to the item's query tile go to their page slots: every
+  // lane stores the 16 bytes it loaded at the page offset it would have read
+  // them from.  The caller runs this before the wave's next loads into `src`.
+  auto write_back = [&](int idx, const unsigned char *src, char *pool, uint32_t lane_off)
+      __attribute__((always_inline)) {
+    if constexpr (FUSED && kDirect) {
+      int qt, kt;
+      my_item(idx, qt, kt);
+      const int key0 = kt * kPfKeys;
+      const int w_lo = max(key0, off + qt * kPfRows);
+      const int w_hi = min(min(key0 + kPfKeys, off + qt * kPfRows + kPfRows), ctx);
+      if (kv_writer && w_lo < w_hi) {
+        char *dp = pool + (size_t)hk * D * 2 + tile_page_off(kt) + lane_off;
+#pragma unroll
+        for (int i = 0; i < C::kLoads; ++i) {
+          const int key = key0 + 16 * i + drow;
+          if (key >= w_lo && key < w_hi)
+            *reinterpret_cast<uint4 *>(dp + (size_t)(16 * i) * row_bytes) =
+                *reinterpret_cast<const uint4 *>(src + (16 * i + 4 * w) * kKRowL + lane * 16);
+        }
+      }
     }
   };
   // Direct path, reading side: the byte offset inside a row of this lane's
@@ -457,14 +516,15 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // sequence and KV head: the same data).  Consecutive query tiles of a
   // window share two key tiles, which the items meet this way (engine 0
   // walking keys upward, engine 1 downward), so each tile is read from
-  // memory about once per run instead of once per query tile.  Fused: an
-  // item that writes new rows needs its tile in registers and always loads.
+  // memory about once per run instead of once per query tile.  Fused, on the
+  // register path: an item that writes new rows needs its tile in registers
+  // and always loads (the direct path writes them from LDS).
   auto resident = [&](int t) __attribute__((always_inline)) {
     if (!RUNS || t < 2) return false;  // pair mode: query tiles share no key-tile pairs
     int qa_, ka_, qb_, kb_;
     my_item(t, qa_, ka_);
     my_item(t - 2, qb_, kb_);
-    return ka_ == kb_ && !writes_new(t);
+    return ka_ == kb_ && (kDirect || !writes_new(t));
   };
   // Fused append: the tile of item idx is in pk / pv; write the rows that
   // are new and belong to the item's query tile into their page slots.
@@ -733,11 +793,11 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       load_q_async(qt);
       qt_q = qt;
       const size_t off0 = (!RUNS && kt == 0) ? (size_t)pg0 * P * row_bytes : tile_page_off(kt);
-      issue_direct(kt, off0, kbase, kbuf(0), lane_dk, false);
-      issue_direct(kt, off0, vbase, vbuf(0), lane_dv, false);
+      issue_direct(kt, off0, kbase, knew, kbuf(0), lane_dk, false);
+      issue_direct(kt, off0, vbase, vnew, vbuf(0), lane_dv, false);
       my_item(min(1, n_mine - 1), q1, k1);
       const bool r1 = RUNS && n_mine < 2;
-      issue_direct(k1, r1 ? 0 : tile_page_off(k1), kbase, kbuf(1), lane_dk, r1);
+      issue_direct(k1, r1 ? 0 : tile_page_off(k1), kbase, knew, kbuf(1), lane_dk, r1);
     }
   } else if (n_mine > 0) {
     int qt, kt;
@@ -805,7 +865,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   };
   auto softmax_phase = [&](int t) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(0);
-    if constexpr (FUSED) {
+    if constexpr (FUSED && !kDirect) {
       // The next tile's new rows go to their pages first, so that the whole
       // softmax hides the stores' completion: the memory counter drains in
       // order, and the wait for the next tile's loads at the end of the
@@ -831,13 +891,22 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       // resident, or an index past the engine's last item, gets the same
       // loads with no data (see issue_direct), so every phase issues the
       // same number of loads.
+      // Fused: first the new rows of K(t) and V(t - 1), the buffers' present
+      // tiles, go from LDS to their pages (V(t - 1) landed before this
+      // step's barrier; K(t) too).  The stores are issued before the loads,
+      // so the wait for all but the last 8 memory operations at the end of
+      // the phase still covers exactly the older loads.
+      if constexpr (FUSED) {
+        if (writes_new(t)) write_back(t, kbuf(t & 1), (char *)a.c.k, lane_dk);
+        if (t >= 1 && writes_new(t - 1)) write_back(t - 1, vbuf((t + 1) & 1), (char *)a.c.v, lane_dv);
+      }
       int q2, k2, q1, k1;
       my_item(min(t + 2, n_mine - 1), q2, k2);
       my_item(min(t + 1, n_mine - 1), q1, k1);
       const bool r2 = RUNS && (t + 2 >= n_mine || resident(t + 2));
       const bool r1 = RUNS && (t + 1 >= n_mine || resident(t + 1));
-      issue_direct(k2, r2 ? 0 : tile_page_off(k2), kbase, kbuf(t & 1), lane_dk, r2);
-      issue_direct(k1, r1 ? 0 : tile_page_off(k1), vbase, vbuf((t + 1) & 1), lane_dv, r1);
+      issue_direct(k2, r2 ? 0 : tile_page_off(k2), kbase, knew, kbuf(t & 1), lane_dk, r2);
+      issue_direct(k1, r1 ? 0 : tile_page_off(k1), vbase, vnew, vbuf((t + 1) & 1), lane_dv, r1);
     }
     softmax(qt, kt);
     if constexpr (!kDirect) {
@@ -846,6 +915,14 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
         store_v((t + 1) & 1, pv);
       }
     }
+  };
+  // Fused, direct path: the last item's V rows, still in their buffer
+  // (landed before the last GEMM phase, which read them), before the merge
+  // reuses the buffers.
+  auto last_write_back = [&]() __attribute__((always_inline)) {
+    if constexpr (FUSED && kDirect)
+      if (n_mine > 0 && writes_new(n_mine - 1))
+        write_back(n_mine - 1, vbuf((n_mine - 1) & 1), (char *)a.c.v, lane_dv);
   };
   // Engine 0 passes 2 * half + 1 barriers in its loop, engine 1 one leading
   // barrier and 2 * n1 + 1 in its loop; the engine with fewer pads one at
@@ -859,6 +936,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       bar_after_loads();
     }
     gemm_phase(n_mine);
+    last_write_back();
     if constexpr (kDirect) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes the LDS
     __syncthreads();
     if (half == n1) __syncthreads();
@@ -871,6 +949,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       bar_after_loads();
     }
     gemm_phase(n_mine);
+    last_write_back();
     if constexpr (kDirect) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes the LDS
     __syncthreads();
     if (half > n1) __syncthreads();
