@@ -69,7 +69,9 @@ def build(debug: bool = False, verbose: bool = True) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         list(ex.map(lambda so: _compile(so[0], so[1], "-O3", extra), zip(srcs, objs)))
     tmp = out + ".tmp"
-    cmd = [HIPCC, *DEVICE_FLAGS, "-shared", "-fPIC", *objs, "-o", tmp]
+    # -z defs: an unresolved symbol fails the link here, not the first load
+    # (a kernel whose host-side launch stub the compiler dropped shows up so).
+    cmd = [HIPCC, *DEVICE_FLAGS, "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // kDirect: K/V tiles go from global memory straight into LDS (16-byte
   // buffer loads with the LDS as destination) instead of through registers;
   // their rows are then unpadded (2D bytes) and XOR-swizzled in 16-byte
-  // chunks (see lane_dk / lane_dv).  Pages smaller than a tile, and head
+  // chunks (see lane_dt).  Pages smaller than a tile, and head
   // dimension 64, keep the register path.
   constexpr bool kDirect = BIG_PAGE && D == 128;
   constexpr int kKRowL = kDirect ? 2 * D : C::kKRow;  // LDS row pitch of staged K
@@ -316,11 +316,15 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   const int lrow = tid / C::kCpr;
   const int lch = tid % C::kCpr;
   const uint32_t lane_goff = (uint32_t)lrow * (uint32_t)row_bytes + lch * 16;
-  // Byte offset of key tile kt inside the K (or V) pool (BIG_PAGE: one page).
-  auto tile_page_off = [&](int kt) __attribute__((always_inline)) {
+  // Byte offset of key tile kt inside the K (or V) pool (BIG_PAGE: one
+  // page), from the block-table entry of its page.
+  auto page_off = [&](int entry, int kt) __attribute__((always_inline)) {
     const int key0 = kt * kPfKeys;
-    const int page = checked(block_table[(size_t)b * a.max_pages + (key0 >> lp)], 0, a.c.num_pages - 1, kSitePageId, b);
+    const int page = checked(entry, 0, a.c.num_pages - 1, kSitePageId, b);
     return ((size_t)page * P + (key0 & (P - 1))) * row_bytes;
+  };
+  auto tile_page_off = [&](int kt) __attribute__((always_inline)) {
+    return page_off(block_table[(size_t)b * a.max_pages + ((kt * kPfKeys) >> lp)], kt);
   };
   // res: the tile is already resident in its LDS buffers (see `resident`):
   // the same loads are issued through a descriptor of length 0, so they
@@ -360,18 +364,32 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   const uint32_t lane_voff = (uint32_t)lrow * C::kVRow + lch * 16;
   auto kbuf = [&](int buf) __attribute__((always_inline)) { return ebase + buf * (kKBufL + kVBufL); };
   auto vbuf = [&](int buf) __attribute__((always_inline)) { return ebase + buf * (kKBufL + kVBufL) + kKBufL; };
-  // Direct path: wave w's load i of a tile fills rows 16 i + 4 w .. +3 (1 KiB,
-  // lane l: row 16 i + 4 w + l / 16, physical chunk l % 16).  The lane loads
-  // the logical chunk that the swizzle puts there, from its row in the page.
-  // K: chunk c of row r sits at chunk c ^ (r % 16), so the 16 rows an MFMA
-  // operand read touches at one logical chunk fall in 16 different bank
-  // groups.  V: chunk c of row r sits at c ^ 2 (r % 4), so the four rows a
-  // transposed read takes two adjacent chunks from fall in four different
-  // 32-byte bank groups.  Both are the same for every i, so each lane's
-  // source offset inside a tile is fixed.
-  const int drow = 4 * w + (lane >> 4);
-  const uint32_t lane_dk = (uint32_t)drow * (uint32_t)row_bytes + (uint32_t)(((lane & 15) ^ (drow & 15)) * 16);
-  const uint32_t lane_dv = (uint32_t)drow * (uint32_t)row_bytes + (uint32_t)(((lane & 15) ^ ((drow & 3) << 1)) * 16);
+  // Direct path: wave w's loads of a tile fill its 16 rows 16 w .. 16 w + 15
+  // (4 KiB), load i the rows 16 w + 4 i .. +3 (lane l: row 16 w + 4 i + l /
+  // 16, physical chunk l % 16).  The four loads share one LDS base (so one
+  // M0 value) and differ in the instruction offset 1024 i, which the
+  // hardware adds to the LDS address and to the memory offset alike (also
+  // in the range check); each lane's memory offset is passed less that.
+  // The lane loads the logical chunk that the swizzle puts there, from its
+  // row in the page.  K: chunk c of row r sits at chunk c ^ (r % 16), so
+  // the 16 rows an MFMA operand read touches at one logical chunk fall in 16
+  // different bank groups.  V: chunk c of row r sits at c ^ 2 (r % 4), so
+  // the four rows a transposed read takes two adjacent chunks from fall in
+  // four different 32-byte bank groups.  lane_dt(v, i): the lane's offset
+  // inside a tile for load i, of K (v false: four registers, as its chunk
+  // depends on i) or V (one register plus a uniform step).
+  const int drow = 16 * w + (lane >> 4);  // the lane's row in load 0; load i: drow + 4 i
+  // (Four named values, not an array: a local array used inside these
+  // lambdas keeps the host compilation pass from emitting the kernel.)
+  auto dk_of = [&](int i) __attribute__((always_inline)) {
+    const int r = drow + 4 * i;
+    return (uint32_t)r * (uint32_t)row_bytes + (uint32_t)(((lane & 15) ^ (r & 15)) * 16);
+  };
+  const uint32_t dk0 = dk_of(0), dk1 = dk_of(1), dk2 = dk_of(2), dk3 = dk_of(3);
+  const uint32_t dv0 = (uint32_t)drow * (uint32_t)row_bytes + (uint32_t)(((lane & 15) ^ ((drow & 3) << 1)) * 16);
+  auto lane_dt = [&](bool v, int i) __attribute__((always_inline)) {
+    return v ? dv0 + (uint32_t)(4 * i) * (uint32_t)row_bytes : i == 0 ? dk0 : i == 1 ? dk1 : i == 2 ? dk2 : dk3;
+  };
   // Tile kt (its page offset tile_off) of the pool at `base` into the LDS
   // buffer `dst`: four 16-byte loads per lane, through a descriptor whose
   // range ends at the context's last key (rows past it arrive as zeros).
@@ -383,9 +401,10 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // that holds both cached and new keys (when the first new position is not
   // a multiple of 64) takes each row from where it is, every lane loading
   // through one of two descriptors, so each LDS slot is written once.
-  auto issue_direct = [&](int kt, size_t tile_off, const char *base, const char *nbase, unsigned char *dst,
-                          uint32_t lane_off, bool res) __attribute__((always_inline)) {
+  auto issue_direct = [&](int kt, size_t tile_off, const char *base, const char *nbase, unsigned char *dst, bool is_v,
+                          bool res) __attribute__((always_inline)) {
     if constexpr (kDirect) {
+      static_assert(!kDirect || C::kLoads == 4, "the direct path issues four loads per lane and tile");
       const int key0 = kt * kPfKeys;
       const uint32_t span = res ? 0u : (uint32_t)(min(kPfKeys, ctx - key0) * row_bytes);
       const char *tb = base + tile_off;
@@ -395,31 +414,51 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
         mixed = !res && key0 < off && key0 + kPfKeys > off;
       }
       const __amdgpu_buffer_rsrc_t r = make_rsrc(tb, span);
-      unsigned char *scratch = ebase + 2 * (kKBufL + kVBufL) + w * 1024;
-      if (FUSED && mixed) {
-        // New rows from nbase (row index key - off), the rest from the page.
-        const __amdgpu_buffer_rsrc_t rn = make_rsrc(uniform_ptr(nbase), (uint32_t)(min(kPfKeys, ctx - off) * row_bytes));
+      unsigned char *dw = dst + 16 * w * kKRowL;  // this wave's 4 KiB of the buffer
+      if (res) {
+        // Into this wave's 1 KiB of scratch LDS, all four at offset 0.
+        unsigned char *scratch = ebase + 2 * (kKBufL + kVBufL) + w * 1024;
 #pragma unroll
         for (int i = 0; i < C::kLoads; ++i) {
-          PA_LDS void *d = (PA_LDS void *)(dst + (16 * i + 4 * w) * kKRowL);
-          // (The distinct asm markers keep the two loads apart: merged into
-          // one, its descriptor would be chosen per lane.)
-          if (key0 + 16 * i + drow < off) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, lane_off + (uint32_t)(16 * i) * (uint32_t)row_bytes, 0,
-                                                     0, 0);
-            __asm__ volatile("; cached rows" ::: "memory");
-          } else {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rn, d, 16, lane_off + (uint32_t)((key0 - off + 16 * i) * (int)row_bytes), 0, 0, 0);
-            __asm__ volatile("; new rows" ::: "memory");
-          }
+          // (Offsets go through a local: a lambda call as the builtin's
+          // argument keeps the host pass from emitting the kernel.)
+          const uint32_t vo = lane_dt(is_v, i);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PA_LDS void *)scratch, 16, vo, 0, 0, 0);
         }
+      } else if (FUSED && mixed) {
+        // New rows from nbase (row index key - off), the rest from the page.
+        const __amdgpu_buffer_rsrc_t rn = make_rsrc(uniform_ptr(nbase), (uint32_t)(min(kPfKeys, ctx - off) * row_bytes));
+        const uint32_t new_off = (uint32_t)((key0 - off) * (int)row_bytes);
+        // (The distinct asm markers keep the two loads apart: merged into
+        // one, its descriptor would be chosen per lane.)
+#define PA_LD_MIXED(I)                                                                      \
+  {                                                                                         \
+    const uint32_t vo = lane_dt(is_v, I) - 1024 * (I);                                      \
+    if (key0 + drow + 4 * (I) < off) {                                                      \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PA_LDS void *)dw, 16, vo, 0, 1024 * (I), 0); \
+      __asm__ volatile("; cached rows" ::: "memory");                                       \
+    } else {                                                                                \
+      const uint32_t vn = vo + new_off;                                                     \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rn, (PA_LDS void *)dw, 16, vn, 0, 1024 * (I), 0); \
+      __asm__ volatile("; new rows" ::: "memory");                                          \
+    }                                                                                       \
+  }
+        PA_LD_MIXED(0)
+        PA_LD_MIXED(1)
+        PA_LD_MIXED(2)
+        PA_LD_MIXED(3)
+#undef PA_LD_MIXED
       } else {
-#pragma unroll
-        for (int i = 0; i < C::kLoads; ++i)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              r, (PA_LDS void *)(res ? scratch : dst + (16 * i + 4 * w) * kKRowL), 16,
-              lane_off + (uint32_t)(16 * i) * (uint32_t)row_bytes, 0, 0, 0);
+#define PA_LD(I)                                                                            \
+  {                                                                                         \
+    const uint32_t vo = lane_dt(is_v, I) - 1024 * (I);                                      \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PA_LDS void *)dw, 16, vo, 0, 1024 * (I), 0); \
+  }
+        PA_LD(0)
+        PA_LD(1)
+        PA_LD(2)
+        PA_LD(3)
+#undef PA_LD
       }
     }
   };
@@ -428,22 +467,20 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // new and belong to the item's query tile go to their page slots: every
   // lane stores the 16 bytes it loaded at the page offset it would have read
   // them from.  The caller runs this before the wave's next loads into `src`.
-  auto write_back = [&](int idx, const unsigned char *src, char *pool, uint32_t lane_off)
+  auto write_back = [&](int qt, int kt, const unsigned char *src, char *pool, bool is_v)
       __attribute__((always_inline)) {
     if constexpr (FUSED && kDirect) {
-      int qt, kt;
-      my_item(idx, qt, kt);
       const int key0 = kt * kPfKeys;
       const int w_lo = max(key0, off + qt * kPfRows);
       const int w_hi = min(min(key0 + kPfKeys, off + qt * kPfRows + kPfRows), ctx);
       if (kv_writer && w_lo < w_hi) {
-        char *dp = pool + (size_t)hk * D * 2 + tile_page_off(kt) + lane_off;
+        char *dp = pool + (size_t)hk * D * 2 + tile_page_off(kt);
 #pragma unroll
         for (int i = 0; i < C::kLoads; ++i) {
-          const int key = key0 + 16 * i + drow;
+          const int key = key0 + drow + 4 * i;
           if (key >= w_lo && key < w_hi)
-            *reinterpret_cast<uint4 *>(dp + (size_t)(16 * i) * row_bytes) =
-                *reinterpret_cast<const uint4 *>(src + (16 * i + 4 * w) * kKRowL + lane * 16);
+            *reinterpret_cast<uint4 *>(dp + lane_dt(is_v, i)) =
+                *reinterpret_cast<const uint4 *>(src + (16 * w + 4 * i) * kKRowL + lane * 16);
         }
       }
     }
@@ -499,17 +536,20 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       }
     }
   };
-  // Fused append: whether item idx writes new rows into their pages (rows
-  // that are new and belong to the item's query tile, in a workgroup of the
-  // first query head of the KV group).
-  auto writes_new = [&](int idx) __attribute__((always_inline)) {
+  // Fused append: whether item (qt, kt) writes new rows into their pages
+  // (rows that are new and belong to the item's query tile, in a workgroup
+  // of the first query head of the KV group).
+  auto writes_new_qk = [&](int qt, int kt) __attribute__((always_inline)) {
     if constexpr (FUSED) {
-      int qt, kt;
-      my_item(idx, qt, kt);
       const int key0 = kt * kPfKeys;
       return kv_writer && max(key0, off + qt * kPfRows) < min(min(key0 + kPfKeys, off + qt * kPfRows + kPfRows), ctx);
     }
     return false;
+  };
+  auto writes_new = [&](int idx) __attribute__((always_inline)) {
+    int qt, kt;
+    my_item(idx, qt, kt);
+    return writes_new_qk(qt, kt);
   };
   // Item t (t >= 2) finds its key tile still in its LDS buffers when item
   // t - 2, the previous user of buffers t % 2, had the same key tile (same
@@ -679,21 +719,35 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     // Mask (only tiles that cross a boundary; this lane's row sees keys
     // [klo, khi]) on the raw scores; the scale (> 0) is applied inside the
     // exponent, after the max.
-    const bool edge = (causal && key0 + kPfKeys - 1 > p_first) || (W >= 0 && key0 < p_last - W) ||
-                      (key0 + kPfKeys > ctx);
-    if (edge) {
+    // A tile needs the upper bound where the causal diagonal or the end of
+    // the context crosses it, the lower bound where the window's start does;
+    // most edge tiles need only one of them.
+    const bool need_hi = (causal && key0 + kPfKeys - 1 > p_first) || (key0 + kPfKeys > ctx);
+    const bool need_lo = W >= 0 && key0 < p_last - W;
+    if (need_hi || need_lo) {
       // Bounds relative to this lane's first key, so that each element's
       // offset in the tile is a constant: visible iff lo <= offset <= hi.
       const int base = key0 + g * 4;
       const int hi = (causal ? min(pos, ctx - 1) : ctx - 1) - base;
       const int lo = (W >= 0 ? pos - W : 0) - base;
+      auto mask = [&](auto LO, auto HI) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int c = kb * 32 + (i >> 2) * 8 + (i & 3);
-          sacc[kb][i] = ((c >= lo) & (c <= hi)) ? sacc[kb][i] : -INFINITY;
-        }
+          for (int i = 0; i < 16; ++i) {
+            const int c = kb * 32 + (i >> 2) * 8 + (i & 3);
+            const bool vis = (!decltype(LO)::value || c >= lo) && (!decltype(HI)::value || c <= hi);
+            sacc[kb][i] = vis ? sacc[kb][i] : -INFINITY;
+          }
+      };
+      // (Pair mode, where edge tiles are rare, and the fused kernel: one
+      // form, fewer registers.)
+      if (!RUNS || FUSED || (need_hi && need_lo))
+        mask(std::true_type{}, std::true_type{});
+      else if (need_hi)
+        mask(std::false_type{}, std::true_type{});
+      else
+        mask(std::true_type{}, std::false_type{});
     }
     float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
@@ -783,21 +837,58 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       __syncthreads();
     }
   };
+  // Direct path: the items t - 1 .. t + 2 of this engine as (query tile,
+  // key tile) pairs, kept from step to step (pair mode: clamped to the last
+  // item, whose tile the loads past the end read again; run mode: past the
+  // end they are never used).  Each step computes one new item: pair mode
+  // from the two runs directly, run mode by walking (the next key tile of
+  // the query tile, or the first of the next query tile in the engine's
+  // direction), which costs a few scalar instructions where the run table
+  // would cost dozens.  pg2: the block-table entry of item t + 2's page,
+  // read a step before it is needed.  (ck, coff, cres): the K tile loaded
+  // last, which is the next V tile.
+  int wq_m1 = 0, wk_m1 = 0, wq0 = 0, wk0 = 0, wq1 = 0, wk1 = 0, wq2 = 0, wk2 = 0;
+  int wlo = 0, whi = 0;  // run mode: the key-tile range of query tile wq2
+  int pg2 = 0;
+  int ck = 0;
+  size_t coff = 0;
+  bool cres = false;
+  auto page_entry = [&](int kt, bool valid) __attribute__((always_inline)) {
+    return block_table[(size_t)b * a.max_pages + (valid ? (kt * kPfKeys) >> lp : 0)];
+  };
+  auto advance = [&](int t) __attribute__((always_inline)) {  // window of step t -> step t + 1
+    wq_m1 = wq0, wk_m1 = wk0, wq0 = wq1, wk0 = wk1, wq1 = wq2, wk1 = wk2;
+    if constexpr (RUNS) {
+      wk2 += ks;
+      if (ks > 0 ? wk2 >= whi : wk2 < wlo) {
+        wq2 += ks;
+        tile_range(wq2, wlo, whi);
+        wk2 = ks > 0 ? wlo : whi - 1;
+      }
+    } else {
+      my_item(min(t + 3, n_mine - 1), wq2, wk2);
+    }
+    pg2 = page_entry(wk2, t + 3 < n_mine || !RUNS);
+  };
   if constexpr (kDirect) {
     // Q^T of the first query tile straight into registers, then K(0), V(0)
     // and K(1) into LDS buffers 0, 0 and 1 (K(t + 2) and V(t + 1) follow in
     // softmax phase t, once the buffers' previous tiles have been read).
     if (n_mine > 0) {
-      int qt, kt, q1, k1;
-      my_item(0, qt, kt);
-      load_q_async(qt);
-      qt_q = qt;
-      const size_t off0 = (!RUNS && kt == 0) ? (size_t)pg0 * P * row_bytes : tile_page_off(kt);
-      issue_direct(kt, off0, kbase, knew, kbuf(0), lane_dk, false);
-      issue_direct(kt, off0, vbase, vnew, vbuf(0), lane_dv, false);
-      my_item(min(1, n_mine - 1), q1, k1);
+      my_item(0, wq0, wk0);
+      my_item(min(1, n_mine - 1), wq1, wk1);
+      my_item(min(2, n_mine - 1), wq2, wk2);
+      if constexpr (RUNS) tile_range(wq2, wlo, whi);
+      pg2 = page_entry(wk2, 2 < n_mine || !RUNS);
+      load_q_async(wq0);
+      qt_q = wq0;
+      const size_t off0 = (!RUNS && wk0 == 0) ? (size_t)pg0 * P * row_bytes : tile_page_off(wk0);
+      issue_direct(wk0, off0, kbase, knew, kbuf(0), false, false);
+      issue_direct(wk0, off0, vbase, vnew, vbuf(0), true, false);
       const bool r1 = RUNS && n_mine < 2;
-      issue_direct(k1, r1 ? 0 : tile_page_off(k1), kbase, knew, kbuf(1), lane_dk, r1);
+      const size_t off1 = r1 ? 0 : tile_page_off(wk1);
+      issue_direct(wk1, off1, kbase, knew, kbuf(1), false, r1);
+      ck = wk1, coff = off1, cres = r1;
     }
   } else if (n_mine > 0) {
     int qt, kt;
@@ -854,8 +945,8 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       // as this tile's QK product is issued: it arrives during the softmax
       // phase, whose K/V stores wait for all loads anyway.
       if (t + 1 < n_mine) {
-        int qn, kn;
-        my_item(t + 1, qn, kn);
+        int qn = wq1, kn;
+        if constexpr (!kDirect) my_item(t + 1, qn, kn);
         if (qn != qt_q) {
           load_q_async(qn);
           qt_q = qn;
@@ -877,8 +968,8 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
         write_new(t + 1);
       }
     }
-    int qt, kt;
-    my_item(t, qt, kt);
+    int qt = wq0, kt = wk0;
+    if constexpr (!kDirect) my_item(t, qt, kt);
     if (qt != qt_o) {
       if (qt_o >= 0) finish(qt_o, m, lsum, o);
       reset_o();
@@ -897,16 +988,17 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       // so the wait for all but the last 8 memory operations at the end of
       // the phase still covers exactly the older loads.
       if constexpr (FUSED) {
-        if (writes_new(t)) write_back(t, kbuf(t & 1), (char *)a.c.k, lane_dk);
-        if (t >= 1 && writes_new(t - 1)) write_back(t - 1, vbuf((t + 1) & 1), (char *)a.c.v, lane_dv);
+        if (writes_new_qk(wq0, wk0)) write_back(wq0, wk0, kbuf(t & 1), (char *)a.c.k, false);
+        if (t >= 1 && writes_new_qk(wq_m1, wk_m1)) write_back(wq_m1, wk_m1, vbuf((t + 1) & 1), (char *)a.c.v, true);
       }
-      int q2, k2, q1, k1;
-      my_item(min(t + 2, n_mine - 1), q2, k2);
-      my_item(min(t + 1, n_mine - 1), q1, k1);
-      const bool r2 = RUNS && (t + 2 >= n_mine || resident(t + 2));
-      const bool r1 = RUNS && (t + 1 >= n_mine || resident(t + 1));
-      issue_direct(k2, r2 ? 0 : tile_page_off(k2), kbase, knew, kbuf(t & 1), lane_dk, r2);
-      issue_direct(k1, r1 ? 0 : tile_page_off(k1), vbase, vnew, vbuf((t + 1) & 1), lane_dv, r1);
+      // K(t + 2): resident when item t had the same key tile (run mode).
+      // V(t + 1): the K tile of the previous step.
+      const bool r2 = RUNS && (t + 2 >= n_mine || wk2 == wk0);
+      const size_t off2 = r2 ? 0 : page_off(pg2, wk2);
+      issue_direct(wk2, off2, kbase, knew, kbuf(t & 1), false, r2);
+      issue_direct(ck, coff, vbase, vnew, vbuf((t + 1) & 1), true, cres);
+      ck = wk2, coff = off2, cres = r2;
+      advance(t);
     }
     softmax(qt, kt);
     if constexpr (!kDirect) {
@@ -920,9 +1012,9 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // (landed before the last GEMM phase, which read them), before the merge
   // reuses the buffers.
   auto last_write_back = [&]() __attribute__((always_inline)) {
-    if constexpr (FUSED && kDirect)
-      if (n_mine > 0 && writes_new(n_mine - 1))
-        write_back(n_mine - 1, vbuf((n_mine - 1) & 1), (char *)a.c.v, lane_dv);
+    if constexpr (FUSED && kDirect)  // the window has moved on: item n_mine - 1 is its first
+      if (n_mine > 0 && writes_new_qk(wq_m1, wk_m1))
+        write_back(wq_m1, wk_m1, vbuf((n_mine - 1) & 1), (char *)a.c.v, true);
   };
   // Engine 0 passes 2 * half + 1 barriers in its loop, engine 1 one leading
   // barrier and 2 * n1 + 1 in its loop; the engine with fewer pads one at
