@@ -719,35 +719,36 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     // Mask (only tiles that cross a boundary; this lane's row sees keys
     // [klo, khi]) on the raw scores; the scale (> 0) is applied inside the
     // exponent, after the max.
-    // A tile needs the upper bound where the causal diagonal or the end of
-    // the context crosses it, the lower bound where the window's start does;
-    // most edge tiles need only one of them.
-    const bool need_hi = (causal && key0 + kPfKeys - 1 > p_first) || (key0 + kPfKeys > ctx);
-    const bool need_lo = W >= 0 && key0 < p_last - W;
-    if (need_hi || need_lo) {
+    const bool edge = (causal && key0 + kPfKeys - 1 > p_first) || (W >= 0 && key0 < p_last - W) ||
+                      (key0 + kPfKeys > ctx);
+    if (edge) {
       // Bounds relative to this lane's first key, so that each element's
       // offset in the tile is a constant: visible iff lo <= offset <= hi.
+      // The lane's visible offsets as a bit mask, one 32-bit word per 32-key
+      // block (vm[kb] bit j: offset 32 kb + j); each element then takes one
+      // sign-extending bit extract and one bit select (score or -inf).
       const int base = key0 + g * 4;
       const int hi = (causal ? min(pos, ctx - 1) : ctx - 1) - base;
       const int lo = (W >= 0 ? pos - W : 0) - base;
-      auto mask = [&](auto LO, auto HI) __attribute__((always_inline)) {
+      uint32_t vm[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        const int h = hi - 32 * kb, l = lo - 32 * kb;
+        const uint32_t le = h >= 31 ? 0xffffffffu : h < 0 ? 0u : (2u << h) - 1u;
+        const uint32_t ge = l <= 0 ? 0xffffffffu : l >= 32 ? 0u : ~((1u << l) - 1u);
+        vm[kb] = le & ge;
+      }
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int c = kb * 32 + (i >> 2) * 8 + (i & 3);
-            const bool vis = (!decltype(LO)::value || c >= lo) && (!decltype(HI)::value || c <= hi);
-            sacc[kb][i] = vis ? sacc[kb][i] : -INFINITY;
-          }
-      };
-      // (Pair mode, where edge tiles are rare, and the fused kernel: one
-      // form, fewer registers.)
-      if (!RUNS || FUSED || (need_hi && need_lo))
-        mask(std::true_type{}, std::true_type{});
-      else if (need_hi)
-        mask(std::false_type{}, std::true_type{});
-      else
-        mask(std::true_type{}, std::false_type{});
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c = (i >> 2) * 8 + (i & 3);  // offset inside the 32-key block
+          const uint32_t keep = (uint32_t)((int32_t)(vm[kb] << (31 - c)) >> 31);
+          // (Through a scalar: a bit cast of a vector element read element 0
+          // with this compiler.)
+          const float v = sacc[kb][i];
+          sacc[kb][i] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, v) & keep) | (0xff800000u & ~keep));
+        }
     }
     float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
@@ -762,9 +763,13 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       // m = -inf and factor 1.
       const float m_new = fmaxf(m, mx);
       const float corr = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
-      lsum *= corr;
+      // Rows without a reference yet hold o = 0 and lsum = 0: the first
+      // visible tile of a query tile rescales nothing.
+      if (__any(m != -INFINITY)) {
+        lsum *= corr;
 #pragma unroll
-      for (int db = 0; db < C::kNdb; ++db) o[db] *= corr;
+        for (int db = 0; db < C::kNdb; ++db) o[db] *= corr;
+      }
       m = m_new;
     }
     const float neg_m = m == -INFINITY ? 0.f : -m;
