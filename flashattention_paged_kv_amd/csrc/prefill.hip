@@ -1110,6 +1110,128 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     merge(std::integral_constant<int, 1>{});
 }
 
+// fp32 caches (the 1e-4 configuration): the same attention with fp32
+// operands on v_mfma_f32_32x32x2_f32, one wave per 32 query rows of one
+// head, K and V read from the pages straight into the operand registers (no
+// LDS), the online softmax of the bf16 kernel in fp32 throughout (P is not
+// rounded).  Operand layout of the 32x32x2 product: lane l gives A[l % 32][l
+// / 32] and B[l / 32][l % 32]; accumulator element e of lane l is row 8 (e /
+// 4) + 4 (l / 32) + e % 4, column l % 32.  So, with g = l / 32:
+//   S^T = K . Q^T over D/2 steps, step s pairing dims s (g = 0) and D/2 + s
+//   (g = 1): lane (g, c) gives K[key0 + c][g D/2 + s] and Q[row c][g D/2 + s];
+//   element e of S^T is key key0 + 8 (e / 4) + 4 g + e % 4 of row c;
+//   O^T += V^T . P^T over 16 steps, step s pairing the keys that the lanes'
+//   own element s holds, so B is P element s of the lane itself and A is
+//   V[key0 + 8 (s / 4) + 4 g + s % 4][32 db + c]: no exchange between lanes.
+template <int D>
+__global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
+  constexpr int kHalf = D / 2;
+  const int rb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x, col = lane & 31, g = lane >> 5;
+  const int max_keys = a.max_pages << a.c.log2_page;
+  const int q0 = checked(a.cu_q[b], 0, 0x7fffffff, kSiteRowOffset, b);
+  const int q_len = checked(a.cu_q[b + 1] - q0, 0, min(a.max_q_len, max_keys), kSiteQueryLen, b);
+  if (rb * 32 >= q_len) return;  // uniform
+  const int ctx = checked(a.ctx_lens[b], q_len, max_keys, kSiteCtxLen, b);
+  const int off = ctx - q_len;
+  const int hk = h / a.group;
+  const int W = a.window_left;
+  const int row = rb * 32 + col;
+  const int pos = off + min(row, q_len - 1);
+  const int p_first = off + rb * 32, p_last = off + min(rb * 32 + 31, q_len - 1);
+  const int k_lo = W >= 0 ? max(0, p_first - W) : 0;
+  const int k_hi = a.causal ? min(p_last, ctx - 1) : ctx - 1;
+  const int hi_r = a.causal ? min(pos, ctx - 1) : ctx - 1;  // this lane's row sees keys [lo_r, hi_r]
+  const int lo_r = W >= 0 ? pos - W : 0;
+  const float *kp = (const float *)a.c.k + (size_t)hk * D;
+  const float *vp = (const float *)a.c.v + (size_t)hk * D;
+  const size_t row_elems = (size_t)a.c.num_kv_heads * D;
+  auto row_of = [&](int key) __attribute__((always_inline)) {  // element offset of key's row
+    const int page = checked(a.block_table[(size_t)b * a.max_pages + (key >> a.c.log2_page)], 0, a.c.num_pages - 1,
+                             kSitePageId, b);
+    return ((size_t)page * a.c.page_size + (key & (a.c.page_size - 1))) * row_elems;
+  };
+  float qv[kHalf];
+  {
+    const float *qr = (const float *)a.q + ((size_t)(q0 + min(row, q_len - 1)) * a.num_q_heads + h) * D + g * kHalf;
+#pragma unroll
+    for (int s = 0; s < kHalf; s += 4) {
+      const float4 v = *reinterpret_cast<const float4 *>(qr + s);
+      qv[s] = v.x, qv[s + 1] = v.y, qv[s + 2] = v.z, qv[s + 3] = v.w;
+    }
+  }
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;  // l: this lane's half of the row sum
+  for (int key0 = k_lo & ~31; key0 <= k_hi; key0 += 32) {
+    // S^T of the 32 keys (rows past the context read the last key; masked).
+    float kv[kHalf];
+    {
+      const float *kr = kp + row_of(min(key0 + col, ctx - 1)) + g * kHalf;
+#pragma unroll
+      for (int s = 0; s < kHalf; s += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(kr + s);
+        kv[s] = v.x, kv[s + 1] = v.y, kv[s + 2] = v.z, kv[s + 3] = v.w;
+      }
+    }
+    f32x16 sacc = {};
+#pragma unroll
+    for (int s = 0; s < kHalf; ++s) sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[s], qv[s], sacc, 0, 0, 0);
+    float x[16], mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = key0 + 8 * (e >> 2) + 4 * g + (e & 3);
+      x[e] = (key >= lo_r && key <= hi_r) ? sacc[e] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, x[e]);
+    }
+    mx = max_xor32(mx);
+    const float m_new = fmaxf(m, mx);
+    const float corr = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
+    l *= corr;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] *= corr;
+    m = m_new;
+    float p[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = m == -INFINITY ? 0.f : fast_exp2(x[e] - m);
+      l += p[e];
+    }
+    // O^T += V^T . P^T; step s takes the keys of the lanes' element s.
+    size_t vrow[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) vrow[s] = row_of(min(key0 + 8 * (s >> 2) + 4 * g + (s & 3), ctx - 1)) + col;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vp[vrow[s] + 32 * db], p[s], o[db], 0, 0, 0);
+  }
+  const float ltot = l + __shfl_xor(l, 32, 64);
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  if (row < q_len) {
+    float *orow = (float *)a.out + ((size_t)(q0 + row) * a.num_q_heads + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4 *>(orow + 32 * db + 8 * j + 4 * g) =
+            make_float4(o[db][4 * j] * inv, o[db][4 * j + 1] * inv, o[db][4 * j + 2] * inv, o[db][4 * j + 3] * inv);
+    if (a.lse != nullptr && g == 0)
+      a.lse[(size_t)(q0 + row) * a.num_q_heads + h] = ltot > 0.f ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
+  }
+}
+
+static hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t s) {
+  const dim3 grid((a.max_q_len + 31) / 32, a.num_q_heads, a.batch);
+  if (a.c.head_dim == 64)
+    hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
 // Query tiles per run-mode workgroup: as many as kPfRun (fewer, longer
 // workgroups: a 128-key window at 8192 rows ran 121 us with 8 tiles against
 // 132 us with 4) while the grid still has a workgroup per CU, down to one
@@ -1128,7 +1250,9 @@ PA_DEFINE_FAULT_READER(take_fault_prefill)
 
 hipError_t launch_prefill(const PrefillArgs &a_in, hipStream_t s) {
   if (a_in.batch == 0 || a_in.max_q_len == 0) return hipSuccess;
-  if (a_in.c.dtype == 0) return launch_rowwise_f32(a_in, s);
+  // fp32: prefill on the fp32 MFMA; a single-token decode (no cu_q) keeps
+  // the one-wave-per-row kernel (a 32-row block would be 1/32 used).
+  if (a_in.c.dtype == 0) return a_in.cu_q != nullptr ? launch_prefill_f32(a_in, s) : launch_rowwise_f32(a_in, s);
   PrefillArgs a = a_in;
   const int n_qt = (a.max_q_len + kPfRows - 1) / kPfRows;
   // Causal without a window: pairs (p, n-1-p) balance the triangle.  A window

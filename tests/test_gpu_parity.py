@@ -61,6 +61,11 @@ PREFILL_CASES = [
     wl.PrefillWorkload("bf16_noncausal_runs", (1100,), 2, 1, 128, 256, "bf16", seed=40, causal=False),
     wl.PrefillWorkload("f32_d64_p16", (128, 45), 2, 1, 64, 16, "f32", seed=36),
     wl.PrefillWorkload("f32_d128_win3", (70,), 2, 2, 128, 32, "f32", seed=37, window_left=3),
+    # fp32 on its MFMA kernel (32-row blocks, 32-key steps): ragged rows over
+    # several blocks, GQA 4:1, 64-key pages, unmasked and with a window that
+    # starts inside a key step
+    wl.PrefillWorkload("f32_d128_g4_noncausal", (97, 200, 1), 8, 2, 128, 64, "f32", seed=38, causal=False),
+    wl.PrefillWorkload("f32_d64_win45", (161, 33), 4, 1, 64, 16, "f32", seed=41, window_left=45),
 ]
 
 
