@@ -163,7 +163,9 @@ pa_status kv_pages_quantize_int8(const void *src, int8_t *codes, float *scales, 
  *   out        : [cu_q[batch], num_q_heads, head_dim], dtype of q
  *   lse        : fp32 [cu_q[batch], num_q_heads] natural-log log-sum-exp of the
  *                scaled scores, or NULL
- * num_q_heads must be a multiple of cache->num_kv_heads. */
+ * num_q_heads must be a multiple of cache->num_kv_heads.
+ * Arithmetic: bf16 caches on bf16 MFMA (P rounded to bf16 as the P.V
+ * operand), fp32 caches on fp32 MFMA; accumulation and softmax in fp32. */
 pa_status attn_prefill_paged(const void *q, const int32_t *cu_q, const pa_kv_cache *cache,
                              const int32_t *block_table, int32_t max_pages_per_seq,
                              const int32_t *ctx_lens, int32_t batch, int32_t max_q_len,
