@@ -40,12 +40,15 @@
 // registers) and S^T = K . Q^T of this tile, both with
 // v_mfma_f32_32x32x16_bf16 (keys on M, the wave's rows on N, Q^T in
 // registers).  The softmax phase applies the mask and the online softmax on
-// the S^T registers (one query per lane column: one cross-lane max per
-// tile) and rounds P^T to bf16.  exp is exp2 with log2(e) folded into the
-// scale.  The running output is rescaled only when a row's maximum grows by
-// more than 2^8 over its reference (the exponent reference may lag the true
-// maximum by at most that much: probabilities stay <= 256, and O and l share
-// the reference, so the result is the same attention).
+// the S^T registers (one query per lane column) and rounds P^T to bf16.
+// exp is exp2 with log2(e) folded into the scale.  The exponent reference
+// of a row (m) is a maximum the row had earlier and may lag its true
+// maximum: a tile's probabilities are first taken against it, and only if
+// some lane's partial row sum leaves [0, 4096] (a probability above 4096,
+// or a row without a reference yet) does the wave compute the rows' maxima
+// (one cross-lane max), move the references up, rescale O and l and take
+// the probabilities again.  O and l share the reference, so the result is
+// the same attention; probabilities stay <= 4096.
 //
 // The FUSED instantiation is the prompt step with the append inside (KV
 // Cache section of "大模型推理优化实战：KV Cache + Flash Attention": the new
@@ -69,7 +72,7 @@ hipError_t launch_rowwise_f32(const PrefillArgs &a, hipStream_t s);
 constexpr int kPfRows = 128;         // query rows per query tile (4 waves x 32)
 constexpr int kPfKeys = 64;          // keys per key tile
 constexpr int kPfEngineThreads = 256;
-constexpr float kPfSlack = 8.f;      // log2 of the largest probability allowed
+constexpr float kPfSumCap = 4096.f;  // largest partial row sum (so probability) the reference may give
 constexpr int kPfRun = 8;            // most query tiles per workgroup in run mode (a.run_tiles <= this)
 
 template <int D>
@@ -656,12 +659,15 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // S^T = K . Q^T for the two 32-key blocks of the tile in LDS buffer `buf`.
   // The K fragments are read kAhead MFMAs ahead of their use (a ring of
   // registers), so the LDS latency hides behind the MFMAs before them.
+  // Consecutive MFMAs alternate between the two blocks' accumulators, so
+  // none waits for the one just issued (a chain of eight on one
+  // accumulator was measurably slower).
   auto qk_mfma = [&](int buf) __attribute__((always_inline)) {
     const unsigned char *ks = kbuf(buf);
     constexpr int kSteps = 2 * C::kNs;  // (key block, k-step) pairs
     constexpr int kAhead = 6;
     auto rd = [&](int u) __attribute__((always_inline)) {
-      const int kb = u / C::kNs, s = u % C::kNs;
+      const int kb = u & 1, s = u >> 1;
       if constexpr (kDirect)  // logical chunk 2 s + g of row kb * 32 + col, swizzled by the row
         return *reinterpret_cast<const bf16x8 *>(ks + (kb * 32 + col) * kKRowL + kd_off[s]);
       else
@@ -672,7 +678,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     for (int u = 0; u < kAhead; ++u) ka[u] = rd(u);
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
-      const int kb = u / C::kNs, s = u % C::kNs;
+      const int kb = u & 1, s = u >> 1;
       const bf16x8 cur = ka[u % kAhead];
       if (u + kAhead < kSteps) ka[u % kAhead] = rd(u + kAhead);
       sacc[kb] = mfma32(cur, bq[s], s == 0 ? f32x16{} : sacc[kb]);
@@ -683,7 +689,8 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     }
   };
   // O^T += V^T . P^T over four 16-key steps, V from LDS buffer `buf`.  The
-  // V^T fragments of step t + 1 are read before the MFMAs of step t.
+  // V^T fragments of step t + 1 are read before the MFMAs of step t; those
+  // of step 0 go out alone, so that its MFMAs wait for them only.
   auto read_v = [&](const unsigned char *vs, int t, bf16x8 *va) __attribute__((always_inline)) {
     const int r0 = (t >> 1) * 32 + (t & 1) * 16 + g * 4;
 #pragma unroll
@@ -701,6 +708,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     const unsigned char *vs = vbuf(buf);
     bf16x8 va[2][C::kNdb];
     read_v(vs, 0, va[0]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if (t + 1 < 4) read_v(vs, t + 1, va[(t + 1) & 1]);
@@ -711,7 +719,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     }
   };
   // Mask and online softmax of tile (qt, kt) on sacc; P^T -> bp.
-  auto softmax = [&](int qt, int kt) __attribute__((always_inline)) {
+  auto softmax = [&](int qt, int kt, bool fresh) __attribute__((always_inline)) {
     const int key0 = kt * kPfKeys;
     const int pos = off + qt * kPfRows + w * 32 + col;
     const int p_first = off + qt * kPfRows;
@@ -750,17 +758,38 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
           sacc[kb][i] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, v) & keep) | (0xff800000u & ~keep));
         }
     }
-    float mx0 = -INFINITY, mx1 = -INFINITY;
+    // P^T against reference nm = -m, rounded into bp; returns this lane's
+    // partial row sum (its 32 of the row's 64 keys).
+    auto exps = [&](float nm) __attribute__((always_inline)) {
+      float ps[4];  // four partial sums, each started at its first term
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      mx0 = fmaxf(mx0, sacc[0][i]);
-      mx1 = fmaxf(mx1, sacc[1][i]);
-    }
-    const float mx = max_xor32(fmaxf(mx0, mx1)) * a.scale_log2;
-    if (__any(mx > m + kPfSlack)) {
-      // New reference for every lane of the wave (a lane whose max did not
-      // grow keeps a factor of 1).  A row without a visible key yet keeps
-      // m = -inf and factor 1.
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(fmaf(sacc[kb][i], a.scale_log2, nm));
+          if (kb == 0 && i < 4)
+            ps[i] = p;
+          else
+            ps[i & 3] += p;
+          bp[2 * kb + (i >> 3)][i & 7] = (__bf16)p;
+        }
+      return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    };
+    // First try the row's present reference: if every lane's partial sum is
+    // at most the cap, every probability is too, and the reference stands.
+    // A lane without a reference yet (m = -inf) gets +inf or NaN and fails.
+    float part = fresh ? INFINITY : exps(m == -INFINITY ? INFINITY : -m);
+    if (__any(!(part <= kPfSumCap))) {
+      // Move every row's reference up to its maximum so far (a row whose
+      // maximum did not grow keeps a factor of 1; one without a visible key
+      // yet keeps m = -inf), rescale, and recompute.
+      float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        mx0 = fmaxf(mx0, sacc[0][i]);
+        mx1 = fmaxf(mx1, sacc[1][i]);
+      }
+      const float mx = max_xor32(fmaxf(mx0, mx1)) * a.scale_log2;
       const float m_new = fmaxf(m, mx);
       const float corr = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
       // Rows without a reference yet hold o = 0 and lsum = 0: the first
@@ -771,28 +800,12 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
         for (int db = 0; db < C::kNdb; ++db) o[db] *= corr;
       }
       m = m_new;
+      part = exps(m == -INFINITY ? 0.f : -m);
     }
-    const float neg_m = m == -INFINITY ? 0.f : -m;
-    float ps[4];  // four partial row sums, each started at its first term
+    lsum += part;
+    // Materialise P in this (softmax) half-step, like S above.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(sacc[kb][i], a.scale_log2, neg_m));
-        if (kb == 0 && i < 4)
-          ps[i] = p;
-        else
-          ps[i & 3] += p;
-        sacc[kb][i] = p;
-      }
-    lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bp[t][e] = (__bf16)sacc[t >> 1][8 * (t & 1) + e];
-      // Materialise P in this (softmax) half-step, like S above.
-      __asm__ volatile("" : "+v"(bp[t]));
-    }
+    for (int t = 0; t < 4; ++t) __asm__ volatile("" : "+v"(bp[t]));
   };
 
   // Ping-pong schedule in half-steps (one workgroup barrier each).  For its
@@ -816,12 +829,15 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // accesses across it.  After a GEMM phase: this wave's LDS reads are done
   // (the buffers they read are reloaded in the next phase).  After a softmax
   // phase and after the prologue: every load but the last 8 (those of this
-  // phase: the next-but-one K tile and the next V tile) has landed.  (The
-  // compiler, which cannot tell those 8 LDS writes from the next GEMM
-  // phase's LDS reads, also waits for them before its first read: their
-  // latency hides behind the softmax phase.)
+  // phase: the next-but-one K tile and the next V tile) has landed, and so
+  // has the phase's block-table read (a scalar load still in flight would
+  // make the compiler wait for all of the next phase's LDS reads before its
+  // first MFMA, as it cannot count them apart).  (The compiler, which
+  // cannot tell those 8 LDS writes from the next GEMM phase's LDS reads,
+  // also waits for them before its first read: their latency hides behind
+  // the softmax phase.)
   constexpr int kWaitLgkm0 = 0xC07F;  // vmcnt(63) expcnt(7) lgkmcnt(0)
-  constexpr int kWaitVm8 = 0x0F78;    // vmcnt(8) expcnt(7) lgkmcnt(15)
+  constexpr int kWaitVm8 = 0x0078;    // vmcnt(8) expcnt(7) lgkmcnt(0)
   auto bar_after_gemm = [&]() __attribute__((always_inline)) {
     if constexpr (kDirect) {
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -975,7 +991,8 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     }
     int qt = wq0, kt = wk0;
     if constexpr (!kDirect) my_item(t, qt, kt);
-    if (qt != qt_o) {
+    const bool fresh = qt != qt_o;
+    if (fresh) {
       if (qt_o >= 0) finish(qt_o, m, lsum, o);
       reset_o();
       qt_o = qt;
@@ -1005,7 +1022,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       ck = wk2, coff = off2, cres = r2;
       advance(t);
     }
-    softmax(qt, kt);
+    softmax(qt, kt, fresh);
     if constexpr (!kDirect) {
       if (t + 1 < n_mine && !resident(t + 1)) {
         store_k((t + 1) & 1, pk);
