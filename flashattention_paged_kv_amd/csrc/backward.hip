@@ -337,14 +337,33 @@ __device__ __forceinline__ void dq_tile(const BackwardArgs &a, int qt, int h, in
     }
     __syncthreads();
     f32x16 sacc[2], dpacc[2];
+    {
+      // Four chains interleaved (u % 4: S^T of key block 0, dP^T of block 0,
+      // S^T of block 1, dP^T of block 1; k-step u / 4), their K / V fragments
+      // read kAhead products ahead (a ring of registers), so no MFMA waits
+      // for an LDS read issued just before it.  The first product of each
+      // chain starts from a zero operand.
+      constexpr int kSteps = 4 * C::kNs;
+      constexpr int kAhead = 8;
+      auto rd = [&](int u) __attribute__((always_inline)) {
+        const int kb = (u >> 1) & 1, s = u >> 2;
+        const unsigned char *base = (u & 1) ? vsm : ksm;
+        return *reinterpret_cast<const bf16x8 *>(base + (kb * 32 + col) * C::kKRow + (16 * s + 8 * g) * 2);
+      };
+      static_assert(C::kKRow == C::kVRow, "K and V staged with one pitch");
+      bf16x8 fa[kAhead];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int u = 0; u < kAhead; ++u) fa[u] = rd(u);
 #pragma unroll
-      for (int s = 0; s < C::kNs; ++s) {  // the first product starts from a zero operand
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ksm + (kb * 32 + col) * C::kKRow + (16 * s + 8 * g) * 2);
-        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vsm + (kb * 32 + col) * C::kVRow + (16 * s + 8 * g) * 2);
-        sacc[kb] = mfma32(kf, bq[s], s == 0 ? f32x16{} : sacc[kb]);
-        dpacc[kb] = mfma32(vf, bdo[s], s == 0 ? f32x16{} : dpacc[kb]);
+      for (int u = 0; u < kSteps; ++u) {
+        const int kb = (u >> 1) & 1, s = u >> 2;
+        const bf16x8 cur = fa[u % kAhead];
+        if (u + kAhead < kSteps) fa[u % kAhead] = rd(u + kAhead);
+        if (u & 1)
+          dpacc[kb] = mfma32(cur, bdo[s], s == 0 ? f32x16{} : dpacc[kb]);
+        else
+          sacc[kb] = mfma32(cur, bq[s], s == 0 ? f32x16{} : sacc[kb]);
+        __builtin_amdgcn_sched_barrier(0);  // keep each read kAhead products ahead
       }
     }
     // dS^T = P^T (dP^T - D), masked; element i of block kb is key
@@ -352,26 +371,46 @@ __device__ __forceinline__ void dq_tile(const BackwardArgs &a, int qt, int h, in
     bf16x8 bds[4];
     // Every key of the tile visible to every row of the workgroup: no mask.
     const bool interior = key0 >= max_lo && key0 + kBwKeys - 1 <= min_hi;
+    // (The choice is made once per tile: inside the loop the compiler
+    // evaluated the mask on every element of every tile.)
+    auto probs = [&](auto MASKED) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(sacc[kb][i] * a.scale_log2 - lse2);
-        if (!interior) {
-          const int key = key0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-          p = (key >= lo_r && key <= hi_r) ? p : 0.f;
+        for (int i = 0; i < 16; ++i) {
+          float p = fast_exp2(sacc[kb][i] * a.scale_log2 - lse2);
+          if constexpr (decltype(MASKED)::value) {
+            const int key = key0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+            p = (key >= lo_r && key <= hi_r) ? p : 0.f;
+          }
+          bds[2 * kb + (i >> 3)][i & 7] = (__bf16)(p * (dpacc[kb][i] - dlt));
         }
-        bds[2 * kb + (i >> 3)][i & 7] = (__bf16)(p * (dpacc[kb][i] - dlt));
-      }
-    // dQ^T += K^T . dS^T over four 16-key steps.
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int r0 = (t >> 1) * 32 + (t & 1) * 16 + g * 4;
-#pragma unroll
-      for (int db = 0; db < C::kNdb; ++db) {
+    };
+    if (interior)
+      probs(std::false_type{});
+    else
+      probs(std::true_type{});
+    // dQ^T += K^T . dS^T over four 16-key steps (product u: step u / kNdb,
+    // output block u % kNdb), K^T fragments read kAhead products ahead.
+    {
+      constexpr int kSteps = 4 * C::kNdb;
+      constexpr int kAhead = 4;
+      auto rd = [&](int u) __attribute__((always_inline)) {
+        const int t = u / C::kNdb, db = u % C::kNdb;
+        const int r0 = (t >> 1) * 32 + (t & 1) * 16 + g * 4;
         const unsigned char *p1 = ksm + (r0 + (tp >> 2)) * C::kKRow + (db * 32 + 16 * (gam & 1) + 4 * (tp & 3)) * 2;
-        const bf16x8 kt_frag = cat(lds_read_tr16(p1), lds_read_tr16(p1 + 8 * C::kKRow));
-        acc[db] = mfma32(kt_frag, bds[t], acc[db]);
+        return cat(lds_read_tr16(p1), lds_read_tr16(p1 + 8 * C::kKRow));
+      };
+      bf16x8 fa[kAhead];
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) fa[u] = rd(u);
+#pragma unroll
+      for (int u = 0; u < kSteps; ++u) {
+        const int t = u / C::kNdb, db = u % C::kNdb;
+        const bf16x8 cur = fa[u % kAhead];
+        if (u + kAhead < kSteps) fa[u % kAhead] = rd(u + kAhead);
+        acc[db] = mfma32(cur, bds[t], acc[db]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __syncthreads();  // the tile is restaged next
@@ -470,14 +509,42 @@ __device__ __forceinline__ void dkv_tile(const BackwardArgs &a, int kt, int hk, 
       __syncthreads();
       load_step(min(j + 1, n_steps - 1));  // unconditional: exact wait counts
       constexpr int kMb = kBwRowTile / 32;  // 32-row blocks
+      static_assert(kMb == 1, "one 32-row block per step");
+      // lse and D of this lane's 16 rows (rows q4*8 + g*4 + 0..3: four
+      // vectors each), read before the products so their latency hides
+      // behind them.
+      f32x4 l4v[4], d4v[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        l4v[q4] = *reinterpret_cast<const f32x4 *>(lse_s + q4 * 8 + g * 4);
+        d4v[q4] = *reinterpret_cast<const f32x4 *>(dl_s + q4 * 8 + g * 4);
+      }
       f32x16 sacc[kMb], dpacc[kMb];
+      {
+        // S and dP alternate (u even: Q . K^T, u odd: dO . V^T, k-step u / 2);
+        // their Q / dO fragments are read kAhead products ahead (a ring of
+        // registers), so each MFMA finds its operand in place instead of
+        // waiting for an LDS read issued just before it.  The first product
+        // of each starts from a zero operand.
+        constexpr int kSteps = 2 * C::kNs;
+        constexpr int kAhead = 6;
+        auto rd = [&](int u) __attribute__((always_inline)) {
+          const int ro = col * kPitch + (16 * (u >> 1) + 8 * g) * 2;
+          return *reinterpret_cast<const bf16x8 *>(((u & 1) ? dosm : qsm) + ro);
+        };
+        bf16x8 fa[kAhead];
 #pragma unroll
-      for (int mb = 0; mb < kMb; ++mb) {
+        for (int u = 0; u < kAhead; ++u) fa[u] = rd(u);
 #pragma unroll
-        for (int s = 0; s < C::kNs; ++s) {  // the first product starts from a zero operand
-          const int ro = (mb * 32 + col) * kPitch + (16 * s + 8 * g) * 2;
-          sacc[mb] = mfma32(*reinterpret_cast<const bf16x8 *>(qsm + ro), bk[s], s == 0 ? f32x16{} : sacc[mb]);
-          dpacc[mb] = mfma32(*reinterpret_cast<const bf16x8 *>(dosm + ro), bv[s], s == 0 ? f32x16{} : dpacc[mb]);
+        for (int u = 0; u < kSteps; ++u) {
+          const int s = u >> 1;
+          const bf16x8 cur = fa[u % kAhead];
+          if (u + kAhead < kSteps) fa[u % kAhead] = rd(u + kAhead);
+          if (u & 1)
+            dpacc[0] = mfma32(cur, bv[s], s == 0 ? f32x16{} : dpacc[0]);
+          else
+            sacc[0] = mfma32(cur, bk[s], s == 0 ? f32x16{} : sacc[0]);
+          __builtin_amdgcn_sched_barrier(0);  // keep each read kAhead products ahead
         }
       }
       // Element i of block mb is row rt + mb*32 + (i/4)*8 + g*4 + i%4 against
@@ -489,39 +556,54 @@ __device__ __forceinline__ void dkv_tile(const BackwardArgs &a, int kt, int hk, 
       const bool interior = key_first + kBwKeyTile <= ctx && rt + kBwRowTile <= q_len &&
                             (!a.causal || key_first + kBwKeyTile - 1 <= off + rt) &&
                             (a.window_left < 0 || off + rt + kBwRowTile - 1 - key_first <= a.window_left);
+      // P and dS; the mask is decided once per step (interior steps skip it).
+      auto probs = [&](auto MASKED) __attribute__((always_inline)) {
 #pragma unroll
-      for (int mb = 0; mb < kMb; ++mb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          // rows mb*32 + q4*8 + g*4 + (0..3): four consecutive lse / D values
-          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(lse_s + mb * 32 + q4 * 8 + g * 4);
-          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(dl_s + mb * 32 + q4 * 8 + g * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = q4 * 4 + e;
-            const int rr = mb * 32 + q4 * 8 + g * 4 + e;
-            float p = fast_exp2(sacc[mb][i] * a.scale_log2 - l4[e]);
-            if (!interior) {
-              const int pos = off + rt + rr;
-              bool vis = key < ctx && rt + rr < q_len;
-              if (a.causal) vis = vis && key <= pos;
-              if (a.window_left >= 0) vis = vis && pos - key <= a.window_left;
-              p = vis ? p : 0.f;
-            }
-            bp[2 * mb + (i >> 3)][i & 7] = (__bf16)p;
-            bds[2 * mb + (i >> 3)][i & 7] = (__bf16)(p * (dpacc[mb][i] - d4[e]));
+        for (int i = 0; i < 16; ++i) {
+          const int q4 = i >> 2, e = i & 3;
+          const int rr = q4 * 8 + g * 4 + e;
+          float p = fast_exp2(sacc[0][i] * a.scale_log2 - l4v[q4][e]);
+          if constexpr (decltype(MASKED)::value) {
+            const int pos = off + rt + rr;
+            bool vis = key < ctx && rt + rr < q_len;
+            if (a.causal) vis = vis && key <= pos;
+            if (a.window_left >= 0) vis = vis && pos - key <= a.window_left;
+            p = vis ? p : 0.f;
           }
+          bp[i >> 3][i & 7] = (__bf16)p;
+          bds[i >> 3][i & 7] = (__bf16)(p * (dpacc[0][i] - d4v[q4][e]));
         }
-#pragma unroll
-      for (int t = 0; t < 2 * kMb; ++t) {
-        const int r0 = (t >> 1) * 32 + (t & 1) * 16 + g * 4;
-#pragma unroll
-        for (int db = 0; db < C::kNdb; ++db) {
+      };
+      if (interior)
+        probs(std::false_type{});
+      else
+        probs(std::true_type{});
+      // dV^T += dO^T . P and dK^T += Q^T . dS over two 16-row steps (product
+      // u: step u / (2 kNdb), output block (u / 2) % kNdb, dV for even u and
+      // dK for odd), the transposed fragments read kAhead products ahead.
+      {
+        constexpr int kSteps = 4 * C::kNdb;
+        constexpr int kAhead = 4;
+        auto rd = [&](int u) __attribute__((always_inline)) {
+          const int t = u / (2 * C::kNdb), db = (u >> 1) % C::kNdb;
+          const int r0 = (t >> 1) * 32 + (t & 1) * 16 + g * 4;
           const int c = (db * 32 + 16 * (gam & 1) + 4 * (tp & 3)) * 2;
-          const unsigned char *pd = dosm + (r0 + (tp >> 2)) * kPitch + c;
-          const unsigned char *pq = qsm + (r0 + (tp >> 2)) * kPitch + c;
-          dv[db] = mfma32(cat(lds_read_tr16(pd), lds_read_tr16(pd + 8 * kPitch)), bp[t], dv[db]);
-          dk[db] = mfma32(cat(lds_read_tr16(pq), lds_read_tr16(pq + 8 * kPitch)), bds[t], dk[db]);
+          const unsigned char *pr = ((u & 1) ? qsm : dosm) + (r0 + (tp >> 2)) * kPitch + c;
+          return cat(lds_read_tr16(pr), lds_read_tr16(pr + 8 * kPitch));
+        };
+        bf16x8 fa[kAhead];
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) fa[u] = rd(u);
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+          const int t = u / (2 * C::kNdb), db = (u >> 1) % C::kNdb;
+          const bf16x8 cur = fa[u % kAhead];
+          if (u + kAhead < kSteps) fa[u % kAhead] = rd(u + kAhead);
+          if (u & 1)
+            dk[db] = mfma32(cur, bds[t], dk[db]);
+          else
+            dv[db] = mfma32(cur, bp[t], dv[db]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       __syncthreads();  // the tiles are restaged next
