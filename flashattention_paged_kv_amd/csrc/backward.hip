@@ -314,21 +314,35 @@ __device__ __forceinline__ void dq_tile(const BackwardArgs &a, int qt, int h, in
   constexpr int kRowsPerPass = 256 / C::kCpr;
   // K/V of a tile through registers into LDS (rows past the context read
   // the last valid row).
+  // The page ids of a tile's rows are looked up two tiles ahead and its K /
+  // V rows loaded one tile ahead, so neither round trip to memory waits in
+  // front of a tile's products (loaded synchronously, the two dependent
+  // round trips took about half of each tile's time).
   u32x4 kreg[C::kLoads], vreg[C::kLoads];
-  auto load_tile = [&](int kt) __attribute__((always_inline)) {
+  int pgs[C::kLoads];
+  auto lookup = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
       const int key = min(kt * kBwKeys + lrow + i * kRowsPerPass, ctx - 1);
-      const int page = bw_page(a, b, key >> a.c.log2_page);
-      const size_t ro = ((size_t)page * a.c.page_size + (key & (a.c.page_size - 1))) * row_elems + lch * 8;
+      pgs[i] = bw_page(a, b, key >> a.c.log2_page);
+    }
+  };
+  auto fetch = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+      const int key = min(kt * kBwKeys + lrow + i * kRowsPerPass, ctx - 1);
+      const size_t ro = ((size_t)pgs[i] * a.c.page_size + (key & (a.c.page_size - 1))) * row_elems + lch * 8;
       kreg[i] = *reinterpret_cast<const u32x4 *>(kpool + ro);
       vreg[i] = *reinterpret_cast<const u32x4 *>(vpool + ro);
     }
   };
+  const int kt_beg = k_lo / kBwKeys;
   const int kt_end = k_hi / kBwKeys;
-  for (int kt = k_lo / kBwKeys; kt <= kt_end; ++kt) {
+  lookup(kt_beg);
+  fetch(kt_beg);
+  lookup(min(kt_beg + 1, kt_end));
+  for (int kt = kt_beg; kt <= kt_end; ++kt) {
     const int key0 = kt * kBwKeys;
-    load_tile(kt);
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
       const int r = lrow + i * kRowsPerPass;
@@ -336,6 +350,10 @@ __device__ __forceinline__ void dq_tile(const BackwardArgs &a, int qt, int h, in
       *reinterpret_cast<u32x4 *>(vsm + r * C::kVRow + lch * 16) = vreg[i];
     }
     __syncthreads();
+    // Next tile's rows, then the page ids of the one after (clamped to the
+    // last tile: the same loads on every path).
+    fetch(min(kt + 1, kt_end));
+    lookup(min(kt + 2, kt_end));
     f32x16 sacc[2], dpacc[2];
     {
       // Four chains interleaved (u % 4: S^T of key block 0, dP^T of block 0,
@@ -627,10 +645,10 @@ __device__ __forceinline__ void dkv_tile(const BackwardArgs &a, int kt, int hk, 
 // under a causal mask the key-tile counts of the two add up to the same
 // total for every p, so all workgroups carry equal work.  (One tile per
 // workgroup, all resident at once, left the kernel as long as its heaviest
-// tile, about twice the average.)  At most 256 registers per lane, so two
-// workgroups can share a CU where the grid is large enough.
+// tile, about twice the average.)  One workgroup per CU: the prefetched
+// tile needs more than 256 registers per lane.
 template <int D>
-__global__ __launch_bounds__(256, 2) void dq_mfma_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(256) void dq_mfma_kernel(BackwardArgs a) {
   using C = BwCfg<D>;
   __shared__ __align__(16) unsigned char ksm[kBwKeys * C::kKRow];
   __shared__ __align__(16) unsigned char vsm[kBwKeys * C::kVRow];
