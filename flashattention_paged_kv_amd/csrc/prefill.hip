@@ -809,9 +809,10 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   };
 
   // Ping-pong schedule in half-steps (one workgroup barrier each).  For its
-  // tile t an engine runs a GEMM phase G(t) = [PV of tile t-1, QK of tile t]
-  // (MFMA) and then a softmax phase S(t) (VALU); after its last tile, G(n) =
-  // PV of tile n-1 alone.  Engine 1 runs one half-step behind engine 0, so on
+  // tile t an engine runs a GEMM phase G(t) = [QK of tile t, PV of tile t-1]
+  // (MFMA; in that order, so the QK results the softmax reads first are done
+  // while the PV products finish) and then a softmax phase S(t) (VALU);
+  // after its last tile, G(n) = PV of tile n-1 alone.  Engine 1 runs one half-step behind engine 0, so on
   // every SIMD one wave's softmax overlaps the other wave's MFMAs.  Tile t
   // lives in LDS buffer t % 2.  Its K and V are loaded into registers at the
   // start of G(t-1) and stored at the end of S(t-1): a whole step of load
@@ -951,7 +952,6 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
         load_tile(kt, RUNS && (t + 1 >= n_mine || resident(t + 1)));
       }
     }
-    if (t >= 1) pv_mfma((t - 1) & 1);
     if (t < n_mine) {
       int qt, kt;
       my_item(t, qt, kt);
@@ -974,6 +974,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
         }
       }
     }
+    if (t >= 1) pv_mfma((t - 1) & 1);
   };
   auto softmax_phase = [&](int t) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(0);
