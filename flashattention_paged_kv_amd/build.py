@@ -45,9 +45,10 @@ def sources():
 
 
 # Per-source device code generation options.  backward.hip: MFMA results in
-# ordinary vector registers where they fit (the dK/dV kernel's score and dP
-# blocks then need no copies out of the accumulation registers before the
-# softmax arithmetic: 134 against 148 us at L=2048).
+# ordinary vector registers (the dK/dV kernel's score and dP blocks then need
+# no copies out of the accumulation registers before the softmax arithmetic:
+# 134 against 148 us at L=2048); its long-lived dK / dV sums are pinned to
+# the accumulation registers in the source instead.
 SOURCE_FLAGS = {"backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 

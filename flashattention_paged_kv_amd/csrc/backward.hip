@@ -94,6 +94,15 @@ __global__ __launch_bounds__(256) void delta_kernel(BackwardArgs a) {
   }
 }
 
+// acc += a . b on v_mfma_f32_32x32x16_bf16 with the accumulator held in the
+// accumulation registers (AGPRs): the dK/dV kernel's long-lived dK and dV
+// sums then leave the vector registers to the operands and the score blocks
+// the softmax arithmetic reads.  Back-to-back products on one accumulator
+// need no wait states; a VALU read of it does (see the reader).
+__device__ __forceinline__ void mfma32_agpr(f32x16 &acc, bf16x8 a, bf16x8 b) {
+  __asm__ volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 // Device-resident integers of sequence b (checked in debug builds against
 // the ranges the entry point documents).
 __device__ __forceinline__ int bw_q0(const BackwardArgs &a, int b) {
@@ -618,15 +627,18 @@ __device__ __forceinline__ void dkv_tile(const BackwardArgs &a, int kt, int hk, 
           const bf16x8 cur = fa[u % kAhead];
           if (u + kAhead < kSteps) fa[u % kAhead] = rd(u + kAhead);
           if (u & 1)
-            dk[db] = mfma32(cur, bds[t], dk[db]);
+            mfma32_agpr(dk[db], cur, bds[t]);
           else
-            dv[db] = mfma32(cur, bp[t], dv[db]);
+            mfma32_agpr(dv[db], cur, bp[t]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
       __syncthreads();  // the tiles are restaged next
     }
   }
+  // The accumulators were written by MFMAs the compiler does not see
+  // (asm): wait out the MFMA-to-VALU read latency before reading them.
+  __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   if (key < ctx) {
     float *dkr = a.dk + krow;
     float *dvr = a.dv + krow;
