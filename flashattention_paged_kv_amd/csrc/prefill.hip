@@ -404,8 +404,8 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // that holds both cached and new keys (when the first new position is not
   // a multiple of 64) takes each row from where it is, every lane loading
   // through one of two descriptors, so each LDS slot is written once.
-  auto issue_direct = [&](int kt, size_t tile_off, const char *base, const char *nbase, unsigned char *dst, bool is_v,
-                          bool res) __attribute__((always_inline)) {
+  auto issue_direct = [&](auto mx, int kt, size_t tile_off, const char *base, const char *nbase, unsigned char *dst,
+                          bool is_v, bool res) __attribute__((always_inline)) {
     if constexpr (kDirect) {
       static_assert(!kDirect || C::kLoads == 4, "the direct path issues four loads per lane and tile");
       const int key0 = kt * kPfKeys;
@@ -414,37 +414,36 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       bool mixed = false;
       if constexpr (FUSED) {
         if (key0 >= off) tb = uniform_ptr(nbase + (size_t)(key0 - off) * row_bytes);
-        mixed = !res && key0 < off && key0 + kPfKeys > off;
+        if constexpr (decltype(mx)::value) mixed = !res && key0 < off && key0 + kPfKeys > off;
       }
       const __amdgpu_buffer_rsrc_t r = make_rsrc(tb, span);
       unsigned char *dw = dst + 16 * w * kKRowL;  // this wave's 4 KiB of the buffer
-      if (res) {
-        // Into this wave's 1 KiB of scratch LDS, all four at offset 0.
-        unsigned char *scratch = ebase + 2 * (kKBufL + kVBufL) + w * 1024;
-#pragma unroll
-        for (int i = 0; i < C::kLoads; ++i) {
-          // (Offsets go through a local: a lambda call as the builtin's
-          // argument keeps the host pass from emitting the kernel.)
-          const uint32_t vo = lane_dt(is_v, i);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PA_LDS void *)scratch, 16, vo, 0, 0, 0);
-        }
-      } else if (FUSED && mixed) {
+      // The resident case takes no branch of its own: a branch around the
+      // loads leaves the compiler a path that it thinks issues none (it cannot
+      // tell that one side always runs), and then it no longer takes the
+      // previous step's Q loads as landed at the end of the phase and waits
+      // for every load in flight before the next QK product.  (The fused
+      // append's tile of both cached and new keys, whose lanes choose
+      // between two descriptors in branches, does that: it is loaded only in
+      // a copy of the loops of its own, for sequences whose cached part does
+      // not end on a 64-key boundary.)
+      if (FUSED && mixed) {
         // New rows from nbase (row index key - off), the rest from the page.
-        const __amdgpu_buffer_rsrc_t rn = make_rsrc(uniform_ptr(nbase), (uint32_t)(min(kPfKeys, ctx - off) * row_bytes));
-        const uint32_t new_off = (uint32_t)((key0 - off) * (int)row_bytes);
         // (The distinct asm markers keep the two loads apart: merged into
         // one, its descriptor would be chosen per lane.)
-#define PA_LD_MIXED(I)                                                                      \
-  {                                                                                         \
-    const uint32_t vo = lane_dt(is_v, I) - 1024 * (I);                                      \
-    if (key0 + drow + 4 * (I) < off) {                                                      \
+        const __amdgpu_buffer_rsrc_t rn = make_rsrc(uniform_ptr(nbase), (uint32_t)(min(kPfKeys, ctx - off) * row_bytes));
+        const uint32_t new_off = (uint32_t)((key0 - off) * (int)row_bytes);
+#define PA_LD_MIXED(I)                                                                         \
+  {                                                                                            \
+    const uint32_t vo = lane_dt(is_v, I) - 1024 * (I);                                         \
+    if (key0 + drow + 4 * (I) < off) {                                                         \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PA_LDS void *)dw, 16, vo, 0, 1024 * (I), 0); \
-      __asm__ volatile("; cached rows" ::: "memory");                                       \
-    } else {                                                                                \
-      const uint32_t vn = vo + new_off;                                                     \
+      __asm__ volatile("; cached rows" ::: "memory");                                          \
+    } else {                                                                                   \
+      const uint32_t vn = vo + new_off;                                                        \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rn, (PA_LDS void *)dw, 16, vn, 0, 1024 * (I), 0); \
-      __asm__ volatile("; new rows" ::: "memory");                                          \
-    }                                                                                       \
+      __asm__ volatile("; new rows" ::: "memory");                                             \
+    }                                                                                          \
   }
         PA_LD_MIXED(0)
         PA_LD_MIXED(1)
@@ -452,10 +451,15 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
         PA_LD_MIXED(3)
 #undef PA_LD_MIXED
       } else {
-#define PA_LD(I)                                                                            \
-  {                                                                                         \
-    const uint32_t vo = lane_dt(is_v, I) - 1024 * (I);                                      \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PA_LDS void *)dw, 16, vo, 0, 1024 * (I), 0); \
+        // A resident tile: the same loads through the descriptor of length 0
+        // land in this wave's 1 KiB of scratch LDS (LDS base moved back by
+        // the instruction offset, so all four write the same 1 KiB).
+        unsigned char *scratch = ebase + 2 * (kKBufL + kVBufL) + w * 1024;
+#define PA_LD(I)                                                                               \
+  {                                                                                            \
+    const uint32_t vo = lane_dt(is_v, I) - 1024 * (I);                                         \
+    unsigned char *d = res ? scratch - 1024 * (I) : dw;                                        \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PA_LDS void *)d, 16, vo, 0, 1024 * (I), 0);   \
   }
         PA_LD(0)
         PA_LD(1)
@@ -465,25 +469,41 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       }
     }
   };
-  // Fused append, direct path: item idx's tile is in the LDS buffer `src`
-  // (K or V), each wave's rows put there by its own loads.  The rows that are
-  // new and belong to the item's query tile go to their page slots: every
-  // lane stores the 16 bytes it loaded at the page offset it would have read
-  // them from.  The caller runs this before the wave's next loads into `src`.
-  auto write_back = [&](int qt, int kt, const unsigned char *src, char *pool, bool is_v)
+  // Fused append, direct path: item (qt, kt)'s tile is in the LDS buffer
+  // `src` (K or V), each wave's rows put there by its own loads; `entry` is
+  // the block-table entry of the tile's page.  The rows that are new and
+  // belong to the item's query tile go to their page slots: every lane
+  // stores the 16 bytes it loaded at the page offset it would have read
+  // them from.  The stores go through a descriptor that ends at the last
+  // such row, so the hardware's range check drops the rows past it; a row
+  // before the first gets the descriptor's length as its offset, out of
+  // range the same way.  No lane branches, and only the 32-bit lane offsets
+  // the loads use.  (The rows are read from LDS as bf16 vectors, like the
+  // QK operands: read as integers, they made the compiler wait for every
+  // load in flight first.)  The caller runs this before the wave's next
+  // loads into `src`.
+  auto write_back = [&](int qt, int kt, int entry, const unsigned char *src, char *pool, bool is_v)
       __attribute__((always_inline)) {
     if constexpr (FUSED && kDirect) {
       const int key0 = kt * kPfKeys;
       const int w_lo = max(key0, off + qt * kPfRows);
       const int w_hi = min(min(key0 + kPfKeys, off + qt * kPfRows + kPfRows), ctx);
       if (kv_writer && w_lo < w_hi) {
-        char *dp = pool + (size_t)hk * D * 2 + tile_page_off(kt);
+        // (Said uniform: the compiler computes w_hi on the vector unit, and a
+        // descriptor it takes as per-lane becomes a loop over its values.)
+        const uint32_t span =
+            (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(w_hi - key0) * (uint32_t)row_bytes));
+        const __amdgpu_buffer_rsrc_t r =
+            make_rsrc(uniform_ptr(pool + (size_t)hk * D * 2 + page_off(entry, kt)), span);
+        const int lo = w_lo - key0;
+        bf16x8 x[C::kLoads];
+#pragma unroll
+        for (int i = 0; i < C::kLoads; ++i)
+          x[i] = *reinterpret_cast<const bf16x8 *>(src + (16 * w + 4 * i) * kKRowL + lane * 16);
 #pragma unroll
         for (int i = 0; i < C::kLoads; ++i) {
-          const int key = key0 + drow + 4 * i;
-          if (key >= w_lo && key < w_hi)
-            *reinterpret_cast<uint4 *>(dp + lane_dt(is_v, i)) =
-                *reinterpret_cast<const uint4 *>(src + (16 * w + 4 * i) * kKRowL + lane * 16);
+          const uint32_t vo = drow + 4 * i >= lo ? lane_dt(is_v, i) : span;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x[i]), r, (int)vo, 0, 0);
         }
       }
     }
@@ -872,6 +892,9 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   int wq_m1 = 0, wk_m1 = 0, wq0 = 0, wk0 = 0, wq1 = 0, wk1 = 0, wq2 = 0, wk2 = 0;
   int wlo = 0, whi = 0;  // run mode: the key-tile range of query tile wq2
   int pg2 = 0;
+  // Fused: the block-table entries of items t - 1, t and t + 1, carried
+  // along so that the write-back of items t and t - 1 reads no table.
+  int pe_m1 = 0, pe0 = 0, pe1 = 0;
   int ck = 0;
   size_t coff = 0;
   bool cres = false;
@@ -880,6 +903,7 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   };
   auto advance = [&](int t) __attribute__((always_inline)) {  // window of step t -> step t + 1
     wq_m1 = wq0, wk_m1 = wk0, wq0 = wq1, wk0 = wk1, wq1 = wq2, wk1 = wk2;
+    if constexpr (FUSED) pe_m1 = pe0, pe0 = pe1, pe1 = pg2;
     if constexpr (RUNS) {
       wk2 += ks;
       if (ks > 0 ? wk2 >= whi : wk2 < wlo) {
@@ -892,27 +916,29 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
     }
     pg2 = page_entry(wk2, t + 3 < n_mine || !RUNS);
   };
-  if constexpr (kDirect) {
+  auto direct_prologue = [&](auto mx) __attribute__((always_inline)) {
     // Q^T of the first query tile straight into registers, then K(0), V(0)
     // and K(1) into LDS buffers 0, 0 and 1 (K(t + 2) and V(t + 1) follow in
     // softmax phase t, once the buffers' previous tiles have been read).
-    if (n_mine > 0) {
+    if (kDirect && n_mine > 0) {
       my_item(0, wq0, wk0);
       my_item(min(1, n_mine - 1), wq1, wk1);
       my_item(min(2, n_mine - 1), wq2, wk2);
       if constexpr (RUNS) tile_range(wq2, wlo, whi);
       pg2 = page_entry(wk2, 2 < n_mine || !RUNS);
+      if constexpr (FUSED) pe0 = page_entry(wk0, true), pe1 = page_entry(wk1, true);
       load_q_async(wq0);
       qt_q = wq0;
       const size_t off0 = (!RUNS && wk0 == 0) ? (size_t)pg0 * P * row_bytes : tile_page_off(wk0);
-      issue_direct(wk0, off0, kbase, knew, kbuf(0), false, false);
-      issue_direct(wk0, off0, vbase, vnew, vbuf(0), true, false);
+      issue_direct(mx, wk0, off0, kbase, knew, kbuf(0), false, false);
+      issue_direct(mx, wk0, off0, vbase, vnew, vbuf(0), true, false);
       const bool r1 = RUNS && n_mine < 2;
       const size_t off1 = r1 ? 0 : tile_page_off(wk1);
-      issue_direct(wk1, off1, kbase, knew, kbuf(1), false, r1);
+      issue_direct(mx, wk1, off1, kbase, knew, kbuf(1), false, r1);
       ck = wk1, coff = off1, cres = r1;
     }
-  } else if (n_mine > 0) {
+  };
+  if (!kDirect && n_mine > 0) {
     int qt, kt;
     my_item(0, qt, kt);
     if (!RUNS && BIG_PAGE && kt == 0) {
@@ -936,7 +962,6 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       *reinterpret_cast<u32x4 *>(kbuf(1) + (lrow + i * kRowsPerPass) * C::kKRow + lch * 16) = qs[i];
     write_new(0);
   }
-  bar_after_loads();
   // Wave priorities: the GEMM wave's MFMAs are the critical path of each
   // half-step, so its instructions win issue slots over the other engine's
   // softmax on the same SIMD.
@@ -962,21 +987,23 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
         qt_q = qt;
       }
       qk_mfma(t & 1);
-      // The next item's Q, if it starts a new query tile, is loaded as soon
-      // as this tile's QK product is issued: it arrives during the softmax
-      // phase, whose K/V stores wait for all loads anyway.
-      if (t + 1 < n_mine) {
-        int qn = wq1, kn;
-        if constexpr (!kDirect) my_item(t + 1, qn, kn);
-        if (qn != qt_q) {
-          load_q_async(qn);
-          qt_q = qn;
-        }
-      }
     }
     if (t >= 1) pv_mfma((t - 1) & 1);
+    // The next item's Q, if it starts a new query tile, is loaded once the
+    // PV product is issued, so that the compiler's wait for the loads in
+    // flight before the first V read (it cannot tell their LDS writes from
+    // those reads) does not take in the Q loads as well.  It arrives during
+    // the softmax phase, at whose end every load but that phase's has landed.
+    if (t + 1 < n_mine) {
+      int qn = wq1, kn;
+      if constexpr (!kDirect) my_item(t + 1, qn, kn);
+      if (qn != qt_q) {
+        load_q_async(qn);
+        qt_q = qn;
+      }
+    }
   };
-  auto softmax_phase = [&](int t) __attribute__((always_inline)) {
+  auto softmax_phase = [&](int t, auto mx) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(0);
     if constexpr (FUSED && !kDirect) {
       // The next tile's new rows go to their pages first, so that the whole
@@ -1011,15 +1038,16 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
       // so the wait for all but the last 8 memory operations at the end of
       // the phase still covers exactly the older loads.
       if constexpr (FUSED) {
-        if (writes_new_qk(wq0, wk0)) write_back(wq0, wk0, kbuf(t & 1), (char *)a.c.k, false);
-        if (t >= 1 && writes_new_qk(wq_m1, wk_m1)) write_back(wq_m1, wk_m1, vbuf((t + 1) & 1), (char *)a.c.v, true);
+        if (writes_new_qk(wq0, wk0)) write_back(wq0, wk0, pe0, kbuf(t & 1), (char *)a.c.k, false);
+        if (t >= 1 && writes_new_qk(wq_m1, wk_m1))
+          write_back(wq_m1, wk_m1, pe_m1, vbuf((t + 1) & 1), (char *)a.c.v, true);
       }
       // K(t + 2): resident when item t had the same key tile (run mode).
       // V(t + 1): the K tile of the previous step.
       const bool r2 = RUNS && (t + 2 >= n_mine || wk2 == wk0);
       const size_t off2 = r2 ? 0 : page_off(pg2, wk2);
-      issue_direct(wk2, off2, kbase, knew, kbuf(t & 1), false, r2);
-      issue_direct(ck, coff, vbase, vnew, vbuf((t + 1) & 1), true, cres);
+      issue_direct(mx, wk2, off2, kbase, knew, kbuf(t & 1), false, r2);
+      issue_direct(mx, ck, coff, vbase, vnew, vbuf((t + 1) & 1), true, cres);
       ck = wk2, coff = off2, cres = r2;
       advance(t);
     }
@@ -1037,37 +1065,54 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   auto last_write_back = [&]() __attribute__((always_inline)) {
     if constexpr (FUSED && kDirect)  // the window has moved on: item n_mine - 1 is its first
       if (n_mine > 0 && writes_new_qk(wq_m1, wk_m1))
-        write_back(wq_m1, wk_m1, vbuf((n_mine - 1) & 1), (char *)a.c.v, true);
+        write_back(wq_m1, wk_m1, pe_m1, vbuf((n_mine - 1) & 1), (char *)a.c.v, true);
   };
-  // Engine 0 passes 2 * half + 1 barriers in its loop, engine 1 one leading
-  // barrier and 2 * n1 + 1 in its loop; the engine with fewer pads one at
-  // the end (half - n1 is 0 or 1).  Each engine's loop is its own
-  // straight-line code so that its registers keep one assignment.
-  if (eng == 0) {
-    for (int t = 0; t < n_mine; ++t) {
-      gemm_phase(t);
+  // The prologue and the loops of both engines, once per kind of sequence:
+  // in the fused append, a sequence whose cached part does not end on a
+  // 64-key boundary has a key tile of both cached and new keys, loaded
+  // through per-lane branches (mx true); the copy for the others has none,
+  // so that the compiler counts the loads in flight of every path exactly.
+  auto run = [&](auto mx) __attribute__((always_inline)) {
+    direct_prologue(mx);
+    bar_after_loads();
+    // Engine 0 passes 2 * half + 1 barriers in its loop, engine 1 one leading
+    // barrier and 2 * n1 + 1 in its loop; the engine with fewer pads one at
+    // the end (half - n1 is 0 or 1).  Each engine's loop is its own
+    // straight-line code so that its registers keep one assignment.
+    if (eng == 0) {
+      for (int t = 0; t < n_mine; ++t) {
+        gemm_phase(t);
+        bar_after_gemm();
+        softmax_phase(t, mx);
+        bar_after_loads();
+      }
+      gemm_phase(n_mine);
+      last_write_back();
+      if constexpr (kDirect) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes the LDS
+      __syncthreads();
+      if (half == n1) __syncthreads();
+    } else {
       bar_after_gemm();
-      softmax_phase(t);
-      bar_after_loads();
+      for (int t = 0; t < n_mine; ++t) {
+        gemm_phase(t);
+        bar_after_gemm();
+        softmax_phase(t, mx);
+        bar_after_loads();
+      }
+      gemm_phase(n_mine);
+      last_write_back();
+      if constexpr (kDirect) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes the LDS
+      __syncthreads();
+      if (half > n1) __syncthreads();
     }
-    gemm_phase(n_mine);
-    last_write_back();
-    if constexpr (kDirect) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes the LDS
-    __syncthreads();
-    if (half == n1) __syncthreads();
+  };
+  if constexpr (FUSED && kDirect) {
+    if (off % kPfKeys != 0)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
   } else {
-    bar_after_gemm();
-    for (int t = 0; t < n_mine; ++t) {
-      gemm_phase(t);
-      bar_after_gemm();
-      softmax_phase(t);
-      bar_after_loads();
-    }
-    gemm_phase(n_mine);
-    last_write_back();
-    if constexpr (kDirect) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes the LDS
-    __syncthreads();
-    if (half > n1) __syncthreads();
+    run(std::false_type{});
   }
   const int qt_cur = qt_o;
 
