@@ -148,7 +148,15 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // on one XCD and stream that head's K/V tiles together.
   int pair = blockIdx.x;  // pair mode: the pair index; run mode: the run index
   int h = blockIdx.y;
-  if ((grid_y & 7) == 0) {
+  if (RUNS && a.window_left >= 0) {
+    // A window reads each key tile about once, at the memory's pace: here
+    // the query head varies fastest, so that the workgroups running together
+    // read every head's part of the same cache rows (whole rows of all KV
+    // heads instead of scattered 256-byte pieces of them).
+    const int k = blockIdx.x + grid_x * blockIdx.y;
+    h = k % grid_y;
+    pair = k / grid_y;
+  } else if ((grid_y & 7) == 0) {
     const int k = blockIdx.x + grid_x * blockIdx.y;  // id inside this sequence
     const int k8 = k >> 3;
     h = (k & 7) + 8 * (k8 / grid_x);
