@@ -59,6 +59,9 @@ PREFILL_CASES = [
     # prefill split work that way), with partial last runs.
     wl.PrefillWorkload("bf16_win200_runs", (1500, 1030), 4, 2, 128, 64, "bf16", seed=39, window_left=200),
     wl.PrefillWorkload("bf16_noncausal_runs", (1100,), 2, 1, 128, 256, "bf16", seed=40, causal=False),
+    # A window orders its workgroups query-head-fastest: 12 heads (groups of
+    # 3, not a power of two), two sequences of several query tiles.
+    wl.PrefillWorkload("bf16_h12_g3_win64", (1400, 520), 12, 4, 128, 64, "bf16", seed=42, window_left=64),
     wl.PrefillWorkload("f32_d64_p16", (128, 45), 2, 1, 64, 16, "f32", seed=36),
     wl.PrefillWorkload("f32_d128_win3", (70,), 2, 2, 128, 32, "f32", seed=37, window_left=3),
     # fp32 on its MFMA kernel (32-row blocks, 32-key steps): ragged rows over
@@ -83,7 +86,7 @@ def test_prefill_matches_oracle(w):
 
 
 RUN_MODE_CASES = [w for w in PREFILL_CASES if w.name in ("bf16_win200_runs", "bf16_noncausal_runs",
-                                                           "bf16_d128_g8_win128")]
+                                                           "bf16_d128_g8_win128", "bf16_h12_g3_win64")]
 
 
 @pytest.mark.parametrize("run_tiles", [2, 3, 8])

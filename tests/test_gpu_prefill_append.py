@@ -29,6 +29,9 @@ CASES = [
     (wl.PrefillWorkload("chunk_g8_p256", (1030,), 8, 1, 128, 256, "bf16", seed=64), (511,)),
     (wl.PrefillWorkload("window128_runs", (1500, 400), 4, 2, 128, 64, "bf16", seed=65, window_left=128), (0, 200)),
     (wl.PrefillWorkload("window0_chunk", (300,), 4, 2, 128, 64, "bf16", seed=66, window_left=0), (90,)),
+    # 12 query heads in groups of 3 (the window's head-fastest order), one
+    # fresh prompt and one chunk after a prefix inside a key tile
+    (wl.PrefillWorkload("window64_h12_g3", (900, 400), 12, 4, 128, 64, "bf16", seed=72, window_left=64), (0, 130)),
     (wl.PrefillWorkload("noncausal_runs", (1100, 300), 2, 1, 128, 256, "bf16", seed=67, causal=False), (0, 70)),
     # a sequence with no new rows in the batch (its whole context cached)
     (wl.PrefillWorkload("empty_chunk_in_batch", (300, 200, 130), 8, 2, 128, 64, "bf16", seed=70), (0, 200, 64)),
@@ -118,7 +121,8 @@ def test_prefill_append_matches_oracle(w, prefix, route, monkeypatch):
 
 
 @pytest.mark.parametrize("run_tiles", [3, 8])
-@pytest.mark.parametrize("w,prefix", [c for c in CASES if c[0].name in ("window128_runs", "noncausal_runs")],
+@pytest.mark.parametrize("w,prefix", [c for c in CASES if c[0].name in ("window128_runs", "noncausal_runs",
+                                                                         "window64_h12_g3")],
                          ids=lambda c: getattr(c, "name", None))
 def test_prefill_append_run_lengths(w, prefix, run_tiles, monkeypatch):
     """The fused kernel in run mode with longer runs than the grid size picks
