@@ -85,6 +85,31 @@ def test_prefill_matches_oracle(w):
     assert err <= (1e-4 if w.dtype == "f32" else 1e-3)
 
 
+def _random_prefill_cases(n, seed=81):
+    """Seeded random shapes for the prefill alone: batch 1-3, lengths
+    1-1500, GQA groups 1-4 over 1-3 KV heads (head counts that are not
+    powers of two included), causal / windowed / unmasked in turn, D = 128,
+    64- and 256-key pages."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        batch = int(rng.integers(1, 4))
+        lens = tuple(int(x) for x in rng.integers(1, 1501, size=batch))
+        hkv = int(rng.choice([1, 2, 3]))
+        group = int(rng.choice([1, 2, 3, 4]))
+        mode = i % 3
+        cases.append(wl.PrefillWorkload(f"random_prefill{i}", lens, hkv * group, hkv, 128, int(rng.choice([64, 256])),
+                                        "bf16", seed=200 + i, causal=mode != 2,
+                                        window_left=int(rng.integers(0, 400)) if mode == 1 else -1))
+    return cases
+
+
+@pytest.mark.parametrize("w", _random_prefill_cases(12), ids=lambda w: w.name)
+def test_prefill_random_shapes(w):
+    """Random ragged batches, head counts, masks and page sizes."""
+    test_prefill_matches_oracle(w)
+
+
 RUN_MODE_CASES = [w for w in PREFILL_CASES if w.name in ("bf16_win200_runs", "bf16_noncausal_runs",
                                                            "bf16_d128_g8_win128", "bf16_h12_g3_win64")]
 
