@@ -411,7 +411,9 @@ __global__ __launch_bounds__(512, 2) void prefill_bf16_kernel(PrefillArgs a, con
   // Fused: a tile of new keys comes from the new rows at nbase; the one tile
   // that holds both cached and new keys (when the first new position is not
   // a multiple of 64) takes each row from where it is, every lane loading
-  // through one of two descriptors, so each LDS slot is written once.
+  // through one of two descriptors, so each LDS slot is written once.  mx
+  // (std::bool_constant): whether this copy of the loops handles such a
+  // tile at all.
   auto issue_direct = [&](auto mx, int kt, size_t tile_off, const char *base, const char *nbase, unsigned char *dst,
                           bool is_v, bool res) __attribute__((always_inline)) {
     if constexpr (kDirect) {
