@@ -590,6 +590,13 @@ BACKWARD_CASES = [
     ("bf16_window64", (257,), (257,), 4, 4, 128, 64, "bf16", True, 64),
     ("bf16_unmasked_d64", (130,), (130,), 4, 1, 64, 32, "bf16", False, -1),
     ("f32_d64", (100, 33), (100, 60), 4, 2, 64, 16, "f32", True, -1),
+    # groups of 3, a window over chunks after a cached prefix, a window of
+    # zero (each row sees its own key only), D = 64 on 256-key pages, and an
+    # unmasked chunk
+    ("bf16_g3_chunked_window100", (190, 333), (400, 333), 6, 2, 128, 64, "bf16", True, 100),
+    ("bf16_window0", (129,), (129,), 2, 1, 128, 64, "bf16", True, 0),
+    ("bf16_d64_gqa_p256", (520,), (520,), 8, 2, 64, 256, "bf16", True, -1),
+    ("bf16_unmasked_chunked", (150, 40), (300, 90), 4, 2, 128, 32, "bf16", False, -1),
 ]
 
 
